@@ -1,0 +1,408 @@
+/*
+ * CPU oracle of the hierarchical sparse KV hot path -- TEST INFRASTRUCTURE ONLY (see hsk_oracle.h).
+ *
+ * Written for readability, not speed: scalar loops, one request at a time, a full sort for victim choice.
+ * Every function names the passage of the pages it follows:
+ *   [HS]  "HiSparse: Scaling Sparse-Attention Decoding with Hierarchical KV Cache Management"
+ *   [AD]  "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy"
+ *
+ * Readings where the pages leave a step open (each is also listed with the design notes):
+ *   - recency: rec = 2e+1 for a hit at epoch e, 2e for a fill at epoch e, 0 for an empty slot, so hits
+ *     rank just above the same step's fills ([HS] 3.2 "Replacement policy", 3.4 phase 3);
+ *   - victims: the non-hit slots in ascending (rec, slot) order; the i-th distinct miss (first
+ *     occurrence order over the flattened query lists) takes the i-th victim;
+ *   - precedence tail > optional history > hot cache ([AD] 3.2, Figure 2 callout order; a row may be in
+ *     the optional map and the hot cache at once, [AD] 3.1);
+ *   - directly resolved rows leave the hot-cache metadata untouched ([AD] 3.2: they never reach
+ *     replacement);
+ *   - misses beyond the free hot slots of a call go to staging in miss order and are not promoted
+ *     ([AD] 3.3 overflow to staging);
+ *   - out-of-range positions and staging overflow reject the whole request before any state changes.
+ */
+#include "hsk_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+struct ora_source {
+  int32_t R, B, T, P, S, row_bytes;
+  int64_t opt_pool_pages;
+  int64_t* ctx;       /* [R] */
+  int32_t* key;       /* [R][B] position held by a hot slot, -1 = empty */
+  uint32_t* rec;      /* [R][B] recency stamp, 0 = empty */
+  int32_t** pt;       /* [R] -> [ctx_r] page table: hot slot of a position or -1 */
+  int32_t** opt;      /* [R] -> [ctx_r / P] optional page id of a complete page or -1 */
+  uint32_t last_epoch;
+  int64_t pool_rows;
+  int64_t* pool;      /* [pool_rows] pool model: r * 2^32 + position, or -1 */
+};
+
+/* pool row addresses, one pool per source (region order: hot, tail, optional, staging) */
+static int64_t hot_loc(const ora_source* s, int32_t r, int32_t slot) { return (int64_t)r * s->B + slot; }
+static int64_t tail_loc(const ora_source* s, int32_t r, int64_t p) {
+  return (int64_t)s->R * s->B + (int64_t)r * s->T + (p % s->T);
+}
+static int64_t opt_loc(const ora_source* s, int64_t page_id, int64_t p) {
+  return (int64_t)s->R * s->B + (int64_t)s->R * s->T + page_id * s->P + (p % s->P);
+}
+static int64_t stg_loc(const ora_source* s, int32_t r, int64_t c) {
+  return (int64_t)s->R * s->B + (int64_t)s->R * s->T + s->opt_pool_pages * s->P + (int64_t)r * s->S + c;
+}
+static int64_t pool_tag(int32_t r, int64_t p) { return ((int64_t)r << 32) | p; }
+
+ora_source* ora_create(int32_t R, const int64_t* ctx, int32_t B, int32_t T, int32_t page_rows,
+                       int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes) {
+  if (R <= 0 || B <= 0 || T < 0 || page_rows < 0 || opt_pool_pages < 0 || staging_rows < 0) return NULL;
+  if (page_rows == 0 && opt_pool_pages != 0) return NULL;
+  ora_source* s = (ora_source*)calloc(1, sizeof(ora_source));
+  if (!s) return NULL;
+  s->R = R; s->B = B; s->T = T; s->P = page_rows; s->S = staging_rows; s->row_bytes = row_bytes;
+  s->opt_pool_pages = opt_pool_pages;
+  s->ctx = (int64_t*)malloc(sizeof(int64_t) * R);
+  s->key = (int32_t*)malloc(sizeof(int32_t) * (size_t)R * B);
+  s->rec = (uint32_t*)calloc((size_t)R * B, sizeof(uint32_t));
+  s->pt = (int32_t**)calloc(R, sizeof(int32_t*));
+  s->opt = (int32_t**)calloc(R, sizeof(int32_t*));
+  s->pool_rows = (int64_t)R * B + (int64_t)R * T + opt_pool_pages * page_rows + (int64_t)R * staging_rows;
+  s->pool = (int64_t*)malloc(sizeof(int64_t) * (size_t)s->pool_rows);
+  if (!s->ctx || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
+  for (int64_t i = 0; i < s->pool_rows; ++i) s->pool[i] = -1;
+  for (int64_t i = 0; i < (int64_t)R * B; ++i) s->key[i] = -1;
+  for (int32_t r = 0; r < R; ++r) {
+    s->ctx[r] = ctx[r];
+    if (ctx[r] <= 0 || ctx[r] > 0x7fffffff) { ora_destroy(s); return NULL; }
+    s->pt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)ctx[r]);
+    int64_t np = page_rows ? ctx[r] / page_rows : 0;
+    s->opt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1));
+    if (!s->pt[r] || !s->opt[r]) { ora_destroy(s); return NULL; }
+    for (int64_t p = 0; p < ctx[r]; ++p) s->pt[r][p] = -1;
+    for (int64_t g = 0; g < np; ++g) s->opt[r][g] = -1;
+  }
+  return s;
+}
+
+void ora_destroy(ora_source* s) {
+  if (!s) return;
+  if (s->pt) for (int32_t r = 0; r < s->R; ++r) free(s->pt[r]);
+  if (s->opt) for (int32_t r = 0; r < s->R; ++r) free(s->opt[r]);
+  free(s->pt); free(s->opt); free(s->ctx); free(s->key); free(s->rec); free(s->pool); free(s);
+}
+
+int64_t ora_pool_rows(const ora_source* s) { return s->pool_rows; }
+
+/* [HS] 3.3 (1) and [AD] 3.1: the newest rows stay in the tail, which is never lent. */
+void ora_commit_prefill(ora_source* s) {
+  for (int32_t r = 0; r < s->R; ++r) {
+    int64_t lo = s->ctx[r] - s->T;
+    if (lo < 0) lo = 0;
+    for (int64_t p = lo; p < s->ctx[r]; ++p) s->pool[tail_loc(s, r, p)] = pool_tag(r, p);
+  }
+}
+
+/* [AD] 3.1: optional residency covers complete pages of imported history; population copies the page
+ * and publishes its ready location afterwards, reclaim drops the location (-1). */
+int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int64_t n_pages) {
+  if (r < 0 || r >= s->R || s->P == 0) return ORA_EINVAL;
+  int64_t complete = s->ctx[r] / s->P;
+  if (n_pages < 0 || n_pages > complete) return ORA_EINVAL;
+  for (int64_t g = 0; g < n_pages; ++g)
+    if (page_ids[g] < -1 || page_ids[g] >= s->opt_pool_pages) return ORA_EINVAL;
+  for (int64_t g = 0; g < n_pages; ++g) {
+    s->opt[r][g] = page_ids[g];
+    if (page_ids[g] >= 0)
+      for (int64_t i = 0; i < s->P; ++i) s->pool[opt_loc(s, page_ids[g], g * s->P + i)] = pool_tag(r, g * s->P + i);
+  }
+  return ORA_OK;
+}
+
+/* victim order: ascending (rec, slot) */
+typedef struct { uint32_t rec; int32_t slot; } rs_pair;
+static int cmp_rs(const void* a, const void* b) {
+  const rs_pair* x = (const rs_pair*)a;
+  const rs_pair* y = (const rs_pair*)b;
+  if (x->rec != y->rec) return x->rec < y->rec ? -1 : 1;
+  return x->slot < y->slot ? -1 : (x->slot > y->slot ? 1 : 0);
+}
+
+/*
+ * One request of one resolve call.  Steps follow [AD] 3.2 / Figure 2 (direct pass, hot-cache scan, host
+ * recovery) with the union of [AD] 3.3 Eqs. 5-6, and the hot-cache phases of [HS] 3.4.
+ */
+static void resolve_request(ora_source* s, int32_t r, uint32_t e, const int32_t* sel, int32_t Qmax, int32_t k,
+                            int32_t nq, int32_t* locs, uint8_t* cls, ora_stats* st,
+                            int32_t* plan_pos, int32_t* plan_loc, int32_t* plan_n, int32_t plan_cap,
+                            int32_t* ev_slot, int32_t* ev_key, int32_t* ev_n) {
+  const int64_t n = s->ctx[r];
+  const int32_t B = s->B;
+  const int64_t nsel = (int64_t)nq * k;
+  int32_t* key = s->key + (int64_t)r * B;
+  uint32_t* rec = s->rec + (int64_t)r * B;
+  int32_t* pt = s->pt[r];
+  memset(st, 0, sizeof(*st));
+  for (int64_t f = 0; f < (int64_t)Qmax * k; ++f) {
+    locs[f] = -1;
+    if (cls) cls[f] = ORA_CLS_NONE;
+  }
+  if (plan_n) plan_n[r] = 0;
+  if (ev_n) ev_n[r] = 0;
+
+  /* (1) intake: every selected position must name a row of the request's history ([HS] 3.3 (3)) */
+  for (int64_t f = 0; f < nsel; ++f)
+    if (sel[f] < 0 || sel[f] >= n) { st->status = ORA_ERANGE; return; }
+
+  /* (2) direct pass, [AD] 3.2 callout 1: tail rows, then ready complete optional pages */
+  uint8_t* klass = (uint8_t*)calloc((size_t)(nsel > 0 ? nsel : 1), 1);
+  for (int64_t f = 0; f < nsel; ++f) {
+    int64_t p = sel[f];
+    if (s->T > 0 && p >= n - s->T) {
+      klass[f] = ORA_CLS_TAIL;
+      locs[f] = (int32_t)tail_loc(s, r, p);
+    } else if (s->P > 0 && p / s->P < n / s->P && s->opt[r][p / s->P] >= 0) {
+      klass[f] = ORA_CLS_OPT;
+      locs[f] = (int32_t)opt_loc(s, s->opt[r][p / s->P], p);
+    }
+  }
+
+  /* (3) distinct pending positions in first-occurrence order over f = j*k + i ([AD] Eq. 6 union) */
+  uint8_t* seen = (uint8_t*)calloc((size_t)n, 1);
+  int32_t* uniq = (int32_t*)malloc(sizeof(int32_t) * (size_t)(nsel > 0 ? nsel : 1));
+  int64_t m = 0;
+  for (int64_t f = 0; f < nsel; ++f) {
+    if (klass[f] != ORA_CLS_NONE) continue;
+    if (!seen[sel[f]]) { seen[sel[f]] = 1; uniq[m++] = sel[f]; }
+  }
+
+  /* (4) hot-cache lookup through the page table ([HS] 3.2, 3.4 phases 1-2): hits and misses */
+  uint8_t* is_hit_slot = (uint8_t*)calloc((size_t)B, 1);
+  int32_t* miss = (int32_t*)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
+  int64_t nmiss = 0, nhit = 0;
+  for (int64_t u = 0; u < m; ++u) {
+    int32_t slot = pt[uniq[u]];
+    if (slot >= 0) { if (!is_hit_slot[slot]) { is_hit_slot[slot] = 1; ++nhit; } }
+    else miss[nmiss++] = uniq[u];
+  }
+
+  /* (5) victims ([HS] 3.4 phase 3): non-hit slots by ascending (rec, slot); the first v are taken */
+  rs_pair* cand = (rs_pair*)malloc(sizeof(rs_pair) * (size_t)B);
+  int32_t ncand = 0;
+  for (int32_t slot = 0; slot < B; ++slot)
+    if (!is_hit_slot[slot]) { cand[ncand].rec = rec[slot]; cand[ncand].slot = slot; ++ncand; }
+  qsort(cand, (size_t)ncand, sizeof(rs_pair), cmp_rs);
+  int64_t v = nmiss < ncand ? nmiss : ncand;
+  int64_t over = nmiss - v;
+  if (over > s->S) {
+    st->status = ORA_ESTAGE;
+    for (int64_t f = 0; f < (int64_t)Qmax * k; ++f) { locs[f] = -1; if (cls) cls[f] = ORA_CLS_NONE; }
+    free(klass); free(seen); free(uniq); free(is_hit_slot); free(miss); free(cand);
+    return;
+  }
+
+  /* (6) fills: evict the victim's old position, install the missing row, copy host -> pool ([HS] 3.4
+   * phases 3-4).  Rows beyond the free slots go to staging ([AD] 3.3), outside the hot cache. */
+  int32_t* staged_at = (int32_t*)malloc(sizeof(int32_t) * (size_t)n); /* position -> staging index */
+  for (int64_t i = 0; i < nmiss; ++i) staged_at[miss[i]] = -1;
+  for (int64_t i = 0; i < nmiss; ++i) {
+    int64_t dst;
+    if (i < v) {
+      int32_t slot = cand[i].slot;
+      if (key[slot] >= 0) {
+        if (ev_n) {
+          ev_slot[(int64_t)r * B + ev_n[r]] = slot;
+          ev_key[(int64_t)r * B + ev_n[r]] = key[slot];
+          ev_n[r] += 1;
+        }
+        pt[key[slot]] = -1;
+      }
+      key[slot] = miss[i];
+      pt[miss[i]] = slot;
+      rec[slot] = 2u * e;
+      dst = hot_loc(s, r, slot);
+    } else {
+      staged_at[miss[i]] = (int32_t)(i - v);
+      dst = stg_loc(s, r, i - v);
+    }
+    s->pool[dst] = pool_tag(r, miss[i]);
+    if (plan_n && i < plan_cap) {
+      plan_pos[(int64_t)r * plan_cap + i] = miss[i];
+      plan_loc[(int64_t)r * plan_cap + i] = (int32_t)dst;
+    }
+  }
+  if (plan_n) plan_n[r] = (int32_t)nmiss;
+
+  /* (7) hits move to the most recent end, above the same step's fills ([HS] 3.2, 3.4 phase 3) */
+  for (int32_t slot = 0; slot < B; ++slot)
+    if (is_hit_slot[slot]) rec[slot] = 2u * e + 1u;
+
+  /* (8) emit locations in selection order ([HS] 3.4 phase 5; [AD] Eq. 12) */
+  uint8_t* missed = seen; /* reuse: 2 = fetched by this call */
+  for (int64_t i = 0; i < nmiss; ++i) missed[miss[i]] = 2;
+  for (int64_t f = 0; f < nsel; ++f) {
+    int64_t p = sel[f];
+    if (klass[f] == ORA_CLS_TAIL) { st->n_tail++; }
+    else if (klass[f] == ORA_CLS_OPT) { st->n_opt++; }
+    else if (missed[p] == 2) {
+      st->n_miss_sel++;
+      if (staged_at[p] >= 0) { klass[f] = ORA_CLS_STAGED; locs[f] = (int32_t)stg_loc(s, r, staged_at[p]); }
+      else { klass[f] = ORA_CLS_FILL; locs[f] = (int32_t)hot_loc(s, r, pt[p]); }
+    } else {
+      st->n_hit_sel++;
+      klass[f] = ORA_CLS_HIT;
+      locs[f] = (int32_t)hot_loc(s, r, pt[p]);
+    }
+    if (cls) cls[f] = klass[f];
+  }
+
+  /* (9) stats */
+  st->n_sel = (int32_t)nsel;
+  st->n_hit = (int32_t)nhit;
+  st->n_miss = (int32_t)nmiss;
+  st->n_staged = (int32_t)over;
+  st->fetched_bytes = nmiss * (int64_t)s->row_bytes;
+  st->status = ORA_OK;
+  free(klass); free(seen); free(uniq); free(is_hit_slot); free(miss); free(cand); free(staged_at);
+}
+
+int32_t ora_resolve(ora_source* s, uint32_t epoch, const int32_t* sel, int32_t Qmax, int32_t k,
+                    const int32_t* nq, int32_t* locs, uint8_t* cls, ora_stats* stats,
+                    int32_t* plan_pos, int32_t* plan_loc, int32_t* plan_n, int32_t plan_cap,
+                    int32_t* ev_slot, int32_t* ev_key, int32_t* ev_n) {
+  /* the LRU clock: a caller-supplied epoch, strictly increasing per source */
+  if (epoch <= s->last_epoch || epoch > 0x7fffffffu) return ORA_EEPOCH;
+  if (Qmax <= 0 || k <= 0) return ORA_EINVAL;
+  for (int32_t r = 0; r < s->R; ++r) {
+    int32_t q = nq ? nq[r] : Qmax;
+    if (q < 0 || q > Qmax) return ORA_EINVAL;
+  }
+  for (int32_t r = 0; r < s->R; ++r) {
+    int64_t off = (int64_t)r * Qmax * k;
+    resolve_request(s, r, epoch, sel + off, Qmax, k, nq ? nq[r] : Qmax, locs + off, cls ? cls + off : NULL,
+                    stats + r, plan_pos, plan_loc, plan_n, plan_cap, ev_slot, ev_key, ev_n);
+  }
+  s->last_epoch = epoch;
+  return ORA_OK;
+}
+
+void ora_snapshot(const ora_source* s, int32_t r, int32_t* key, uint32_t* rec, int32_t* order, int32_t* pt,
+                  int32_t* opt) {
+  const int32_t B = s->B;
+  if (key) memcpy(key, s->key + (int64_t)r * B, sizeof(int32_t) * (size_t)B);
+  if (rec) memcpy(rec, s->rec + (int64_t)r * B, sizeof(uint32_t) * (size_t)B);
+  if (order) {
+    rs_pair* all = (rs_pair*)malloc(sizeof(rs_pair) * (size_t)B);
+    for (int32_t slot = 0; slot < B; ++slot) { all[slot].rec = s->rec[(int64_t)r * B + slot]; all[slot].slot = slot; }
+    qsort(all, (size_t)B, sizeof(rs_pair), cmp_rs);
+    for (int32_t i = 0; i < B; ++i) order[i] = all[i].slot;
+    free(all);
+  }
+  if (pt) memcpy(pt, s->pt[r], sizeof(int32_t) * (size_t)s->ctx[r]);
+  if (opt && s->P > 0) memcpy(opt, s->opt[r], sizeof(int32_t) * (size_t)(s->ctx[r] / s->P));
+}
+
+void ora_pool_lookup(const ora_source* s, const int32_t* locs, int64_t n, int64_t* out) {
+  for (int64_t i = 0; i < n; ++i)
+    out[i] = (locs[i] >= 0 && locs[i] < s->pool_rows) ? s->pool[locs[i]] : -1;
+}
+
+/* ---------------------------------------------------------------------------------------------- */
+/* attention: the plain definition, [AD] Eq. 1 with exactness of section 3.5                       */
+/* ---------------------------------------------------------------------------------------------- */
+static double bf16_to_f64(uint16_t h) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)h << 16;
+  return (double)v.f;
+}
+
+/* softmax(scale * q . k_i) weighted sum of v_i, for one head, from precomputed scores */
+static void softmax_weighted(const double* scores, int64_t nk, const uint16_t* vals, int64_t vstride, int32_t dv,
+                             double* out) {
+  double mx = -INFINITY;
+  for (int64_t i = 0; i < nk; ++i) if (scores[i] > mx) mx = scores[i];
+  double denom = 0.0;
+  for (int32_t c = 0; c < dv; ++c) out[c] = 0.0;
+  for (int64_t i = 0; i < nk; ++i) {
+    double w = exp(scores[i] - mx);
+    denom += w;
+    const uint16_t* v = vals + i * vstride;
+    for (int32_t c = 0; c < dv; ++c) out[c] += w * bf16_to_f64(v[c]);
+  }
+  for (int32_t c = 0; c < dv; ++c) out[c] /= denom;
+}
+
+void ora_mla_attention(const uint16_t* q, const uint16_t* rows, int32_t k, int32_t H, int32_t dk, int32_t dv,
+                       int32_t row_elems, double scale, double* out) {
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+  for (int32_t h = 0; h < H; ++h) {
+    const uint16_t* qh = q + (int64_t)h * dk;
+    for (int32_t i = 0; i < k; ++i) {
+      const uint16_t* row = rows + (int64_t)i * row_elems;
+      double acc = 0.0;
+      for (int32_t d = 0; d < dk; ++d) acc += bf16_to_f64(qh[d]) * bf16_to_f64(row[d]);
+      sc[i] = scale * acc;
+    }
+    softmax_weighted(sc, k, rows, row_elems, dv, out + (int64_t)h * dv);
+  }
+  free(sc);
+}
+
+void ora_gqa_attention(const uint16_t* q, const uint16_t* pages, int32_t kp, int32_t page_tokens, int32_t Hg,
+                       int32_t dh, double scale, double* out) {
+  const int64_t nk = (int64_t)kp * page_tokens;
+  const int64_t tok = 2 * (int64_t)dh; /* one token: [K dh | V dh] */
+  double* sc = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+  for (int32_t h = 0; h < Hg; ++h) {
+    const uint16_t* qh = q + (int64_t)h * dh;
+    for (int64_t i = 0; i < nk; ++i) {
+      const uint16_t* kv = pages + i * tok;
+      double acc = 0.0;
+      for (int32_t d = 0; d < dh; ++d) acc += bf16_to_f64(qh[d]) * bf16_to_f64(kv[d]);
+      sc[i] = scale * acc;
+    }
+    softmax_weighted(sc, nk, pages + dh, tok, dh, out + (int64_t)h * dh);
+  }
+  free(sc);
+}
+
+void ora_bf16_from_f64(const double* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    double a = x[i];
+    if (a != a) { out[i] = 0x7FC0; continue; }
+    /* round the double to 8 significant bits (nearest, ties to even), then take the float bits */
+    int ex;
+    double m = frexp(fabs(a), &ex);     /* |a| = m * 2^ex, m in [0.5, 1) */
+    if (m == 0.0) { out[i] = a < 0 || (a == 0.0 && signbit(a)) ? 0x8000 : 0x0000; continue; }
+    double scaled = ldexp(m, 8);        /* 8 significant bits before the point */
+    if (ex - 1 < -126) scaled = ldexp(m, 8 - (-126 - (ex - 1)));   /* subnormal range */
+    double fl = floor(scaled);
+    double frac = scaled - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) != 0.0)) fl += 1.0;
+    double mag = (ex - 1 < -126) ? ldexp(fl, -133) : ldexp(fl, ex - 8);
+    union { float f; uint32_t u; } v;
+    v.f = (float)mag;                   /* exact: mag has at most 8 significant bits */
+    if (isinf(v.f) || mag > 3.3895313892515355e38) v.u = 0x7F800000u;
+    out[i] = (uint16_t)((v.u >> 16) | (a < 0 ? 0x8000u : 0u));
+  }
+}
+
+/* [AD] Eq. 4: walk the reclaim order and take the first q requests whose optional pages cover Delta */
+int32_t ora_reclaim_plan(const int64_t* pages_held, int32_t n, int64_t deficit) {
+  if (deficit <= 0) return 0;
+  int64_t acc = 0;
+  for (int32_t q = 1; q <= n; ++q) {
+    acc += pages_held[q - 1];
+    if (acc >= deficit) return q;
+  }
+  return -1; /* the optional pages do not cover the deficit: admission waits */
+}
+
+/* [AD] Eq. 9: R_d = p * ceil((W + p - 1 + K_max) / p) */
+int64_t ora_ring_rows(int64_t window, int64_t page_rows, int64_t k_max) {
+  int64_t need = window + page_rows - 1 + k_max;
+  return page_rows * ((need + page_rows - 1) / page_rows);
+}
+/* [AD] Eq. 10: phi(i, t) = i * R_d + (t mod R_d) */
+int64_t ora_ring_addr(int64_t slot, int64_t t, int64_t ring_rows) { return slot * ring_rows + (t % ring_rows); }
+/* [AD] Eq. 11: M_stage = chi * N * K_max * k * d_KV */
+double ora_staging_bytes(int64_t live_sources, int64_t slots, int64_t k_max, int64_t k, int64_t row_bytes) {
+  return (double)live_sources * (double)slots * (double)k_max * (double)k * (double)row_bytes;
+}

@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: long-running case")
+
+
+def _ensure_built(mod):
+    if not os.path.exists(mod.LIB_PATH):
+        mod.build()
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _cpu_libs():
+    import oracle
+    import synth
+    _ensure_built(synth)
+    _ensure_built(oracle)
+    yield
