@@ -1,0 +1,303 @@
+"""hierarchical_sparse_kv_layer_amd -- Python binding of libhsk.so (MI355X / gfx950).
+
+Argument marshalling only: every step of the hot path runs in the HIP kernels of libhsk.so (see
+include/hsk.h).  PyTorch supplies device memory (tensors) and streams; the names below mirror the C ABI:
+
+    kv_store_init / host_rows / commit_prefill / residency_set / reclaim_plan / resolve_step /
+    replay_plan / pool_base / sparse_decode_attn / attn_scratch_bytes / snapshot / read_plan /
+    sync_status / kv_store_destroy
+
+The library must be built (``__graft_entry__.build()``); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhsk.so")
+
+HSK_OK, HSK_EINVAL, HSK_ENOMEM, HSK_EHIP, HSK_ESTATE, HSK_ERANGE, HSK_ESTAGE, HSK_EEPOCH = 0, -1, -2, -3, -4, -5, -6, -7
+GATHER_ZEROCOPY, GATHER_NO_IO = 0, 1
+ATTN_MLA, ATTN_GQA = 0, 1
+MAX_HOT_SLOTS = 8192
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: the HIP library must be built (__graft_entry__.build()); "
+                      "there is no fallback path")
+
+_i32, _i64, _u32, _vp, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("num_requests", _i32), ("num_sources", _i32), ("row_bytes", _i32), ("hot_slots", _i32),
+                ("tail_rows", _i32), ("page_rows", _i32), ("opt_pool_pages", _i64), ("max_queries", _i32),
+                ("top_k", _i32), ("staging_rows", _i32), ("host_alias_sources", _i32), ("max_ctx", _i64),
+                ("ctx_len", _vp), ("gather_mode", _i32), ("gather_blocks", _i32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("num_requests", _i32), ("max_queries", _i32), ("heads", _i32),
+                ("kv_heads", _i32), ("dk", _i32), ("dv", _i32), ("top_k", _i32), ("row_elems", _i32),
+                ("page_tokens", _i32), ("split", _i32), ("scale", _f32)]
+
+
+STATS_DTYPE = np.dtype([("n_sel", np.int32), ("n_tail", np.int32), ("n_opt", np.int32), ("n_hit", np.int32),
+                        ("n_hit_sel", np.int32), ("n_miss", np.int32), ("n_miss_sel", np.int32),
+                        ("n_staged", np.int32), ("status", np.int32), ("reserved", np.int32),
+                        ("fetched_bytes", np.int64)])
+STATS_BYTES = STATS_DTYPE.itemsize  # 48
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.POINTER
+_sig = {
+    "hsk_workspace_bytes": (_i32, [_P(Desc), _P(ctypes.c_size_t), _P(ctypes.c_size_t)]),
+    "hsk_kv_store_init": (_i32, [_P(Desc), _vp, _vp, _vp, _P(_vp)]),
+    "hsk_host_rows": (_i32, [_vp, _i32, _i32, _P(_vp), _P(_i64)]),
+    "hsk_commit_prefill": (_i32, [_vp, _vp]),
+    "hsk_residency_set": (_i32, [_vp, _i32, _i32, _vp, _i64, _vp]),
+    "hsk_reclaim_plan": (_i32, [_vp, _i32, _i64, _P(_i32)]),
+    "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
+    "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
+    "hsk_pool_base": (_i32, [_vp, _i32, _P(_vp)]),
+    "hsk_attn_scratch_bytes": (_i32, [_P(AttnDesc), _P(ctypes.c_size_t)]),
+    "hsk_sparse_decode_attn": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "hsk_snapshot": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "hsk_read_plan": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _P(_i32)]),
+    "hsk_sync_status": (_i32, [_vp, _vp]),
+    "hsk_kv_store_destroy": (None, [_vp]),
+    "hsk_status_str": (ctypes.c_char_p, [_i32]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_sig)
+
+
+class HskError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}" if what else status_str(status))
+
+
+def status_str(s: int) -> str:
+    return _lib.hsk_status_str(int(s)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != HSK_OK:
+        raise HskError(rc, what)
+
+
+def _ptr(x) -> Optional[int]:
+    """Device/host address of a torch tensor, numpy array or int (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------------------------------------ C ABI
+def workspace_bytes(desc: Desc):
+    ws, pool = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.hsk_workspace_bytes(ctypes.byref(desc), ctypes.byref(ws), ctypes.byref(pool)), "hsk_workspace_bytes")
+    return ws.value, pool.value
+
+
+def kv_store_init(desc: Desc, workspace, pool, stream=None) -> int:
+    h = _vp()
+    _check(_lib.hsk_kv_store_init(ctypes.byref(desc), _ptr(workspace), _ptr(pool), _stream(stream), ctypes.byref(h)),
+           "hsk_kv_store_init")
+    return h.value
+
+
+def host_rows(store: int, source: int, req: int):
+    p, n = _vp(), _i64()
+    _check(_lib.hsk_host_rows(store, source, req, ctypes.byref(p), ctypes.byref(n)), "hsk_host_rows")
+    return p.value, n.value
+
+
+def commit_prefill(store: int, stream=None) -> None:
+    _check(_lib.hsk_commit_prefill(store, _stream(stream)), "hsk_commit_prefill")
+
+
+def residency_set(store: int, source: int, req: int, page_ids, stream=None) -> None:
+    ids = np.ascontiguousarray(np.asarray(page_ids, dtype=np.int32))
+    _check(_lib.hsk_residency_set(store, source, req, _ptr(ids), ids.size, _stream(stream)), "hsk_residency_set")
+
+
+def reclaim_plan(pages_held, deficit: int) -> int:
+    a = np.ascontiguousarray(np.asarray(pages_held, dtype=np.int64))
+    q = _i32()
+    _check(_lib.hsk_reclaim_plan(_ptr(a), a.size, int(deficit), ctypes.byref(q)), "hsk_reclaim_plan")
+    return q.value
+
+
+def resolve_step(store: int, source: int, epoch: int, sel, nq, locs, stats, stream=None) -> None:
+    _check(_lib.hsk_resolve_step(store, source, int(epoch), _ptr(sel), _ptr(nq), _ptr(locs), _ptr(stats),
+                                 _stream(stream)), "hsk_resolve_step")
+
+
+def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> None:
+    _check(_lib.hsk_replay_plan(store, plan_source, dst_source, _stream(stream)), "hsk_replay_plan")
+
+
+def pool_base(store: int, source: int) -> int:
+    p = _vp()
+    _check(_lib.hsk_pool_base(store, source, ctypes.byref(p)), "hsk_pool_base")
+    return p.value
+
+
+def attn_scratch_bytes(adesc: AttnDesc) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib.hsk_attn_scratch_bytes(ctypes.byref(adesc), ctypes.byref(b)), "hsk_attn_scratch_bytes")
+    return b.value
+
+
+def sparse_decode_attn(adesc: AttnDesc, q, pool, locs, nq, out, scratch, scratch_bytes: int, stream=None) -> None:
+    _check(_lib.hsk_sparse_decode_attn(ctypes.byref(adesc), _ptr(q), _ptr(pool), _ptr(locs), _ptr(nq), _ptr(out),
+                                       _ptr(scratch), int(scratch_bytes), _stream(stream)), "hsk_sparse_decode_attn")
+
+
+def snapshot(store: int, source: int, req: int, B: int, n_rows: int, page_rows: int) -> dict:
+    key = np.zeros(B, np.int32)
+    rec = np.zeros(B, np.uint32)
+    order = np.zeros(B, np.uint16)
+    pt = np.zeros(n_rows, np.int32)
+    opt = np.zeros(max(1, n_rows // page_rows) if page_rows else 1, np.int32)
+    _check(_lib.hsk_snapshot(store, source, req, _ptr(key), _ptr(rec), _ptr(order), _ptr(pt), _ptr(opt)),
+           "hsk_snapshot")
+    return {"key": key, "rec": rec, "order": order.astype(np.int32), "pt": pt,
+            "opt": opt if page_rows else np.zeros(0, np.int32)}
+
+
+def read_plan(store: int, source: int, req: int, cap: int):
+    pos = np.zeros(max(cap, 1), np.int32)
+    dst = np.zeros(max(cap, 1), np.int32)
+    n = _i32()
+    _check(_lib.hsk_read_plan(store, source, req, _ptr(pos), _ptr(dst), cap, ctypes.byref(n)), "hsk_read_plan")
+    m = min(n.value, cap)
+    return pos[:m].copy(), dst[:m].copy()
+
+
+def sync_status(store: int, stream=None) -> int:
+    return int(_lib.hsk_sync_status(store, _stream(stream)))
+
+
+def kv_store_destroy(store: int) -> None:
+    _lib.hsk_kv_store_destroy(store)
+
+
+# ------------------------------------------------------------------------------------------------ helpers
+class KVStore:
+    """Owns the device workspace and pool (torch tensors) of one store and the library handle."""
+
+    def __init__(self, *, requests: int, sources: int, row_bytes: int, hot_slots: int, tail_rows: int, ctx,
+                 max_ctx: Optional[int] = None, page_rows: int = 0, opt_pool_pages: int = 0, max_queries: int = 1,
+                 top_k: int, staging_rows: int = 0, host_alias: bool = False, gather_mode: int = GATHER_ZEROCOPY,
+                 gather_blocks: int = 0, device: str = "cuda", stream=None):
+        import torch
+        self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, np.int64), (requests,)))
+        self.desc = Desc(num_requests=requests, num_sources=sources, row_bytes=row_bytes, hot_slots=hot_slots,
+                         tail_rows=tail_rows, page_rows=page_rows, opt_pool_pages=opt_pool_pages,
+                         max_queries=max_queries, top_k=top_k, staging_rows=staging_rows,
+                         host_alias_sources=1 if host_alias else 0,
+                         max_ctx=int(max_ctx if max_ctx is not None else self.ctx.max()),
+                         ctx_len=self.ctx.ctypes.data, gather_mode=gather_mode, gather_blocks=gather_blocks)
+        ws, pool = workspace_bytes(self.desc)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.pool = torch.empty(pool, dtype=torch.uint8, device=device)
+        self.handle = kv_store_init(self.desc, self.workspace, self.pool, stream)
+        self.R, self.S, self.B, self.T = requests, sources, hot_slots, tail_rows
+        self.row_bytes, self.page_rows, self.max_queries, self.top_k = row_bytes, page_rows, max_queries, top_k
+        self.staging_rows, self.opt_pool_pages = staging_rows, opt_pool_pages
+        self.rows_per_source = requests * hot_slots + requests * tail_rows + opt_pool_pages * page_rows + \
+            requests * staging_rows
+
+    def host_rows(self, source: int, req: int) -> np.ndarray:
+        """The pinned host rows of (source, req) as a writable uint8 array [max_ctx, row_bytes]."""
+        p, n = host_rows(self.handle, source, req)
+        buf = (ctypes.c_uint8 * (n * self.row_bytes)).from_address(p)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(n, self.row_bytes)
+
+    def host_ptr(self, source: int, req: int) -> int:
+        return host_rows(self.handle, source, req)[0]
+
+    def commit_prefill(self, stream=None):
+        commit_prefill(self.handle, stream)
+
+    def residency_set(self, source: int, req: int, page_ids, stream=None):
+        residency_set(self.handle, source, req, page_ids, stream)
+
+    def resolve_step(self, source: int, epoch: int, sel, locs, stats=None, nq=None, stream=None):
+        resolve_step(self.handle, source, epoch, sel, nq, locs, stats, stream)
+
+    def replay_plan(self, plan_source: int, dst_source: int, stream=None):
+        replay_plan(self.handle, plan_source, dst_source, stream)
+
+    def pool_base(self, source: int) -> int:
+        return pool_base(self.handle, source)
+
+    def pool_rows(self, source: int):
+        """torch uint8 view [rows_per_source, row_bytes] of a source's pool region."""
+        off = source * self.rows_per_source * self.row_bytes
+        return self.pool[off: off + self.rows_per_source * self.row_bytes].view(self.rows_per_source, self.row_bytes)
+
+    def snapshot(self, source: int, req: int) -> dict:
+        return snapshot(self.handle, source, req, self.B, int(self.ctx[req]), self.page_rows)
+
+    def read_plan(self, source: int, req: int):
+        return read_plan(self.handle, source, req, self.max_queries * self.top_k)
+
+    def sync_status(self, stream=None) -> int:
+        return sync_status(self.handle, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            kv_store_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def stats_tensor(R: int, device: str = "cuda"):
+    import torch
+    return torch.zeros(R * STATS_BYTES, dtype=torch.uint8, device=device)
+
+
+def stats_to_numpy(t) -> np.ndarray:
+    return t.cpu().numpy().view(STATS_DTYPE)
+
+
+def mla_desc(*, requests: int, max_queries: int, heads: int, dk: int, dv: int, top_k: int, row_elems: int,
+             scale: float, split: int = 0) -> AttnDesc:
+    return AttnDesc(kind=ATTN_MLA, num_requests=requests, max_queries=max_queries, heads=heads, kv_heads=1, dk=dk,
+                    dv=dv, top_k=top_k, row_elems=row_elems, page_tokens=1, split=split, scale=scale)
+
+
+def gqa_desc(*, requests: int, heads: int, kv_heads: int, dh: int, top_k: int, page_tokens: int, scale: float,
+             split: int = 0) -> AttnDesc:
+    return AttnDesc(kind=ATTN_GQA, num_requests=requests, max_queries=1, heads=heads, kv_heads=kv_heads, dk=dh,
+                    dv=dh, top_k=top_k, row_elems=page_tokens * 2 * dh, page_tokens=page_tokens, split=split,
+                    scale=scale)

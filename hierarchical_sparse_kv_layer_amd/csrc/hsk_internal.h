@@ -1,0 +1,110 @@
+// Internal declarations shared by the host runtime and the kernels of libhsk.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "hsk.h"
+
+#define HSK_HIP(call)                                   \
+  do {                                                  \
+    hipError_t hsk_e_ = (call);                         \
+    if (hsk_e_ != hipSuccess) return HSK_EHIP;          \
+  } while (0)
+
+namespace hsk {
+
+constexpr int kResolveThreads = 1024;
+constexpr int kResolveWaves = kResolveThreads / 64;
+constexpr int kGatherThreads = 256;
+constexpr int64_t kAlign = 256;
+
+// Device pointers of one source's metadata (all inside the caller's workspace).
+struct SourceMeta {
+  int32_t* key;       // [R][B] position held by a hot slot, -1 empty
+  uint32_t* rec;      // [R][B] recency stamp: 2e+1 hit, 2e fill, 0 empty
+  uint16_t* order;    // [R][B] slots in ascending (rec, slot) order
+  int32_t* pt;        // [R][max_ctx] page table: slot of a position, or -1 (transiently: claims/staging codes)
+  int32_t* opt;       // [R][max_pages] optional page id of a complete page, or -1 (null without pages)
+  int32_t* plan_n;    // [R] distinct missing rows of the last resolve call
+  int32_t* plan_pos;  // [R][plan_cap] their positions, in miss order
+  int32_t* plan_dst;  // [R][plan_cap] the pool row each was copied to
+};
+
+// Byte offsets of every region of the workspace.
+struct WorkspaceLayout {
+  int64_t ctx, err, total;
+  std::vector<int64_t> key, rec, order, pt, opt, plan_n, plan_pos, plan_dst;
+};
+
+bool layout_workspace(const hsk_desc& d, WorkspaceLayout* out);
+int64_t rows_per_source(const hsk_desc& d);
+
+struct ResolveArgs {
+  const int32_t* sel;
+  const int32_t* nq;
+  int32_t* locs;
+  hsk_stats* stats;
+  const int64_t* ctx;
+  SourceMeta m;
+  int32_t* err;
+  int64_t max_ctx;
+  int64_t max_pages;
+  int64_t opt_base;   // first optional row: R*B + R*T
+  int64_t stg_base;   // first staging row: R*B + R*T + opt_pool_pages*page_rows
+  int32_t plan_cap;
+  int32_t R, B, T, P, S, Qmax, k, row_bytes;
+  uint32_t epoch;
+};
+
+struct GatherArgs {
+  const char* host;        // device-visible address of host rows of (host source, request 0)
+  char* pool;              // row 0 of the destination source's pool
+  const int32_t* plan_n;
+  const int32_t* plan_pos;
+  const int32_t* plan_dst;
+  int64_t host_req_stride; // bytes between requests in the host rows
+  int32_t plan_cap;
+  int32_t row_bytes;
+};
+
+struct CopyRun {           // one contiguous byte run, host -> pool
+  int64_t src;             // byte offset from the host source base
+  int64_t dst;             // byte offset from the pool source base
+  int64_t bytes;
+};
+
+hipError_t launch_init_meta(const SourceMeta& m, int32_t R, int32_t B, int64_t max_ctx, int64_t max_pages,
+                            hipStream_t s);
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks_per_req, hipStream_t s);
+hipError_t launch_tail_copy(const char* host, int64_t host_req_stride, char* pool, const int64_t* d_ctx,
+                            int32_t R, int32_t B, int32_t T, int32_t row_bytes, hipStream_t s);
+hipError_t launch_copy_runs(const char* host, char* pool, const CopyRun* runs, int32_t n, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+}  // namespace hsk
+
+struct hsk_store {
+  hsk_desc d;
+  std::vector<int64_t> ctx;
+  int64_t max_pages = 0;
+  int32_t plan_cap = 0;
+  int64_t rows_per_src = 0;
+  int32_t host_sources = 0;
+  int32_t device = 0;
+  char* ws = nullptr;
+  char* pool = nullptr;
+  int64_t* d_ctx = nullptr;
+  int32_t* d_err = nullptr;
+  std::vector<hsk::SourceMeta> meta;
+  std::vector<char*> host;                  // pinned host rows per host source
+  std::vector<uint32_t> last_epoch;         // per source
+  std::vector<std::vector<int32_t>> opt_mirror;  // [source * R + r] host copy of the optional map
+  void* h_stage = nullptr;                  // pinned staging for map and run-list uploads
+  size_t h_stage_bytes = 0;
+  void* d_stage = nullptr;                  // device copy of run lists
+  size_t d_stage_bytes = 0;
+};

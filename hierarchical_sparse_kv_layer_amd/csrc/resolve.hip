@@ -1,0 +1,447 @@
+// Resolve and row-movement kernels for gfx950.
+//
+// resolve_kernel: one 1024-thread workgroup per request.  It implements the fused resolve of "HiSparse:
+// Scaling Sparse-Attention Decoding with Hierarchical KV Cache Management" (section 3.4: stage the
+// selection, mark hot slots hit or evictable, scan marks to pick victims and update LRU metadata, publish
+// locations) with the residency-aware order of "Adaptive DHiSparse: Speculative Decoding over a
+// Load-Adaptive KV Hierarchy" (section 3.2 / Figure 2: tail and ready optional pages first) and the
+// multi-query union of its section 3.3 (Eqs. 5-6: each distinct missing row once, overflow to staging).
+//
+// How the phases map to CDNA4:
+//   * the selection is probed through the page table (one load per selected row) instead of hashing the
+//     selection and probing every slot: hits set bits in a B-bit LDS bitmap with LDS atomics;
+//   * duplicate misses are collapsed without a hash: each missing selection f does atomicMin(pt[p],
+//     INT_MIN + f), so the page-table word itself ends holding the first occurrence (order-independent,
+//     hence deterministic); the first-occurrence flags are then compacted with wave ballots and a
+//     block-wide prefix sum, in ascending f, giving every distinct miss its index in miss order;
+//   * victims come from the per-request slot order kept in (rec, slot) order: a ballot/prefix scan over
+//     that list, skipping hit slots, yields the oldest unselected slots in order -- no sort, no atomics;
+//   * the new order is written as [unselected non-victims in old order][fills by slot][hits by slot],
+//     which is exactly the ascending (rec, slot) order once fills get 2e and hits 2e+1 (epochs increase).
+// The host-to-device copies of the missing rows run in gather_kernel, a second launch whose grid scales
+// with the batch so that enough 16-byte host reads are in flight to fill the PCIe link.
+#include <climits>
+
+#include "hsk_internal.h"
+
+namespace hsk {
+
+__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix count of `flag` over the workgroup in thread order; *total gets the count.
+// Uses wave ballots plus one LDS slot per wave.  Must be called by every thread of the block.
+__device__ __forceinline__ int block_flag_scan(bool flag, int* total, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t mask = __ballot(flag);
+  const int below = __popcll(mask & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wsum[wave] = __popcll(mask);
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kResolveWaves; ++w) {
+    const int c = s_wsum[w];
+    base += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + below;
+}
+
+// Exclusive prefix sum of small non-negative ints over the workgroup in thread order.
+__device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wsum[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kResolveWaves; ++w) {
+    const int c = s_wsum[w];
+    base += (w < wave) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+enum { kDirectNone = 0, kDirectTail = 1, kDirectOpt = 2 };
+
+// Direct pass of one selection (Adaptive DHiSparse section 3.2, callout 1): tail, then a ready complete
+// optional page; returns the class and sets *loc for direct rows.
+__device__ __forceinline__ int classify(const ResolveArgs& a, int r, int64_t n, const int32_t* opt, int32_t p,
+                                        int32_t* loc) {
+  if (p >= n - a.T) {
+    *loc = (int32_t)((int64_t)a.R * a.B + (int64_t)r * a.T + (p % a.T));
+    return kDirectTail;
+  }
+  if (opt != nullptr && (int64_t)(p / a.P) < n / a.P) {
+    const int32_t g = opt[p / a.P];
+    if (g >= 0) {
+      *loc = (int32_t)(a.opt_base + (int64_t)g * a.P + (p % a.P));
+      return kDirectOpt;
+    }
+  }
+  return kDirectNone;
+}
+
+__global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a) {
+  __shared__ uint32_t s_hit[HSK_MAX_HOT_SLOTS / 32];
+  __shared__ uint32_t s_vic[HSK_MAX_HOT_SLOTS / 32];
+  __shared__ int32_t s_hit_pre[HSK_MAX_HOT_SLOTS / 32];
+  __shared__ int32_t s_vic_pre[HSK_MAX_HOT_SLOTS / 32];
+  __shared__ uint16_t s_order[HSK_MAX_HOT_SLOTS];
+  __shared__ uint16_t s_victim[HSK_MAX_HOT_SLOTS];
+  __shared__ int s_wsum[kResolveWaves];
+  __shared__ int s_cnt[4];
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int NT = kResolveThreads;
+  const int64_t n = a.ctx[r];
+  const int B = a.B;
+  const int nwords = (B + 31) >> 5;
+  const int total = a.Qmax * a.k;
+  const int nq = a.nq ? a.nq[r] : a.Qmax;
+  const bool nq_ok = nq >= 0 && nq <= a.Qmax;
+  const int nsel = nq_ok ? nq * a.k : 0;
+  const int32_t* sel = a.sel + (int64_t)r * total;
+  int32_t* locs = a.locs + (int64_t)r * total;
+  int32_t* key = a.m.key + (int64_t)r * B;
+  uint32_t* rec = a.m.rec + (int64_t)r * B;
+  uint16_t* order = a.m.order + (int64_t)r * B;
+  int32_t* pt = a.m.pt + (int64_t)r * a.max_ctx;
+  const int32_t* opt = a.m.opt ? a.m.opt + (int64_t)r * a.max_pages : nullptr;
+  int32_t* ppos = a.m.plan_pos + (int64_t)r * a.plan_cap;
+  int32_t* pdst = a.m.plan_dst + (int64_t)r * a.plan_cap;
+
+  // ---- phase 0: slot order to LDS, clear bitmaps; validate every selected position --------------------
+  for (int q = tid; q < B; q += NT) s_order[q] = order[q];
+  for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
+  if (tid < 4) s_cnt[tid] = 0;
+  bool bad = !nq_ok;
+  for (int f = tid; f < nsel; f += NT) {
+    const int32_t p = sel[f];
+    bad |= (p < 0) || ((int64_t)p >= n);
+  }
+  if (__syncthreads_or(bad)) {
+    for (int f = tid; f < total; f += NT) locs[f] = -1;
+    if (tid == 0) {
+      a.m.plan_n[r] = 0;
+      if (a.stats) {
+        hsk_stats z = {};
+        z.status = HSK_ERANGE;
+        a.stats[r] = z;
+      }
+      atomicCAS(a.err, 0, HSK_ERANGE);
+    }
+    return;
+  }
+
+  // ---- phase 1: direct pass, page-table probe, hit bitmap, first-occurrence claims of misses ----------
+  int my_tail = 0, my_opt = 0;
+  for (int f = tid; f < nsel; f += NT) {
+    const int32_t p = sel[f];
+    int32_t loc;
+    const int c = classify(a, r, n, opt, p, &loc);
+    if (c == kDirectTail) { ++my_tail; continue; }
+    if (c == kDirectOpt) { ++my_opt; continue; }
+    const int32_t s = pt[p];
+    if (s >= 0) atomicOr(&s_hit[s >> 5], 1u << (s & 31));
+    else atomicMin(&pt[p], INT_MIN + f);
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- phase 2: distinct misses in first-occurrence order (rounds of NT selections, ascending f) -------
+  int my_hit_sel = 0, my_miss_sel = 0;
+  int m = 0;
+  for (int base = 0; base < nsel; base += NT) {
+    const int f = base + tid;
+    bool first = false;
+    int32_t p = 0;
+    if (f < nsel) {
+      p = sel[f];
+      int32_t loc;
+      if (classify(a, r, n, opt, p, &loc) == kDirectNone) {
+        const int32_t v = ld_agent(&pt[p]);
+        if (v >= 0) ++my_hit_sel;
+        else { ++my_miss_sel; first = (v == INT_MIN + f); }
+      }
+    }
+    int cnt;
+    const int idx = block_flag_scan(first, &cnt, s_wsum);
+    if (first) ppos[m + idx] = p;
+    m += cnt;
+  }
+
+  // ---- phase 3: hit count, victims over the slot order, staging overflow check -----------------------
+  int nhit = 0;
+  {
+    const int hw = tid < nwords ? __popc(s_hit[tid]) : 0;
+    const int pre = block_sum_scan(hw, &nhit, s_wsum);
+    if (tid < nwords) s_hit_pre[tid] = pre;
+  }
+  const int free_slots = B - nhit;
+  const int v = m < free_slots ? m : free_slots;
+  const int over = m - v;
+  if (over > a.S) {
+    __threadfence();
+    __syncthreads();
+    for (int i = tid; i < m; i += NT) st_agent(&pt[ppos[i]], -1);
+    for (int f = tid; f < total; f += NT) locs[f] = -1;
+    if (tid == 0) {
+      a.m.plan_n[r] = 0;
+      if (a.stats) {
+        hsk_stats z = {};
+        z.status = HSK_ESTAGE;
+        a.stats[r] = z;
+      }
+      atomicCAS(a.err, 0, HSK_ESTAGE);
+    }
+    return;
+  }
+  const int n_keep = free_slots - v;
+  {
+    int nonhit_base = 0;
+    for (int base = 0; base < B; base += NT) {
+      const int q = base + tid;
+      bool nh = false;
+      int s = 0;
+      if (q < B) {
+        s = s_order[q];
+        nh = ((s_hit[s >> 5] >> (s & 31)) & 1u) == 0u;
+      }
+      int cnt;
+      const int rank = nonhit_base + block_flag_scan(nh, &cnt, s_wsum);
+      if (nh) {
+        if (rank < v) {
+          s_victim[rank] = (uint16_t)s;
+          atomicOr(&s_vic[s >> 5], 1u << (s & 31));
+        } else {
+          order[rank - v] = (uint16_t)s;  // unselected non-victims keep their relative order
+        }
+      }
+      nonhit_base += cnt;
+    }
+  }
+  __syncthreads();
+  {
+    const int vw = tid < nwords ? __popc(s_vic[tid]) : 0;
+    int vtot;
+    const int pre = block_sum_scan(vw, &vtot, s_wsum);
+    if (tid < nwords) s_vic_pre[tid] = pre;
+  }
+  __syncthreads();
+
+  // ---- phase 4: metadata update -- fills (2e) then hits (2e+1) at the most recent end ------------------
+  const uint32_t e2 = 2u * a.epoch;
+  for (int s = tid; s < B; s += NT) {
+    const int w = s >> 5;
+    const uint32_t bit = 1u << (s & 31), below = bit - 1u;
+    if (s_vic[w] & bit) {
+      order[n_keep + s_vic_pre[w] + __popc(s_vic[w] & below)] = (uint16_t)s;
+    } else if (s_hit[w] & bit) {
+      order[n_keep + v + s_hit_pre[w] + __popc(s_hit[w] & below)] = (uint16_t)s;
+      rec[s] = e2 + 1u;
+    }
+  }
+  for (int i = tid; i < m; i += NT) {
+    const int32_t p = ppos[i];
+    if (i < v) {
+      const int s = s_victim[i];
+      const int32_t old = key[s];
+      if (old >= 0) st_agent(&pt[old], -1);  // eviction: old is not selected in this call
+      key[s] = p;
+      rec[s] = e2;
+      st_agent(&pt[p], s);
+      pdst[i] = (int32_t)((int64_t)r * B + s);
+    } else {
+      st_agent(&pt[p], -2 - (i - v));  // staged: a transient code read back by the emit phase
+      pdst[i] = (int32_t)(a.stg_base + (int64_t)r * a.S + (i - v));
+    }
+  }
+  __threadfence();
+  __syncthreads();
+
+  // ---- phase 5: publish locations in selection order ---------------------------------------------------
+  for (int f = tid; f < total; f += NT) {
+    int32_t loc = -1;
+    if (f < nsel) {
+      const int32_t p = sel[f];
+      if (classify(a, r, n, opt, p, &loc) == kDirectNone) {
+        const int32_t s = ld_agent(&pt[p]);
+        loc = s >= 0 ? (int32_t)((int64_t)r * B + s) : (int32_t)(a.stg_base + (int64_t)r * a.S + (-2 - s));
+      }
+    }
+    locs[f] = loc;
+  }
+  atomicAdd(&s_cnt[0], my_tail);
+  atomicAdd(&s_cnt[1], my_opt);
+  atomicAdd(&s_cnt[2], my_hit_sel);
+  atomicAdd(&s_cnt[3], my_miss_sel);
+  __threadfence();
+  __syncthreads();
+  // staged rows stay outside the hot cache: clear their transient page-table codes
+  for (int i = v + tid; i < m; i += NT) st_agent(&pt[ppos[i]], -1);
+  if (tid == 0) {
+    a.m.plan_n[r] = m;
+    if (a.stats) {
+      hsk_stats st;
+      st.n_sel = nsel;
+      st.n_tail = s_cnt[0];
+      st.n_opt = s_cnt[1];
+      st.n_hit = nhit;
+      st.n_hit_sel = s_cnt[2];
+      st.n_miss = m;
+      st.n_miss_sel = s_cnt[3];
+      st.n_staged = over;
+      st.status = HSK_OK;
+      st.reserved = 0;
+      st.fetched_bytes = (int64_t)m * a.row_bytes;
+      a.stats[r] = st;
+    }
+  }
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy one row of `chunks` 16-byte chunks with the 64 lanes of a wave: all loads first, then stores.
+__device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int chunks,
+                                              int lane) {
+  constexpr int kDepth = 8;
+  for (int c0 = 0; c0 < chunks; c0 += 64 * kDepth) {
+    u32x4 buf[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int c = c0 + d * 64 + lane;
+      if (c < chunks) buf[d] = __builtin_nontemporal_load(src + c);
+    }
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      const int c = c0 + d * 64 + lane;
+      if (c < chunks) dst[c] = buf[d];
+    }
+  }
+}
+
+// Host -> device gather of a miss plan (HiSparse section 3.4 phase 4, section 3.5 replay): every wave
+// copies whole rows from pinned host memory (zero-copy 16-byte loads over PCIe) into their pool rows.
+// Grid: (blocks per request, requests); each request's rows are spread over its blocks' waves.
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs g) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGatherThreads / 64;
+  const int m = g.plan_n[r];
+  const int chunks = g.row_bytes >> 4;
+  const char* hbase = g.host + (int64_t)r * g.host_req_stride;
+  const int32_t* pp = g.plan_pos + (int64_t)r * g.plan_cap;
+  const int32_t* pd = g.plan_dst + (int64_t)r * g.plan_cap;
+  for (int i = blockIdx.x * kWaves + wave; i < m; i += gridDim.x * kWaves) {
+    const u32x4* src = (const u32x4*)(hbase + (int64_t)pp[i] * g.row_bytes);
+    u32x4* dst = (u32x4*)(g.pool + (int64_t)pd[i] * g.row_bytes);
+    wave_copy_row(src, dst, chunks, lane);
+  }
+}
+
+// Tail rows [n_r - T, n_r) of every request: host -> pool row R*B + r*T + (p mod T).
+__global__ __launch_bounds__(kGatherThreads) void tail_copy_kernel(const char* host, int64_t stride, char* pool,
+                                                                   const int64_t* ctx, int32_t R, int32_t B,
+                                                                   int32_t T, int32_t row_bytes) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGatherThreads / 64;
+  const int64_t n = ctx[r];
+  for (int t = blockIdx.x * kWaves + wave; t < T; t += gridDim.x * kWaves) {
+    const int64_t p = n - T + t;
+    if (p < 0) continue;
+    const u32x4* src = (const u32x4*)(host + r * stride + p * row_bytes);
+    u32x4* dst = (u32x4*)(pool + ((int64_t)R * B + (int64_t)r * T + (p % T)) * row_bytes);
+    wave_copy_row(src, dst, row_bytes >> 4, lane);
+  }
+}
+
+// Contiguous byte runs host -> pool (optional-history population); one block per run.
+__global__ __launch_bounds__(kGatherThreads) void copy_runs_kernel(const char* host, char* pool, const CopyRun* runs) {
+  const CopyRun run = runs[blockIdx.x];
+  const u32x4* src = (const u32x4*)(host + run.src);
+  u32x4* dst = (u32x4*)(pool + run.dst);
+  const int64_t chunks = run.bytes >> 4;
+  for (int64_t c = threadIdx.x; c < chunks; c += kGatherThreads) dst[c] = __builtin_nontemporal_load(src + c);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void init_order_kernel(uint16_t* order, uint32_t* rec, int64_t total, int32_t B) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    order[i] = (uint16_t)(i % B);
+    rec[i] = 0u;
+  }
+}
+
+static unsigned grid_for(int64_t n, int threads) {
+  int64_t g = (n + threads - 1) / threads;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (unsigned)g;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_meta(const SourceMeta& m, int32_t R, int32_t B, int64_t max_ctx, int64_t max_pages,
+                            hipStream_t s) {
+  hipError_t e;
+  if ((e = launch_fill_i32(m.key, (int64_t)R * B, -1, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(init_order_kernel, dim3(grid_for((int64_t)R * B, 256)), dim3(256), 0, s, m.order, m.rec,
+                     (int64_t)R * B, B);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_fill_i32(m.pt, (int64_t)R * max_ctx, -1, s)) != hipSuccess) return e;
+  if (m.opt && (e = launch_fill_i32(m.opt, (int64_t)R * max_pages, -1, s)) != hipSuccess) return e;
+  return launch_fill_i32(m.plan_n, R, 0, s);
+}
+
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(resolve_kernel, dim3(a.R), dim3(kResolveThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks_per_req, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks_per_req, R), dim3(kGatherThreads), 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_copy(const char* host, int64_t stride, char* pool, const int64_t* d_ctx, int32_t R,
+                            int32_t B, int32_t T, int32_t row_bytes, hipStream_t s) {
+  const int blocks = (T + 3) / 4 < 64 ? (T + 3) / 4 : 64;
+  hipLaunchKernelGGL(tail_copy_kernel, dim3(blocks > 0 ? blocks : 1, R), dim3(kGatherThreads), 0, s, host, stride,
+                     pool, d_ctx, R, B, T, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_runs(const char* host, char* pool, const CopyRun* runs, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_runs_kernel, dim3(n), dim3(kGatherThreads), 0, s, host, pool, runs);
+  return hipGetLastError();
+}
+
+}  // namespace hsk

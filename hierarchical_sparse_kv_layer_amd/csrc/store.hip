@@ -1,0 +1,372 @@
+// Host runtime of libhsk.so: store lifetime, workspace layout, residency, resolve/attention entry points.
+//
+// Data layout in HBM (caller-owned):
+//   workspace: per request context lengths, a sticky error word, then per source
+//              key[R][B] i32, rec[R][B] u32, order[R][B] u16, pt[R][max_ctx] i32, opt[R][max_pages] i32,
+//              plan_n[R] i32, plan_pos[R][Qmax*k] i32, plan_dst[R][Qmax*k] i32 (each region 256-B aligned)
+//   pool:      per source rows_per_source rows of row_bytes: [R*B hot | R*T tail | optional pages | R*S staging]
+// Host (library-owned, pinned and mapped): per host source R x max_ctx rows of row_bytes.
+#include <algorithm>
+#include <cstring>
+#include <new>
+
+#include "hsk_internal.h"
+
+namespace hsk {
+
+static int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t rows_per_source(const hsk_desc& d) {
+  return (int64_t)d.num_requests * d.hot_slots + (int64_t)d.num_requests * d.tail_rows +
+         d.opt_pool_pages * d.page_rows + (int64_t)d.num_requests * d.staging_rows;
+}
+
+static bool valid_desc(const hsk_desc* d) {
+  if (!d) return false;
+  if (d->num_requests < 1 || d->num_sources < 1) return false;
+  if (d->row_bytes <= 0 || d->row_bytes % 16 != 0) return false;
+  if (d->hot_slots < 1 || d->hot_slots > HSK_MAX_HOT_SLOTS) return false;
+  if (d->tail_rows < 0 || d->page_rows < 0 || d->opt_pool_pages < 0 || d->staging_rows < 0) return false;
+  if (d->page_rows == 0 && d->opt_pool_pages != 0) return false;
+  if (d->max_queries < 1 || d->top_k < 1) return false;
+  if ((int64_t)d->max_queries * d->top_k > HSK_MAX_SELECTIONS_PER_REQUEST) return false;
+  if (d->max_ctx < 1 || d->max_ctx > 0x7fffffffLL || !d->ctx_len) return false;
+  if (d->gather_mode != HSK_GATHER_ZEROCOPY && d->gather_mode != HSK_GATHER_NO_IO) return false;
+  if (d->gather_blocks < 0 || d->host_alias_sources < 0 || d->host_alias_sources > 1) return false;
+  for (int32_t r = 0; r < d->num_requests; ++r)
+    if (d->ctx_len[r] < 1 || d->ctx_len[r] > d->max_ctx) return false;
+  if (rows_per_source(*d) > 0x7fffffffLL) return false;  // locations are int32 rows
+  return true;
+}
+
+bool layout_workspace(const hsk_desc& d, WorkspaceLayout* L) {
+  const int64_t R = d.num_requests, B = d.hot_slots;
+  const int64_t max_pages = d.page_rows ? d.max_ctx / d.page_rows : 0;
+  const int64_t cap = (int64_t)d.max_queries * d.top_k;
+  int64_t off = 0;
+  L->ctx = off; off = align_up(off + 8 * R);
+  L->err = off; off = align_up(off + 4);
+  L->key.clear(); L->rec.clear(); L->order.clear(); L->pt.clear(); L->opt.clear();
+  L->plan_n.clear(); L->plan_pos.clear(); L->plan_dst.clear();
+  for (int32_t s = 0; s < d.num_sources; ++s) {
+    L->key.push_back(off); off = align_up(off + 4 * R * B);
+    L->rec.push_back(off); off = align_up(off + 4 * R * B);
+    L->order.push_back(off); off = align_up(off + 2 * R * B);
+    L->pt.push_back(off); off = align_up(off + 4 * R * d.max_ctx);
+    L->opt.push_back(off); off = align_up(off + 4 * R * max_pages);
+    L->plan_n.push_back(off); off = align_up(off + 4 * R);
+    L->plan_pos.push_back(off); off = align_up(off + 4 * R * cap);
+    L->plan_dst.push_back(off); off = align_up(off + 4 * R * cap);
+  }
+  L->total = off;
+  return true;
+}
+
+}  // namespace hsk
+
+using namespace hsk;
+
+extern "C" {
+
+const char* hsk_status_str(hsk_status s) {
+  switch (s) {
+    case HSK_OK: return "HSK_OK";
+    case HSK_EINVAL: return "HSK_EINVAL: bad argument or shape";
+    case HSK_ENOMEM: return "HSK_ENOMEM: pinned host allocation failed";
+    case HSK_EHIP: return "HSK_EHIP: HIP runtime call failed";
+    case HSK_ESTATE: return "HSK_ESTATE: call not valid in this state";
+    case HSK_ERANGE: return "HSK_ERANGE: selected position outside the request's history";
+    case HSK_ESTAGE: return "HSK_ESTAGE: missing rows exceed free hot slots plus staging";
+    case HSK_EEPOCH: return "HSK_EEPOCH: epoch not greater than the source's last epoch";
+    default: return "unknown hsk_status";
+  }
+}
+
+hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, size_t* pool_bytes) {
+  if (!valid_desc(desc) || !workspace_bytes || !pool_bytes) return HSK_EINVAL;
+  WorkspaceLayout L;
+  layout_workspace(*desc, &L);
+  *workspace_bytes = (size_t)L.total;
+  *pool_bytes = (size_t)rows_per_source(*desc) * desc->num_sources * desc->row_bytes;
+  return HSK_OK;
+}
+
+void hsk_kv_store_destroy(hsk_store* st) {
+  if (!st) return;
+  (void)hipDeviceSynchronize();
+  for (char* h : st->host)
+    if (h) (void)hipHostFree(h);
+  if (st->h_stage) (void)hipHostFree(st->h_stage);
+  delete st;
+}
+
+hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_pool, hsk_stream_t stream,
+                             hsk_store** out) {
+  if (!out) return HSK_EINVAL;
+  *out = nullptr;
+  if (!valid_desc(desc) || !d_workspace || !d_pool) return HSK_EINVAL;
+  if (((uintptr_t)d_workspace % kAlign) || ((uintptr_t)d_pool % kAlign)) return HSK_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  hsk_store* st = new (std::nothrow) hsk_store();
+  if (!st) return HSK_ENOMEM;
+  st->d = *desc;
+  st->ctx.assign(desc->ctx_len, desc->ctx_len + desc->num_requests);
+  st->d.ctx_len = st->ctx.data();
+  const int32_t R = desc->num_requests, B = desc->hot_slots;
+  st->max_pages = desc->page_rows ? desc->max_ctx / desc->page_rows : 0;
+  st->plan_cap = desc->max_queries * desc->top_k;
+  st->rows_per_src = rows_per_source(*desc);
+  st->host_sources = desc->host_alias_sources ? 1 : desc->num_sources;
+  st->ws = (char*)d_workspace;
+  st->pool = (char*)d_pool;
+  if (hipGetDevice(&st->device) != hipSuccess) { delete st; return HSK_EHIP; }
+  WorkspaceLayout L;
+  layout_workspace(*desc, &L);
+  st->d_ctx = (int64_t*)(st->ws + L.ctx);
+  st->d_err = (int32_t*)(st->ws + L.err);
+  for (int32_t k = 0; k < desc->num_sources; ++k) {
+    SourceMeta m;
+    m.key = (int32_t*)(st->ws + L.key[k]);
+    m.rec = (uint32_t*)(st->ws + L.rec[k]);
+    m.order = (uint16_t*)(st->ws + L.order[k]);
+    m.pt = (int32_t*)(st->ws + L.pt[k]);
+    m.opt = st->max_pages ? (int32_t*)(st->ws + L.opt[k]) : nullptr;
+    m.plan_n = (int32_t*)(st->ws + L.plan_n[k]);
+    m.plan_pos = (int32_t*)(st->ws + L.plan_pos[k]);
+    m.plan_dst = (int32_t*)(st->ws + L.plan_dst[k]);
+    st->meta.push_back(m);
+  }
+  st->last_epoch.assign(desc->num_sources, 0u);
+  st->opt_mirror.assign((size_t)desc->num_sources * R, std::vector<int32_t>());
+  for (auto& v : st->opt_mirror) v.assign((size_t)st->max_pages, -1);
+  // pinned, device-mapped host rows
+  const size_t host_bytes = (size_t)R * (size_t)desc->max_ctx * (size_t)desc->row_bytes;
+  for (int32_t k = 0; k < st->host_sources; ++k) {
+    void* h = nullptr;
+    if (hipHostMalloc(&h, host_bytes, hipHostMallocMapped) != hipSuccess || !h) {
+      (void)hipGetLastError();
+      hsk_kv_store_destroy(st);
+      return HSK_ENOMEM;
+    }
+    st->host.push_back((char*)h);
+  }
+  st->h_stage_bytes = std::max<size_t>(1 << 20, (size_t)st->max_pages * sizeof(CopyRun) + 4 * (size_t)st->max_pages);
+  if (hipHostMalloc(&st->h_stage, st->h_stage_bytes, hipHostMallocMapped) != hipSuccess) {
+    (void)hipGetLastError();
+    hsk_kv_store_destroy(st);
+    return HSK_ENOMEM;
+  }
+  // metadata: empty caches, slot order 0..B-1
+  if (hipMemcpyAsync(st->d_ctx, st->ctx.data(), sizeof(int64_t) * R, hipMemcpyHostToDevice, s) != hipSuccess ||
+      launch_fill_i32(st->d_err, 1, 0, s) != hipSuccess) {
+    hsk_kv_store_destroy(st);
+    return HSK_EHIP;
+  }
+  for (int32_t k = 0; k < desc->num_sources; ++k) {
+    if (launch_init_meta(st->meta[k], R, B, desc->max_ctx, st->max_pages, s) != hipSuccess) {
+      hsk_kv_store_destroy(st);
+      return HSK_EHIP;
+    }
+  }
+  // the context-length copy reads pageable host memory owned by the store: wait for it
+  if (hipStreamSynchronize(s) != hipSuccess) { hsk_kv_store_destroy(st); return HSK_EHIP; }
+  *out = st;
+  return HSK_OK;
+}
+
+hsk_status hsk_host_rows(hsk_store* st, int32_t source, int32_t req, void** h_rows, int64_t* n_rows) {
+  if (!st || !h_rows || !n_rows || source < 0 || source >= st->d.num_sources || req < 0 ||
+      req >= st->d.num_requests)
+    return HSK_EINVAL;
+  const int32_t hs = st->d.host_alias_sources ? 0 : source;
+  *h_rows = st->host[hs] + (size_t)req * (size_t)st->d.max_ctx * (size_t)st->d.row_bytes;
+  *n_rows = st->d.max_ctx;
+  return HSK_OK;
+}
+
+hsk_status hsk_pool_base(hsk_store* st, int32_t source, void** d_pool_source) {
+  if (!st || !d_pool_source || source < 0 || source >= st->d.num_sources) return HSK_EINVAL;
+  *d_pool_source = st->pool + (size_t)source * (size_t)st->rows_per_src * (size_t)st->d.row_bytes;
+  return HSK_OK;
+}
+
+hsk_status hsk_commit_prefill(hsk_store* st, hsk_stream_t stream) {
+  if (!st) return HSK_EINVAL;
+  if (st->d.tail_rows == 0) return HSK_OK;
+  const int64_t stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
+  for (int32_t k = 0; k < st->d.num_sources; ++k) {
+    void* pool;
+    hsk_pool_base(st, k, &pool);
+    const int32_t hs = st->d.host_alias_sources ? 0 : k;
+    HSK_HIP(launch_tail_copy(st->host[hs], stride, (char*)pool, st->d_ctx, st->d.num_requests, st->d.hot_slots,
+                             st->d.tail_rows, st->d.row_bytes, (hipStream_t)stream));
+  }
+  return HSK_OK;
+}
+
+hsk_status hsk_residency_set(hsk_store* st, int32_t source, int32_t req, const int32_t* h_page_ids,
+                             int64_t n_pages, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;
+  if (st->d.page_rows == 0) return HSK_ESTATE;
+  const int64_t complete = st->ctx[req] / st->d.page_rows;
+  if (n_pages < 0 || n_pages > complete || (n_pages > 0 && !h_page_ids)) return HSK_EINVAL;
+  for (int64_t g = 0; g < n_pages; ++g)
+    if (h_page_ids[g] < -1 || h_page_ids[g] >= st->d.opt_pool_pages) return HSK_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t>& mirror = st->opt_mirror[(size_t)source * st->d.num_requests + req];
+  const int64_t P = st->d.page_rows, rb = st->d.row_bytes;
+  const int64_t opt_base_row = (int64_t)st->d.num_requests * st->d.hot_slots + (int64_t)st->d.num_requests * st->d.tail_rows;
+  int32_t* d_map = st->meta[source].opt + (size_t)req * st->max_pages;
+  bool all_drop = true, any_change = false;
+  for (int64_t g = 0; g < n_pages; ++g) {
+    if (h_page_ids[g] >= 0) all_drop = false;
+    if (h_page_ids[g] != mirror[g]) any_change = true;
+  }
+  if (!any_change) return HSK_OK;
+  if (all_drop) {
+    // reclaim: clear the ready locations in stream order, after earlier readers; no host staging needed
+    HSK_HIP(launch_fill_i32(d_map, n_pages, -1, s));
+    for (int64_t g = 0; g < n_pages; ++g) mirror[g] = -1;
+    return HSK_OK;
+  }
+  // population: copy newly mapped pages, then publish the map after the copies (same stream)
+  CopyRun* runs = (CopyRun*)st->h_stage;
+  int32_t* map_stage = (int32_t*)((char*)st->h_stage + sizeof(CopyRun) * (size_t)st->max_pages);
+  int32_t nrun = 0;
+  const int64_t host_off = (int64_t)req * st->d.max_ctx * rb;
+  for (int64_t g = 0; g < n_pages; ++g) {
+    int32_t id = h_page_ids[g];
+    if (id < 0 || id == mirror[g]) continue;
+    int64_t src = host_off + g * P * rb;
+    int64_t dst = (opt_base_row + (int64_t)id * P) * rb;
+    if (nrun > 0 && runs[nrun - 1].src + runs[nrun - 1].bytes == src && runs[nrun - 1].dst + runs[nrun - 1].bytes == dst) {
+      runs[nrun - 1].bytes += P * rb;
+    } else {
+      runs[nrun].src = src; runs[nrun].dst = dst; runs[nrun].bytes = P * rb;
+      ++nrun;
+    }
+  }
+  for (int64_t g = 0; g < n_pages; ++g) map_stage[g] = h_page_ids[g];
+  void* pool;
+  hsk_pool_base(st, source, &pool);
+  const int32_t hs = st->d.host_alias_sources ? 0 : source;
+  if (nrun > 0) HSK_HIP(launch_copy_runs(st->host[hs], (char*)pool, runs, nrun, s));
+  HSK_HIP(hipMemcpyAsync(d_map, map_stage, sizeof(int32_t) * (size_t)n_pages, hipMemcpyHostToDevice, s));
+  HSK_HIP(hipStreamSynchronize(s));  // the staging buffer is reused by the next call
+  for (int64_t g = 0; g < n_pages; ++g) mirror[g] = h_page_ids[g];
+  return HSK_OK;
+}
+
+hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t deficit, int32_t* q_out) {
+  if (!q_out || n < 0 || (n > 0 && !h_pages_held)) return HSK_EINVAL;
+  if (deficit <= 0) { *q_out = 0; return HSK_OK; }
+  int64_t acc = 0;
+  for (int32_t q = 0; q < n; ++q) {
+    if (h_pages_held[q] < 0) return HSK_EINVAL;
+    acc += h_pages_held[q];
+    if (acc >= deficit) { *q_out = q + 1; return HSK_OK; }
+  }
+  *q_out = -1;
+  return HSK_OK;
+}
+
+static int32_t gather_blocks_for(const hsk_store* st) {
+  if (st->d.gather_blocks > 0) return st->d.gather_blocks;
+  int32_t g = 1024 / st->d.num_requests;
+  return std::max(1, std::min(64, g));
+}
+
+hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, const int32_t* d_nq,
+                            int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs) return HSK_EINVAL;
+  if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
+  hipStream_t s = (hipStream_t)stream;
+  ResolveArgs a;
+  a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats; a.ctx = st->d_ctx; a.m = st->meta[source];
+  a.err = st->d_err; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
+  const int64_t R = st->d.num_requests;
+  a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
+  a.stg_base = a.opt_base + st->d.opt_pool_pages * st->d.page_rows;
+  a.plan_cap = st->plan_cap;
+  a.R = st->d.num_requests; a.B = st->d.hot_slots; a.T = st->d.tail_rows; a.P = st->d.page_rows;
+  a.S = st->d.staging_rows; a.Qmax = st->d.max_queries; a.k = st->d.top_k; a.row_bytes = st->d.row_bytes;
+  a.epoch = epoch;
+  HSK_HIP(launch_resolve(a, s));
+  st->last_epoch[source] = epoch;
+  if (st->d.gather_mode == HSK_GATHER_ZEROCOPY) {
+    void* pool;
+    hsk_pool_base(st, source, &pool);
+    GatherArgs g;
+    const int32_t hs = st->d.host_alias_sources ? 0 : source;
+    g.host = st->host[hs]; g.pool = (char*)pool;
+    g.plan_n = a.m.plan_n; g.plan_pos = a.m.plan_pos; g.plan_dst = a.m.plan_dst;
+    g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
+    g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
+    HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
+  }
+  return HSK_OK;
+}
+
+hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
+  if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
+      dst_source >= st->d.num_sources)
+    return HSK_EINVAL;
+  if (st->d.gather_mode != HSK_GATHER_ZEROCOPY) return HSK_OK;
+  void* pool;
+  hsk_pool_base(st, dst_source, &pool);
+  GatherArgs g;
+  const int32_t hs = st->d.host_alias_sources ? 0 : dst_source;
+  g.host = st->host[hs]; g.pool = (char*)pool;
+  g.plan_n = st->meta[plan_source].plan_n; g.plan_pos = st->meta[plan_source].plan_pos;
+  g.plan_dst = st->meta[plan_source].plan_dst;
+  g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
+  g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
+  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), (hipStream_t)stream));
+  return HSK_OK;
+}
+
+hsk_status hsk_snapshot(hsk_store* st, int32_t source, int32_t req, int32_t* key, uint32_t* rec, uint16_t* order,
+                        int32_t* pt, int32_t* opt) {
+  if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;
+  HSK_HIP(hipDeviceSynchronize());
+  const SourceMeta& m = st->meta[source];
+  const size_t B = st->d.hot_slots;
+  if (key) HSK_HIP(hipMemcpy(key, m.key + req * B, 4 * B, hipMemcpyDeviceToHost));
+  if (rec) HSK_HIP(hipMemcpy(rec, m.rec + req * B, 4 * B, hipMemcpyDeviceToHost));
+  if (order) HSK_HIP(hipMemcpy(order, m.order + req * B, 2 * B, hipMemcpyDeviceToHost));
+  if (pt) HSK_HIP(hipMemcpy(pt, m.pt + (size_t)req * st->d.max_ctx, 4 * (size_t)st->ctx[req], hipMemcpyDeviceToHost));
+  if (opt && st->max_pages) {
+    const size_t np = (size_t)(st->ctx[req] / st->d.page_rows);
+    if (np) HSK_HIP(hipMemcpy(opt, m.opt + (size_t)req * st->max_pages, 4 * np, hipMemcpyDeviceToHost));
+  }
+  return HSK_OK;
+}
+
+hsk_status hsk_read_plan(hsk_store* st, int32_t source, int32_t req, int32_t* pos, int32_t* dst, int32_t cap,
+                         int32_t* n) {
+  if (!st || !n || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests || cap < 0)
+    return HSK_EINVAL;
+  HSK_HIP(hipDeviceSynchronize());
+  const SourceMeta& m = st->meta[source];
+  int32_t cnt = 0;
+  HSK_HIP(hipMemcpy(&cnt, m.plan_n + req, 4, hipMemcpyDeviceToHost));
+  *n = cnt;
+  const size_t w = (size_t)std::min(cnt, cap);
+  if (w && pos) HSK_HIP(hipMemcpy(pos, m.plan_pos + (size_t)req * st->plan_cap, 4 * w, hipMemcpyDeviceToHost));
+  if (w && dst) HSK_HIP(hipMemcpy(dst, m.plan_dst + (size_t)req * st->plan_cap, 4 * w, hipMemcpyDeviceToHost));
+  return HSK_OK;
+}
+
+hsk_status hsk_sync_status(hsk_store* st, hsk_stream_t stream) {
+  if (!st) return HSK_EINVAL;
+  HSK_HIP(hipStreamSynchronize((hipStream_t)stream));
+  int32_t e = 0;
+  HSK_HIP(hipMemcpy(&e, st->d_err, 4, hipMemcpyDeviceToHost));
+  if (e != 0) {
+    HSK_HIP(launch_fill_i32(st->d_err, 1, 0, (hipStream_t)stream));
+    HSK_HIP(hipStreamSynchronize((hipStream_t)stream));
+  }
+  return e;
+}
+
+}  // extern "C"

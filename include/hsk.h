@@ -1,0 +1,235 @@
+/*
+ * hsk -- hierarchical sparse KV resolve + sparse decode attention for MI355X (gfx950).
+ *
+ * C ABI of libhsk.so.  Plain pointers and sizes only; every call returns an hsk_status and never throws.
+ *
+ * What the library does, per decode step and layer (the hot path):
+ *   1. hsk_resolve_step: the model's top-k selected positions of each request ("logical indices in") are
+ *      turned into physical rows of a device pool ("physical slots out"), as the fused Resolve kernel of
+ *      "HiSparse: Scaling Sparse-Attention Decoding with Hierarchical KV Cache Management" (section 3.4)
+ *      does: tail rows and ready optional-history pages resolve directly ("Adaptive DHiSparse:
+ *      Speculative Decoding over a Load-Adaptive KV Hierarchy", section 3.2, Figure 2 callout 1), the
+ *      rest are looked up in a per-request hot cache of B slots managed by LRU with hits ranked above the
+ *      same step's fills (HiSparse section 3.2), and missing rows are copied from a pinned host-memory
+ *      store into LRU victim slots, or into staging rows when a multi-query union overflows the free slots
+ *      (Adaptive DHiSparse section 3.3, Eqs. 5-6).  Each distinct missing row is copied once.
+ *   2. hsk_sparse_decode_attn: exact softmax attention of each query over the rows at the emitted
+ *      locations (MLA: 576-wide rows, keys = row[0:dk], values = row[0:dv]; GQA: 16-token pages).
+ *
+ * Ownership: the library owns the opaque store and its pinned host KV rows (allocated with hipHostMalloc,
+ * freed by hsk_kv_store_destroy).  The caller owns every device buffer (workspace, pool, selections,
+ * locations, queries, outputs, statistics, attention scratch) and every stream; device buffers must stay
+ * valid until the work queued on them completes.  A store is not thread-safe; calls on one source are
+ * ordered by the stream they are issued on.
+ *
+ * Errors: argument and ordering errors return synchronously and change nothing.  Errors found on the
+ * device (a selected position outside [0, n_r): HSK_ERANGE; a multi-query union that overflows staging:
+ * HSK_ESTAGE) are written to that request's hsk_stats.status, leave that request's metadata unchanged,
+ * set every location of that request to -1, and are also latched in a sticky store word that
+ * hsk_sync_status returns and clears.
+ */
+#ifndef HSK_H
+#define HSK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hsk_status;
+enum {
+  HSK_OK = 0,
+  HSK_EINVAL = -1,  /* bad argument or shape */
+  HSK_ENOMEM = -2,  /* pinned host allocation failed */
+  HSK_EHIP = -3,    /* a HIP runtime call failed */
+  HSK_ESTATE = -4,  /* call not valid in the store's state */
+  HSK_ERANGE = -5,  /* a selected position is outside [0, n_r) */
+  HSK_ESTAGE = -6,  /* a request's missing rows exceed its free hot slots plus its staging rows */
+  HSK_EEPOCH = -7   /* epoch not greater than the last epoch resolved on that source */
+};
+
+/* A hipStream_t, passed as a plain pointer; NULL is the null stream. */
+typedef void* hsk_stream_t;
+
+/* Gather modes.  HSK_GATHER_NO_IO skips the host reads (the rows left in the slots are stale): it is a
+ * timing bound only, like the no-IO oracle of HiSparse section 4.6, and never a correct result. */
+enum { HSK_GATHER_ZEROCOPY = 0, HSK_GATHER_NO_IO = 1 };
+
+/* Limits of this build. */
+#define HSK_MAX_HOT_SLOTS 8192
+#define HSK_MAX_SELECTIONS_PER_REQUEST 65536
+
+/*
+ * Store description.  Sizes are in rows unless noted.  A "row" is what one selected position names: one
+ * token's KV record (MLA: 576 bf16 = 1,152 B) or one page of tokens (GQA: 16 tokens x [K|V] = 8,192 B).
+ *
+ * Per source and request the device pool holds B hot slots, T tail rows and S staging rows; each source
+ * also has an optional-history pool of opt_pool_pages pages of page_rows rows.  Pool row layout of one
+ * source (row indices are what hsk_resolve_step emits):
+ *     hot      r*B + slot                                   r < R, slot < B
+ *     tail     R*B + r*T + (p mod T)                        positions p >= n_r - T
+ *     optional R*B + R*T + g*page_rows + (p mod page_rows)  page id g of a ready complete page
+ *     staging  R*B + R*T + opt_pool_pages*page_rows + r*S + c
+ */
+typedef struct hsk_desc {
+  int32_t num_requests;        /* R: resolution units (requests, or request x KV head for GQA pages) */
+  int32_t num_sources;         /* payload sources; each has its own host rows, pool region and metadata */
+  int32_t row_bytes;           /* bytes per row; a positive multiple of 16 */
+  int32_t hot_slots;           /* B: 1..HSK_MAX_HOT_SLOTS; B >= top_k keeps one query's selection in cache */
+  int32_t tail_rows;           /* T >= 0: newest rows of each request, always resident */
+  int32_t page_rows;           /* rows per optional-history page; 0 disables optional history */
+  int64_t opt_pool_pages;      /* optional-history pages per source (0 if page_rows == 0) */
+  int32_t max_queries;         /* Qmax >= 1: queries per request in one resolve call */
+  int32_t top_k;               /* k >= 1: selections per query */
+  int32_t staging_rows;        /* S >= 0: per request and source */
+  int32_t host_alias_sources;  /* 1: every source reads source 0's host rows (one host payload) */
+  int64_t max_ctx;             /* rows of host history reserved per request and source */
+  const int64_t* ctx_len;      /* host array [R]: n_r, 1 <= n_r <= max_ctx, n_r < 2^31 */
+  int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
+  int32_t gather_blocks;       /* workgroups per request in the gather kernel; 0 = automatic */
+} hsk_desc;
+
+/* Per-request result of one resolve call (device memory, written by hsk_resolve_step). */
+typedef struct hsk_stats {
+  int32_t n_sel;       /* selections examined: nq[r] * k */
+  int32_t n_tail;      /* selections resolved from the tail */
+  int32_t n_opt;       /* selections resolved from ready optional-history pages */
+  int32_t n_hit;       /* distinct hot slots hit */
+  int32_t n_hit_sel;   /* selections resolved by hot hits */
+  int32_t n_miss;      /* distinct rows copied from host (hot fills + staged) */
+  int32_t n_miss_sel;  /* selections resolved by this call's copies */
+  int32_t n_staged;    /* distinct rows copied into staging */
+  int32_t status;      /* HSK_OK, HSK_ERANGE or HSK_ESTAGE */
+  int32_t reserved;
+  int64_t fetched_bytes; /* n_miss * row_bytes */
+} hsk_stats;
+
+typedef struct hsk_store hsk_store;
+
+/* Device memory the caller must provide for a store described by *desc: the metadata workspace and the
+ * row pool of all sources.  Both must be 256-byte aligned. */
+hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, size_t* pool_bytes);
+
+/* Create a store over caller-owned device memory (sizes from hsk_workspace_bytes) and allocate its pinned
+ * host rows (num_sources, or 1 with host_alias_sources, x R x max_ctx x row_bytes).  Metadata is set empty
+ * on `stream`: keys -1, recency 0, page tables -1, optional maps -1, slot order 0..B-1.  The host rows are
+ * uninitialised: the caller writes them (hsk_host_rows) before hsk_commit_prefill.
+ * Returns HSK_ENOMEM if the pinned allocation fails. */
+hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_pool, hsk_stream_t stream,
+                             hsk_store** out);
+
+/* Host pointer to the pinned rows [0, max_ctx) of (source, request); the caller may write them (the
+ * prefill stand-in).  With host_alias_sources every source returns source 0's rows. */
+hsk_status hsk_host_rows(hsk_store* store, int32_t source, int32_t req, void** h_rows, int64_t* n_rows);
+
+/* Copy every request's tail rows (positions [n_r - T, n_r)) of every source from host to pool.  HiSparse
+ * section 3.3 (1): prefill writes each layer's KV to the host pool; the newest rows stay on device. */
+hsk_status hsk_commit_prefill(hsk_store* store, hsk_stream_t stream);
+
+/* Set the optional-history map of complete pages [0, n_pages) of (source, request): h_page_ids[g] is the
+ * page id in the source's optional pool (0 <= id < opt_pool_pages), or -1 to drop page g.  Newly mapped
+ * pages are copied from host first and their map entries published after the copy, in stream order;
+ * dropped entries are cleared in stream order, after earlier readers on the stream (Adaptive DHiSparse
+ * section 3.1: ready locations tracked apart from allocated pages, reclaim after earlier readers).
+ * Only complete pages of history may be mapped: n_pages <= n_r / page_rows.  A call that copies rows
+ * waits for its copies before returning. */
+hsk_status hsk_residency_set(hsk_store* store, int32_t source, int32_t req, const int32_t* h_page_ids,
+                             int64_t n_pages, hsk_stream_t stream);
+
+/* Adaptive DHiSparse Eq. 4 (pure host function): walking requests in reclaim order with optional pages
+ * h_pages_held[0..n), the smallest q whose first q entries cover `deficit` pages; *q_out = -1 when the
+ * optional pages cannot cover it (admission waits), 0 when deficit <= 0. */
+hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t deficit, int32_t* q_out);
+
+/*
+ * One resolve call on `source` at LRU clock `epoch` (strictly increasing per source; EEPOCH otherwise).
+ *   d_sel   int32 [R][Qmax][k] device: query j of request r uses d_sel[r][j][0..k) when j < nq[r]
+ *   d_nq    int32 [R] device queries per request (1..Qmax), or NULL for Qmax everywhere
+ *   d_locs  int32 [R][Qmax][k] device out: pool row of every selection, in selection order (-1 for
+ *           queries j >= nq[r] and for rejected requests)
+ *   d_stats hsk_stats [R] device out, or NULL
+ * Queued on `stream`: one resolve kernel (one workgroup per request) then one gather kernel that copies
+ * the distinct missing rows from pinned host memory into their slots with 16-byte loads.  Locations are
+ * final when the stream reaches the end of the call.  The distinct missing rows and their destination
+ * rows are kept as the source's miss plan (HiSparse section 3.5) until its next resolve call.
+ */
+hsk_status hsk_resolve_step(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
+                            const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream);
+
+/* Plan replay (HiSparse section 3.5, plan-then-IO): copy the rows listed in plan_source's last miss plan
+ * from dst_source's host rows into dst_source's pool, at the same pool rows.  A layer that shares its
+ * anchor's selection then reads its own payload at the anchor's locations.  Order it after the anchor's
+ * resolve and before the consumer's attention with events when it runs on a side stream. */
+hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_source, hsk_stream_t stream);
+
+/* Device address of a source's pool region (row 0 of the layout above). */
+hsk_status hsk_pool_base(hsk_store* store, int32_t source, void** d_pool_source);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Sparse decode attention                                                                              */
+/* ---------------------------------------------------------------------------------------------------- */
+enum { HSK_ATTN_MLA = 0, HSK_ATTN_GQA = 1 };
+
+typedef struct hsk_attn_desc {
+  int32_t kind;          /* HSK_ATTN_MLA or HSK_ATTN_GQA */
+  int32_t num_requests;  /* MLA: R.  GQA: requests (units = requests x kv_heads) */
+  int32_t max_queries;   /* MLA: Qmax.  GQA: 1 */
+  int32_t heads;         /* MLA: query heads sharing the latent row.  GQA: query heads per request */
+  int32_t kv_heads;      /* MLA: 1.  GQA: KV heads; q head h reads KV head h / (heads / kv_heads) */
+  int32_t dk;            /* MLA: key width (row[0:dk]).  GQA: head dim */
+  int32_t dv;            /* MLA: value width (row[0:dv], dv <= dk).  GQA: head dim (= dk) */
+  int32_t top_k;         /* selected rows (MLA) or pages (GQA) per query */
+  int32_t row_elems;     /* bf16 values per pool row (MLA >= dk; GQA page_tokens * 2 * dk) */
+  int32_t page_tokens;   /* GQA: tokens per page row, each [K dk | V dk].  MLA: 1 */
+  int32_t split;         /* partitions of the k rows per query (split-k); 0 = automatic */
+  float scale;           /* softmax scale, e.g. 1/sqrt(dk) */
+} hsk_attn_desc;
+
+/* Device scratch (bytes) that hsk_sparse_decode_attn needs for split-k partial results. */
+hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* desc, size_t* scratch_bytes);
+
+/*
+ * out = softmax(scale * q . K^T) V over the rows at d_locs, bf16 in, fp32 accumulation, bf16 out
+ * (Adaptive DHiSparse Eq. 1; section 3.5: the rows are the model's selected rows, so the result equals
+ * attention over a fully resident cache at the same indices).
+ *   MLA: d_q bf16 [R][Qmax][H][dk]; d_locs int32 [R][Qmax][k]; d_out bf16 [R][Qmax][H][dv];
+ *        d_nq int32 [R] or NULL (queries j >= nq[r] are skipped and their outputs left untouched).
+ *   GQA: d_q bf16 [R][H][dk]; d_locs int32 [R * kv_heads][k] (page rows); d_out bf16 [R][H][dk].
+ *   d_pool: row 0 of the source's pool (hsk_pool_base); every location must be a valid row of it.
+ *   d_scratch: at least hsk_attn_scratch_bytes bytes, 256-byte aligned.
+ */
+hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* desc, const void* d_q, const void* d_pool,
+                                  const int32_t* d_locs, const int32_t* d_nq, void* d_out, void* d_scratch,
+                                  size_t scratch_bytes, hsk_stream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Inspection (tests) and lifetime                                                                     */
+/* ---------------------------------------------------------------------------------------------------- */
+/* Synchronous copy of (source, request) metadata into caller host buffers (any may be NULL):
+ * key[B] (position held, -1 empty), rec[B] (2e+1 after a hit at epoch e, 2e after a fill, 0 empty),
+ * order[B] (slots in ascending (rec, slot) order), pt[n_r] (slot of a position or -1),
+ * opt[n_r / page_rows] (optional page id or -1).  Waits for all work on the device. */
+hsk_status hsk_snapshot(hsk_store* store, int32_t source, int32_t req, int32_t* key, uint32_t* rec,
+                        uint16_t* order, int32_t* pt, int32_t* opt);
+
+/* Synchronous copy of (source, request)'s last miss plan: *n distinct missing positions in miss order
+ * (first occurrence over the flattened query lists) and the pool row each was copied to; at most cap
+ * entries are written. */
+hsk_status hsk_read_plan(hsk_store* store, int32_t source, int32_t req, int32_t* pos, int32_t* dst, int32_t cap,
+                         int32_t* n);
+
+/* Wait for `stream`, then return and clear the first device-side error latched since the last call. */
+hsk_status hsk_sync_status(hsk_store* store, hsk_stream_t stream);
+
+/* Free the pinned host rows and the store (device memory stays with the caller).  Waits for the device. */
+void hsk_kv_store_destroy(hsk_store* store);
+
+const char* hsk_status_str(hsk_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSK_H */
