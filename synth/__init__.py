@@ -200,9 +200,9 @@ def queries(w: Workload, layer: int, step: int) -> np.ndarray:
     nq = 1 if w.kind == "gqa" else w.queries
     elems = w.heads * w.dk
     out = np.empty((R, nq, elems), dtype=np.uint16)
-    for r in range(R):
-        lib().synth_rows_bf16(ctypes.c_void_p(_ptr(out[r])), w.seed, DOMAIN_QUERY, layer * 1_000_000 + step, r,
-                              0, nq, elems, 1)
+    # one stream per (layer, step); row r * nq + j is query j of request r
+    lib().synth_rows_bf16(ctypes.c_void_p(_ptr(out)), w.seed, DOMAIN_QUERY, layer, step, 0, R * nq, elems,
+                          default_threads())
     if w.kind == "gqa":
         return out.reshape(R, w.heads, w.dk)
     return out.reshape(R, nq, w.heads, w.dk)
