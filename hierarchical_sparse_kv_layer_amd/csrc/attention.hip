@@ -45,104 +45,299 @@ struct AttnArgs {
 };
 
 // ------------------------------------------------------------------------------------------------------
-// MLA: grid (split, H / kMlaHeads, R * Qmax), 256 threads.  A block holds kMlaHeads query heads in LDS
-// (fp32) and streams its partition of rows through LDS in tiles of kMlaTile rows.
+// MLA on the matrix cores.
+//
+// One workgroup = NPAIR pairs of waves; pair p owns 16*NHB query heads, and its two waves split the work
+// in half: wave `half` computes the partial scores over key dims [288*half, 288*half + 288) and, after the
+// pair has summed its partials through LDS, accumulates the output columns [256*half, 256*half + 256).
+// Per tile of 32 selected rows:
+//   S^T (32 rows x heads) = K (32 x 576) . Q^T            v_mfma_f32_16x16x32_bf16, A = K from LDS,
+//                                                          B = Q held in registers for the whole kernel
+//   online softmax per head (fp32, exp2 domain)
+//   O^T (cols x heads) += V^T (cols x 32 rows) . P        A = V read with ds_read_b64_tr_b16 (transposing
+//                                                          loads from the row-major tile), B = P as bf16
+// The scores' accumulator layout (lane: head = lane % 16, rows 4*(lane/16)+v of each 16-row block) is used
+// directly as the B operand of the P.V product: the 8 rows a lane holds are its k-slots, and the V operand
+// is read with the same row order, so no shuffle is needed between the two products.
+//
+// Rows are gathered by their locations straight from the pool into LDS with 16-byte LDS-DMA loads, three
+// tiles in flight.  A tile is stored as 9 groups of 8 chunks (16 bytes each) per row, and the chunk position
+// inside a row's 128-byte group is XOR-swizzled by a function of the row so that the 16-row A-operand reads
+// and the transposing V reads are both free of LDS bank conflicts.
 // ------------------------------------------------------------------------------------------------------
-constexpr int kMlaThreads = 256;
-constexpr int kMlaHeads = 16;
-constexpr int kMlaTile = 32;
-constexpr int kMlaMaxDk = 576;
-constexpr int kMlaMaxDv = 512;
-constexpr int kMlaRowWords = kMlaMaxDk / 2 + 2;  // bf16 pairs per LDS row, +2 words against bank conflicts
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define HSK_LDS __attribute__((address_space(3)))
 
-__global__ __launch_bounds__(kMlaThreads) void mla_attn_kernel(AttnArgs a) {
-  __shared__ float s_q[kMlaHeads][kMlaMaxDk];
-  __shared__ uint32_t s_row[kMlaTile][kMlaRowWords];
-  __shared__ float s_p[kMlaHeads][kMlaTile];
+constexpr int kMlaDk = 576;
+constexpr int kMlaDv = 512;
+constexpr int kTile = 32;
+constexpr int kTileBytes = kTile * kMlaDk * 2;   // 36,864
+constexpr int kDmaPerTile = kTileBytes / 1024;   // 36 wave-wide 16-byte loads
+constexpr int kBufs = 3;
+constexpr int kMaxSplitRows = 2048;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
-  const int sp = blockIdx.x, hg = blockIdx.y, rq = blockIdx.z;
-  const int r = rq / a.Qmax, j = rq % a.Qmax;
-  if (a.nq && j >= a.nq[r]) return;
-  const int tid = threadIdx.x;
+struct MlaArgs {
+  const uint16_t* q;
+  const char* pool;
+  const int32_t* locs;
+  const int32_t* nq;
+  uint16_t* out;
+  float* po;
+  float* pm;
+  float* pl;
+  int32_t Qmax, H, k, row_bytes, split, rows_per_split;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// byte offset in a tile of 16-byte chunk c (values 8c..8c+7) of tile row t
+__device__ __forceinline__ int tile_off(int t, int c) {
+  const int a = (t >> 1) & 7;
+  const int f = (a >> 1) | ((a & 1) << 2);
+  return (((c >> 3) << 8) + (t << 3) + ((c & 7) ^ f)) << 4;
+}
+
+// The LDS-DMA loads are issued from inline assembly so that the compiler, which cannot tell the tile
+// buffers apart, does not wait for every load in flight before each LDS read; the kernel waits itself:
+// `vmcnt(N)` with N = this wave's loads of the next tile, then a workgroup barrier.
+__device__ __forceinline__ void dma16(const char* gsrc, const HSK_LDS char* ldst) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)ldst;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gsrc) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_tile_barrier_n(int n) {
+  switch (n) {
+    case 4: wait_tile_barrier<4>(); break;
+    case 5: wait_tile_barrier<5>(); break;
+    case 9: wait_tile_barrier<9>(); break;
+    case 18: wait_tile_barrier<18>(); break;
+    default: wait_tile_barrier<0>(); break;
+  }
+}
+
+// LDS writes of this wave complete, then a workgroup barrier (no wait on global loads)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int NHB, int NPAIR>
+__global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
+  constexpr int NW = 2 * NPAIR;
+  constexpr int NT = 64 * NW;
+  constexpr int HW = 16 * NHB;          // heads of one wave pair
+  constexpr int KS = kMlaDk / 2 / 32;   // 9 k-steps per half of the key dims
+  constexpr int CB = kMlaDv / 2 / 16;   // 16 column blocks per half of the value dims
+  constexpr int kGroup = 2048;          // half the bytes of one 8-chunk group of the 32 tile rows
+  __shared__ __attribute__((aligned(1024))) char s_tile[kBufs][kTileBytes];
+  __shared__ f32x4 s_x[NW][2 * NHB][64];
+  __shared__ int32_t s_loc[kMaxSplitRows];
+
+  const int sp = blockIdx.x, hgrp = blockIdx.y, rq = blockIdx.z;
+  if (a.nq) {
+    const int r = rq / a.Qmax, qi = rq % a.Qmax;
+    if (qi >= a.nq[r]) return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1, half = wave & 1;
+  const int g = lane >> 4, jl = lane & 15;
   const int i0 = sp * a.rows_per_split;
-  const int i1 = min(a.k, i0 + a.rows_per_split);
-  const int h0 = hg * kMlaHeads;
-  const int dk = a.dk, dv = a.dv;
+  const int nrows = max(0, min(a.k, i0 + a.rows_per_split) - i0);
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  const int hbase = hgrp * (HW * NPAIR) + pair * HW;
+  const int my_dma = (kDmaPerTile - wave + NW - 1) / NW;
 
-  const uint16_t* q = a.q + ((int64_t)rq * a.H + h0) * dk;
-  for (int x = tid; x < kMlaHeads * dk; x += kMlaThreads) s_q[x / dk][x % dk] = bf16f(q[x]);
+  const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
+  for (int x = tid; x < nrows; x += NT) s_loc[x] = locs[x];
 
-  // output ownership: head hh = tid / 16, columns c * 16 + sub (interleaved -> conflict-free LDS reads)
-  const int hh = tid >> 4, sub = tid & 15;
-  const int ncol = (dv + 15) >> 4;  // <= 32
-  float o[kMlaMaxDv / 16];
+  bf16x8 qf[NHB][KS];
+  {
+    const uint16_t* qb = a.q + ((int64_t)rq * a.H + hbase + jl) * kMlaDk + 288 * half + 8 * g;
 #pragma unroll
-  for (int c = 0; c < kMlaMaxDv / 16; ++c) o[c] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const int32_t* locs = a.locs + (int64_t)rq * a.k;
-  const int row_bytes = a.row_elems * 2;
-  const int chunks8 = dk / 4;  // 8-byte chunks of the key part
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[hb][ks] = *(const bf16x8*)(qb + (int64_t)hb * 16 * kMlaDk + 32 * ks);
+  }
+  // Q and the locations are in registers/LDS before any tile load is issued: the compiler then has no
+  // global load of its own in flight inside the loop, where a vmcnt wait would also wait for the tiles.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  for (int t0 = i0; t0 < i1; t0 += kMlaTile) {
-    const int nt = min(kMlaTile, i1 - t0);
-    __syncthreads();
-    for (int x = tid; x < nt * chunks8; x += kMlaThreads) {
-      const int i = x / chunks8, c = x % chunks8;
-      const u32x2* src = (const u32x2*)(a.pool + (int64_t)locs[t0 + i] * row_bytes) + c;
-      const u32x2 w = *src;
-      s_row[i][2 * c] = w.x;
-      s_row[i][2 * c + 1] = w.y;
+  // Lane-constant parts of the LDS addresses; every unrolled read adds a compile-time offset.
+  //  S:  chunk 36 half + 4 ks + g of row 16 tb + jl.  Even and odd ks differ in the swizzled position;
+  //      ks and ks + 2 are one 4,096-byte chunk group apart; tb = 1 is 2,048 bytes after tb = 0.
+  const int s_even = tile_off(jl, 36 * half + g);
+  const int s_odd = tile_off(jl, 36 * half + g + 4);
+  //  PV: chunk 32 half + 2 cb + (q4 >> 1) of row t1 (and t1 + 16), byte (q4 & 1) * 8; cb = 4 u + w.
+  const int t1 = 4 * g + (jl >> 2);
+  const int q4 = jl & 3;
+  int v_base[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) v_base[w] = tile_off(t1, 32 * half + 2 * w + (q4 >> 1)) + (q4 & 1) * 8;
+  // DMA: wave-wide load i (i = wave + NW u) covers tile rows 8 (i & 3) .. + 7 and chunk group i >> 2; a lane
+  // copies 16 bytes of one row: with 4 or more waves every load of a wave uses the same rows (NTOK = 1),
+  // with 2 waves the loads alternate between two rows.
+  constexpr int NTOK = NW >= 4 ? 1 : 2;
+  const uint32_t lds_tile0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
+  int tok[NTOK], swz[NTOK];
+#pragma unroll
+  for (int v = 0; v < NTOK; ++v) {
+    tok[v] = 8 * ((wave + NW * v) & 3) + (lane >> 3);
+    const int aa = (tok[v] >> 1) & 7;
+    const int f = (aa >> 1) | ((aa & 1) << 2);
+    swz[v] = (((lane & 7) ^ f) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
+  }
+
+  auto issue = [&](int T, int b) {
+    const int tb = T * kTile;
+    const uint32_t lbase = lds_tile0 + b * kTileBytes + wave * 1024;
+    const char* rp[NTOK];
+#pragma unroll
+    for (int v = 0; v < NTOK; ++v) {
+      const int x = tb + tok[v] < nrows ? tb + tok[v] : 0;   // rows past the end re-read row 0 (masked)
+      rp[v] = a.pool + (int64_t)s_loc[x] * a.row_bytes + swz[v];
     }
-    __syncthreads();
-    // scores: kMlaHeads x nt dot products of length dk
-    for (int x = tid; x < kMlaHeads * kMlaTile; x += kMlaThreads) {
-      const int h = x / kMlaTile, i = x % kMlaTile;
-      float acc = -INFINITY;
-      if (i < nt) {
-        acc = 0.f;
-        const float* qh = s_q[h];
-        const uint32_t* row = s_row[i];
-        for (int d2 = 0; d2 < dk / 2; ++d2) {
-          const uint32_t w = row[d2];
-          acc = fmaf(qh[2 * d2], bf16lo(w), acc);
-          acc = fmaf(qh[2 * d2 + 1], bf16hi(w), acc);
+#pragma unroll
+    for (int u = 0; u < (kDmaPerTile + NW - 1) / NW; ++u) {
+      if (wave + NW * u < kDmaPerTile) {
+        // the instruction's immediate offset would also move the LDS destination, so the row offset of
+        // the chunk group goes into the address register
+        constexpr int kStep = NW >= 4 ? (NW / 4) * 128 : 0;
+        const uint32_t m0 = lbase + NW * u * 1024;
+        const char* src = NW >= 4 ? rp[0] + kStep * u : rp[u % NTOK] + (u >> 1) * 128;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+      }
+    }
+  };
+
+  f32x4 oacc[CB][NHB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) oacc[cb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NHB], l_run[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) { m_run[hb] = -INFINITY; l_run[hb] = 0.f; }
+
+  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
+  for (int T = 0; T < ntiles; ++T) {
+    const int b = T % kBufs;
+    if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
+    if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
+    const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[b][0];
+
+    // partial scores over this wave's half of the key dims
+    f32x4 sacc[2][NHB];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const HSK_LDS char* se = tile + s_even;
+    const HSK_LDS char* so = tile + s_odd;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const HSK_LDS char* sb = (ks & 1) ? so + (ks >> 1) * kGroup * 2 : se + (ks >> 1) * kGroup * 2;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 kf = *(const HSK_LDS bf16x8*)(sb + tb * 2048);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb)
+          sacc[tb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[hb][ks], sacc[tb][hb], 0, 0, 0);
+      }
+    }
+    // the pair sums its two halves (both waves get the same, commutative, sum)
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) s_x[wave][tb * NHB + hb][lane] = sacc[tb][hb];
+    lds_barrier();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] += s_x[wave ^ 1][tb * NHB + hb][lane];
+
+    // online softmax; lane holds head hbase + 16 hb + jl, rows 16 tb + 4 g + v
+    const int rem = nrows - T * kTile;
+    bf16x8 pf[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float x = sacc[tb][hb][v] * a.scale_log2;
+          if (16 * tb + 4 * g + v >= rem) x = -INFINITY;
+          sv[4 * tb + v] = x;
+          tmax = fmaxf(tmax, x);
         }
-        acc *= a.scale;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m_run[hb], tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[hb] - mn);
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sv[i] - mn);
+        psum += p;
+        pf[hb][i] = (__bf16)p;
       }
-      s_p[h][i] = acc;
+      l_run[hb] = l_run[hb] * alpha + psum;
+      m_run[hb] = mn;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) oacc[cb][hb] *= alpha;
     }
-    __syncthreads();
-    // online softmax and P.V for head hh over this tile
-    float tmax = -INFINITY;
-    for (int i = 0; i < nt; ++i) tmax = fmaxf(tmax, s_p[hh][i]);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __expf(m_run - m_new);
-    l_run *= alpha;
+
+    // O^T += V^T P over this wave's half of the value columns
 #pragma unroll
-    for (int c = 0; c < kMlaMaxDv / 16; ++c) o[c] *= alpha;
-    for (int i = 0; i < nt; ++i) {
-      const float p = __expf(s_p[hh][i] - m_new);
-      l_run += p;
-      const uint16_t* v = (const uint16_t*)s_row[i];
+    for (int cb = 0; cb < CB; ++cb) {
+      const HSK_LDS char* p0 = tile + v_base[cb & 3] + (cb >> 2) * kGroup * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSK_LDS i16x4*)p0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSK_LDS i16x4*)(p0 + 2048));
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-      for (int c = 0; c < kMlaMaxDv / 16; ++c) {
-        const int col = c * 16 + sub;
-        if (c < ncol && col < dv) o[c] = fmaf(p, bf16f(v[col]), o[c]);
+      for (int hb = 0; hb < NHB; ++hb)
+        oacc[cb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[hb], oacc[cb][hb], 0, 0, 0);
+    }
+  }
+
+  // epilogue: lane holds head hbase + 16 hb + jl, columns 256 half + 16 cb + 4 g + v
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    float l = l_run[hb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int head = hbase + 16 * hb + jl;
+    if (a.split == 1) {
+      const float inv = 1.f / l;
+      uint16_t* o = a.out + ((int64_t)rq * a.H + head) * kMlaDv + 256 * half + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const f32x4 v = oacc[cb][hb] * inv;
+        u32x2 w;
+        w.x = (uint32_t)f2bf16(v[0]) | ((uint32_t)f2bf16(v[1]) << 16);
+        w.y = (uint32_t)f2bf16(v[2]) | ((uint32_t)f2bf16(v[3]) << 16);
+        *(u32x2*)(o + 16 * cb) = w;
+      }
+    } else {
+      const int64_t ps = ((int64_t)rq * a.split + sp) * a.H + head;
+      float* po = a.po + ps * kMlaDv + 256 * half + 4 * g;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) *(f32x4*)(po + 16 * cb) = oacc[cb][hb];
+      if (half == 0 && g == 0) {
+        a.pm[ps] = m_run[hb] * kLn2;   // natural-log units, as the combine expects
+        a.pl[ps] = l;
       }
     }
-    m_run = m_new;
-  }
-  // partial results
-  const int64_t ps = ((int64_t)rq * a.split + sp) * a.H + h0 + hh;
-  float* po = a.po + ps * dv;
-#pragma unroll
-  for (int c = 0; c < kMlaMaxDv / 16; ++c) {
-    const int col = c * 16 + sub;
-    if (c < ncol && col < dv) po[col] = o[c];
-  }
-  if (sub == 0) {
-    a.pm[ps] = m_run;
-    a.pl[ps] = l_run;
   }
 }
 
@@ -223,37 +418,72 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int dv) {
   }
 }
 
-static int auto_split(const hsk_attn_desc* d) {
-  if (d->split > 0) return d->split;
-  if (d->kind == HSK_ATTN_MLA) {
-    // enough workgroups for 256 CUs: (R * Qmax) * (H / 16) * split >= ~2048
-    const int64_t base = (int64_t)d->num_requests * d->max_queries * (d->heads / kMlaHeads);
-    int s = (int)((2048 + base - 1) / base);
-    s = s < 1 ? 1 : s;
-    const int max_s = (d->top_k + kMlaTile - 1) / kMlaTile;
-    return s > max_s ? max_s : s;
-  }
-  const int64_t base = (int64_t)d->num_requests * d->kv_heads;
-  int s = (int)((2048 + base - 1) / base);
-  s = s < 1 ? 1 : s;
-  return s > d->top_k ? d->top_k : s;
-}
+// Launch plan of one attention call: split-k partitions and, for MLA, the wave-pair shape.
+struct AttnPlan {
+  int split, rows_per_split;
+  int nhb, npair, hgroups;  // MLA: 16-head blocks per wave pair, pairs per workgroup, head groups
+  int64_t po_bytes, pm_bytes, scratch;
+};
 
-static bool valid_attn(const hsk_attn_desc* d) {
+static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
   if (!d || d->num_requests < 1 || d->max_queries < 1 || d->heads < 1 || d->top_k < 1 || d->split < 0) return false;
+  const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
+  const int k = d->top_k;
   if (d->kind == HSK_ATTN_MLA) {
-    if (d->kv_heads != 1 || d->dk < 2 || d->dk > kMlaMaxDk || d->dk % 4 || d->dv < 1 || d->dv > d->dk ||
-        d->dv > kMlaMaxDv || d->row_elems < d->dk || d->row_elems % 8 || d->heads % kMlaHeads || d->page_tokens != 1)
+    if (d->kv_heads != 1 || d->dk != kMlaDk || d->dv != kMlaDv || d->row_elems < kMlaDk || d->row_elems % 8 ||
+        d->heads % 16 || d->page_tokens != 1)
       return false;
-    return true;
-  }
-  if (d->kind == HSK_ATTN_GQA) {
+    p->nhb = d->heads % 32 == 0 ? 2 : 1;
+    const int units = d->heads / (16 * p->nhb);
+    p->npair = units % 4 == 0 ? 4 : units % 2 == 0 ? 2 : 1;
+    p->hgroups = units / p->npair;
+    const int min_split = (k + kMaxSplitRows - 1) / kMaxSplitRows;
+    if (d->split > 0) {
+      p->split = d->split;
+      p->rows_per_split = (k + p->split - 1) / p->split;
+      if (p->rows_per_split > kMaxSplitRows) return false;
+    } else {
+      // about one workgroup per compute unit (a workgroup fills a CU's LDS), tiles of whole 32-row blocks
+      const int64_t base = RQ * p->hgroups;
+      int64_t s = (256 + base - 1) / base;
+      const int64_t max_s = (k + kTile - 1) / kTile;
+      s = s > max_s ? max_s : s;
+      s = s < min_split ? min_split : s;
+      int rps = (int)((k + s - 1) / s);
+      if (s > 1) rps = (rps + kTile - 1) / kTile * kTile;
+      if (rps > kMaxSplitRows) rps = kMaxSplitRows;
+      p->rows_per_split = rps;
+      p->split = (k + rps - 1) / rps;
+    }
+  } else if (d->kind == HSK_ATTN_GQA) {
     if (d->max_queries != 1 || d->kv_heads < 1 || d->heads % d->kv_heads || d->heads / d->kv_heads > 4 ||
         d->dk != 128 || d->dv != 128 || d->page_tokens < 1 || d->row_elems != d->page_tokens * 2 * d->dk)
       return false;
-    return true;
+    p->nhb = p->npair = p->hgroups = 0;
+    if (d->split > 0) {
+      p->split = d->split;
+    } else {
+      const int64_t base = (int64_t)d->num_requests * d->kv_heads;
+      int64_t s = (2048 + base - 1) / base;
+      s = s < 1 ? 1 : s;
+      p->split = (int)(s > k ? k : s);
+    }
+    p->rows_per_split = (k + p->split - 1) / p->split;
+  } else {
+    return false;
   }
-  return false;
+  const int64_t parts = RQ * p->split * d->heads;
+  const bool partials = !(d->kind == HSK_ATTN_MLA && p->split == 1);
+  p->po_bytes = partials ? (parts * d->dv * 4 + 255) / 256 * 256 : 0;
+  p->pm_bytes = partials ? (parts * 4 + 255) / 256 * 256 : 0;
+  p->scratch = p->po_bytes + 2 * p->pm_bytes;
+  if (p->scratch < 256) p->scratch = 256;
+  return true;
+}
+
+template <int NHB, int NPAIR>
+static void launch_mla(const MlaArgs& m, const AttnPlan& p, int64_t RQ, hipStream_t s) {
+  hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR>), dim3(p.split, p.hgroups, RQ), dim3(128 * NPAIR), 0, s, m);
 }
 
 }  // namespace hsk
@@ -263,24 +493,20 @@ using namespace hsk;
 extern "C" {
 
 hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* d, size_t* bytes) {
-  if (!valid_attn(d) || !bytes) return HSK_EINVAL;
-  const int64_t split = auto_split(d);
-  const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
-  const int64_t parts = RQ * split * d->heads;
-  const int64_t po = (parts * d->dv * 4 + 255) / 256 * 256;
-  const int64_t pm = (parts * 4 + 255) / 256 * 256;
-  *bytes = (size_t)(po + 2 * pm);
+  AttnPlan p;
+  if (!bytes || !plan_attn(d, &p)) return HSK_EINVAL;
+  *bytes = (size_t)p.scratch;
   return HSK_OK;
 }
 
 hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const void* d_pool, const int32_t* d_locs,
                                   const int32_t* d_nq, void* d_out, void* d_scratch, size_t scratch_bytes,
                                   hsk_stream_t stream) {
-  if (!valid_attn(d) || !d_q || !d_pool || !d_locs || !d_out || !d_scratch) return HSK_EINVAL;
-  size_t need = 0;
-  hsk_attn_scratch_bytes(d, &need);
-  if (scratch_bytes < need || ((uintptr_t)d_scratch % 256)) return HSK_EINVAL;
+  AttnPlan p;
+  if (!plan_attn(d, &p) || !d_q || !d_pool || !d_locs || !d_out || !d_scratch) return HSK_EINVAL;
+  if (scratch_bytes < (size_t)p.scratch || ((uintptr_t)d_scratch % 256)) return HSK_EINVAL;
   hipStream_t s = (hipStream_t)stream;
+  const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
   AttnArgs a;
   a.q = (const uint16_t*)d_q;
   a.pool = (const char*)d_pool;
@@ -289,23 +515,30 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
   a.out = (uint16_t*)d_out;
   a.R = d->num_requests; a.Qmax = d->max_queries; a.H = d->heads; a.Hkv = d->kv_heads;
   a.dk = d->dk; a.dv = d->dv; a.k = d->top_k; a.row_elems = d->row_elems; a.page_tokens = d->page_tokens;
-  a.split = auto_split(d);
-  a.rows_per_split = (d->top_k + a.split - 1) / a.split;
+  a.split = p.split;
+  a.rows_per_split = p.rows_per_split;
   a.scale = d->scale;
-  const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
-  const int64_t parts = RQ * a.split * d->heads;
-  const int64_t po_bytes = (parts * d->dv * 4 + 255) / 256 * 256;
-  const int64_t pm_bytes = (parts * 4 + 255) / 256 * 256;
   a.po = (float*)d_scratch;
-  a.pm = (float*)((char*)d_scratch + po_bytes);
-  a.pl = (float*)((char*)d_scratch + po_bytes + pm_bytes);
+  a.pm = (float*)((char*)d_scratch + p.po_bytes);
+  a.pl = (float*)((char*)d_scratch + p.po_bytes + p.pm_bytes);
   if (d->kind == HSK_ATTN_MLA) {
-    hipLaunchKernelGGL(mla_attn_kernel, dim3(a.split, d->heads / kMlaHeads, RQ), dim3(kMlaThreads), 0, s, a);
+    MlaArgs m;
+    m.q = a.q; m.pool = a.pool; m.locs = a.locs; m.nq = a.nq; m.out = a.out;
+    m.po = a.po; m.pm = a.pm; m.pl = a.pl;
+    m.Qmax = d->max_queries; m.H = d->heads; m.k = d->top_k; m.row_bytes = d->row_elems * 2;
+    m.split = p.split; m.rows_per_split = p.rows_per_split;
+    m.scale_log2 = d->scale * kLog2e;
+    if (p.nhb == 2 && p.npair == 4) launch_mla<2, 4>(m, p, RQ, s);
+    else if (p.nhb == 2 && p.npair == 2) launch_mla<2, 2>(m, p, RQ, s);
+    else if (p.nhb == 2) launch_mla<2, 1>(m, p, RQ, s);
+    else launch_mla<1, 1>(m, p, RQ, s);
+    HSK_HIP(hipGetLastError());
+    if (p.split == 1) return HSK_OK;
   } else {
     hipLaunchKernelGGL(gqa_attn_kernel, dim3(a.split, (int64_t)d->num_requests * d->kv_heads),
                        dim3(64 * (d->heads / d->kv_heads)), 0, s, a);
+    HSK_HIP(hipGetLastError());
   }
-  HSK_HIP(hipGetLastError());
   hipLaunchKernelGGL(combine_kernel, dim3(RQ, d->heads), dim3(128), 0, s, a, d->dv);
   HSK_HIP(hipGetLastError());
   return HSK_OK;

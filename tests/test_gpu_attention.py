@@ -1,0 +1,105 @@
+"""GPU parity of the sparse decode attention kernels alone (no resolver): random pools and locations,
+every head-count variant of the MLA kernel, forced and automatic split-k, ragged k, duplicate and repeated
+locations, against the fp64 oracle (|gpu - ref| <= 1e-2 + 2e-2 |ref| per element)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import hierarchical_sparse_kv_layer_amd as hsk  # noqa: E402
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+ATOL, RTOL = 1e-2, 2e-2
+
+
+def _bf16(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+def _run_mla(R, Q, H, k, n_rows, split=0, nq=None, seed=0, row_elems=576, q_scale=1.0):
+    rng = np.random.default_rng(seed)
+    rows = _bf16(rng.standard_normal((n_rows, row_elems)))
+    q = _bf16(q_scale * rng.standard_normal((R, Q, H, 576)))
+    locs = rng.integers(0, n_rows, size=(R, Q, k)).astype(np.int32)
+    ad = hsk.mla_desc(requests=R, max_queries=Q, heads=H, dk=576, dv=512, top_k=k, row_elems=row_elems,
+                      scale=576 ** -0.5, split=split)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    pool = torch.from_numpy(rows.view(np.int16)).cuda()
+    out = torch.full((R, Q, H, 512), 77, dtype=torch.int16, device="cuda")
+    d_nq = None if nq is None else torch.from_numpy(np.asarray(nq, np.int32)).cuda()
+    print(f"[attn] R={R} Q={Q} H={H} k={k} split={split} rows={n_rows}", flush=True)
+    hsk.sparse_decode_attn(ad, torch.from_numpy(q.view(np.int16)).cuda(), pool.data_ptr(),
+                           torch.from_numpy(locs).cuda(), d_nq, out, scratch, nb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for r in range(R):
+        for j in range(Q):
+            if nq is not None and j >= nq[r]:
+                assert np.all(got[r, j] == 77), "skipped query's output was written"
+                continue
+            ref = oracle.mla_attention(q[r, j], rows[locs[r, j]], 576, 512, 576 ** -0.5)
+            g = synth.bf16_to_f32(got[r, j].view(np.uint16)).astype(np.float64)
+            err = np.abs(g - ref)
+            assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"r={r} j={j}: max abs err {err.max():.3e}"
+            worst = max(worst, float(err.max()))
+    return worst
+
+
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 128, 256])
+def test_mla_head_variants(H):
+    """Every wave-pair shape: 16 heads (1 pair of 16-head waves), 32/64/128 (1, 2, 4 pairs of 32), 48
+    (three 16-head groups), 256 (two 128-head groups)."""
+    _run_mla(R=3, Q=1, H=H, k=100, n_rows=700, seed=H)
+
+
+@pytest.mark.parametrize("k,split", [(1, 0), (31, 0), (32, 1), (33, 1), (100, 3), (257, 5), (2048, 1),
+                                     (2048, 0), (4096, 0)])
+def test_mla_split_and_ragged_k(k, split):
+    """Ragged last tiles, one row, one partition (direct bf16 output), uneven forced splits, partitions
+    that end inside a tile, and k larger than one partition may hold (forced to several)."""
+    _run_mla(R=2, Q=2, H=32, k=k, n_rows=5000, split=split, seed=k + split)
+
+
+def test_mla_partial_queries_and_wide_rows():
+    """Per-request query counts (outputs of skipped queries untouched), pool rows wider than the 576 key
+    values (only row[0:576] is read), large score range (q scaled up)."""
+    _run_mla(R=4, Q=3, H=64, k=77, n_rows=900, nq=[3, 0, 1, 2], seed=9, row_elems=640, q_scale=4.0)
+
+
+def test_mla_identical_rows_and_duplicates():
+    """All selected rows identical -> output = that row's values (within the bf16 tolerance: the weights
+    enter the P.V product rounded to bf16); lists that repeat locations."""
+    rng = np.random.default_rng(3)
+    row = _bf16(rng.standard_normal(576))
+    rows = np.tile(row, (50, 1))
+    R, H, k = 2, 128, 64
+    q = _bf16(rng.standard_normal((R, 1, H, 576)))
+    locs = rng.integers(0, 50, size=(R, 1, k)).astype(np.int32)
+    ad = hsk.mla_desc(requests=R, max_queries=1, heads=H, dk=576, dv=512, top_k=k, row_elems=576,
+                      scale=576 ** -0.5)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    pool = torch.from_numpy(rows.view(np.int16)).cuda()
+    out = torch.empty((R, 1, H, 512), dtype=torch.int16, device="cuda")
+    hsk.sparse_decode_attn(ad, torch.from_numpy(q.view(np.int16)).cuda(), pool.data_ptr(),
+                           torch.from_numpy(locs).cuda(), None, out, scratch, nb)
+    torch.cuda.synchronize()
+    got = synth.bf16_to_f32(out.cpu().numpy().view(np.uint16))
+    want = np.broadcast_to(synth.bf16_to_f32(row[:512]), got.shape)
+    assert np.all(np.abs(got - want) <= ATOL + RTOL * np.abs(want))
+
+
+def test_mla_rejects_unsupported_shapes():
+    for kw in ({"dk": 512}, {"dv": 256}, {"heads": 24}, {"row_elems": 500}, {"top_k": 4096, "split": 1}):
+        args = dict(requests=1, max_queries=1, heads=16, dk=576, dv=512, top_k=8, row_elems=576, scale=0.1)
+        args.update(kw)
+        with pytest.raises(hsk.HskError):
+            hsk.attn_scratch_bytes(hsk.mla_desc(**args))
