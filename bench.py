@@ -92,6 +92,9 @@ def main() -> int:
     ap.add_argument("--workload", default="dsa100k")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 4 device-to-device copies of 1 GiB (the known-size kernel that scales the "
+                         "HBM byte counters of a profile)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the hot path on a single MI355X and has no "
@@ -99,6 +102,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 4}))
+        return 0
 
     import hierarchical_sparse_kv_layer_amd as hsk
     import synth
