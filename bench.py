@@ -83,12 +83,115 @@ def cpu_baseline(w, sel_layer0, q_layer0, host_rows_fn, steps_for_resolve: int) 
             "steps_per_s": 1.0 / (per_layer_step * w.layers)}
 
 
+def resolve_algorithmic_bytes(w) -> int:
+    """Bytes one resolve call must move for a single-query layer-step with no misses: selections in and
+    locations out (4 B each), the slot order (2 B per slot) and keys (4 B per slot) read, the order written,
+    one page-table word per selected row and a recency stamp per hit written."""
+    R, k, B = w.requests, w.top_k, w.hot_slots
+    return R * (k * 4 + k * 4 + B * 2 + B * 4 + B * 2 + k * 4 + k * 4)
+
+
+def attn_algorithmic_bytes(w) -> int:
+    """Selected rows (576 bf16 each), queries, bf16 outputs and locations of one MLA attention call."""
+    R, k = w.requests, w.top_k
+    return R * k * w.dk * 2 + R * w.heads * w.dk * 2 + R * w.heads * w.dv * 2 + R * k * 4
+
+
+def hits_only(hsk, w, store, sels, d_q, d_locs, d_stats, ad, scratch, nscratch, pools, first_epoch: int,
+              reps: int = 20) -> dict:
+    """Every layer repeats its last selection (keep fraction 1): every pending row is a hot hit, so one
+    layer-step is resolve (no copies) + attention, bounded by HBM."""
+    import torch
+    stream = torch.cuda.current_stream()
+    last = [sels[l].shape[0] - 1 for l in range(w.layers)]
+    sel_l = [torch.from_numpy(np.ascontiguousarray(sels[l][last[l]])).cuda() for l in range(w.layers)]
+    out = torch.empty((w.requests, 1, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    e = first_epoch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps * w.layers)]
+    for i in range(reps + 1):
+        for l in range(w.layers):
+            if i:
+                ev[(i - 1) * w.layers + l][0].record(stream)
+            store.resolve_step(l, e, sel_l[l], d_locs[l], d_stats[l])
+            if i:
+                ev[(i - 1) * w.layers + l][1].record(stream)
+            hsk.sparse_decode_attn(ad, d_q[l][last[l]], pools[l], d_locs[l], None, out, scratch, nscratch)
+            if i:
+                ev[(i - 1) * w.layers + l][2].record(stream)
+        e += 1
+    torch.cuda.synchronize()
+    misses = sum(int(hsk.stats_to_numpy(d_stats[l])["n_miss"].sum()) for l in range(w.layers))
+    res_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    att_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    both = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
+    nbytes = resolve_algorithmic_bytes(w) + attn_algorithmic_bytes(w)
+    gbs = nbytes / (both * 1e-3) / 1e9
+    rows = w.requests * w.top_k
+    return {"ms_per_layer_step": both, "resolve_ms": res_ms, "attention_ms": att_ms, "misses": misses,
+            "algorithmic_bytes_per_layer_step": nbytes, "achieved_GBps": gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
+            "frac_hbm": gbs / HBM_PEAK_GBS, "rows_per_s": rows / (both * 1e-3),
+            "steps_per_s": 1.0 / (both * 1e-3 * w.layers)}
+
+
+def misses_only(hsk, synth, w, gather_blocks: int, calls: int = 12) -> dict:
+    """Fig. 8a analog at the 100K batch-64 shape: B = k, no tail, every call selects k rows no earlier call
+    selected, so every selected row is copied from pinned host memory (64 x 2048 x 1152 B = 151 MB)."""
+    import torch
+    R, k = w.requests, w.top_k
+    n = w.ctx
+    st = hsk.KVStore(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=k, tail_rows=0, ctx=n, max_queries=1,
+                     top_k=k, gather_blocks=gather_blocks)
+    for r in range(R):
+        synth.fill_kv_rows(st.host_ptr(0, r), w, 0, r, 0, n)
+    g = np.random.default_rng([w.seed, 99])
+    perms = np.stack([g.permutation(n)[: (calls + 1) * k] for _ in range(R)]).astype(np.int32)
+    d_sel = [torch.from_numpy(np.ascontiguousarray(perms[:, c * k:(c + 1) * k].reshape(R, 1, k))).cuda()
+             for c in range(calls + 1)]
+    locs = torch.empty((R, 1, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(R)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    st.resolve_step(0, 1, d_sel[0], locs, stats)  # warm
+    fetched = 0
+    for c in range(calls):
+        ev[c][0].record(stream)
+        st.resolve_step(0, c + 2, d_sel[c + 1], locs, stats)
+        ev[c][1].record(stream)
+    torch.cuda.synchronize()
+    fetched = int(hsk.stats_to_numpy(stats)["fetched_bytes"].sum())
+    status = st.sync_status()
+    st.close()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gbs = fetched / (ms * 1e-3) / 1e9
+    return {"bytes_per_call": fetched, "ms_per_call": ms, "achieved_GBps": gbs, "host_link_peak_GBps": PCIE_PEAK_GBS,
+            "frac_host_link": gbs / PCIE_PEAK_GBS, "status": status,
+            "note": "resolve kernel + zero-copy gather per call; bytes = distinct misses x 1152"}
+
+
+def memcpy_ceiling(nbytes: int = 1 << 28, reps: int = 8) -> dict:
+    """Pinned host -> device hipMemcpyAsync of 256 MiB: the DMA-engine ceiling of the host link."""
+    import torch
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        d.copy_(h, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"bytes": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the hits-only, misses-only and memcpy runs")
     ap.add_argument("--workload", default="dsa100k")
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
@@ -188,8 +291,7 @@ def main() -> int:
     ms_per_step = elapsed * 1e3 / K
     att_avg = float(np.mean(att_ms))
     res_avg = float(np.mean(res_ms))
-    kv_bytes = w.requests * w.top_k * w.dk * 2
-    attn_bytes = kv_bytes + w.requests * w.heads * w.dk * 2 + w.requests * w.heads * w.dv * 2 + w.requests * w.top_k * 4
+    attn_bytes = attn_algorithmic_bytes(w)
     achieved = attn_bytes / (att_avg * 1e-3) / 1e9
     traffic = counter_traffic("mla_attention", os.path.join(ROOT, "hierarchical_sparse_kv_layer_amd", "csrc",
                                                             "attention.hip"))
@@ -213,6 +315,11 @@ def main() -> int:
                     "host_link_peak_GBps": PCIE_PEAK_GBS},
         "status": status,
     }
+    if not args.no_extras:
+        result["hits_only"] = hits_only(hsk, w, store, sels, d_q, d_locs, d_stats, ad, scratch, nscratch, pools,
+                                        first_epoch=total_steps + 1)
+        result["misses_only"] = misses_only(hsk, synth, w, args.gather_blocks)
+        result["host_link_ceiling"] = memcpy_ceiling()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, sels[0], q_host[0][min(3, total_steps) - 1],

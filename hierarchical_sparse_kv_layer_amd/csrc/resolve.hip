@@ -26,11 +26,16 @@
 
 namespace hsk {
 
-__device__ __forceinline__ int32_t ld_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Everything a resolve workgroup shares through global memory (its request's page table, locations and
+// miss plan) is touched by that workgroup alone during the kernel, so workgroup scope is enough: on this
+// multi-XCD part an agent-scope fence would write back and invalidate the whole L2.  A value that another
+// thread changed with an atomic is read back with an atomic (it executes at L2), never a plain load that
+// could hit a line this CU cached before the atomic.
+__device__ __forceinline__ int32_t rmw_read(int32_t* p) {
+  return __hip_atomic_fetch_or(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void st_agent(int32_t* p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void claim_min(int32_t* p, int32_t v) {
+  __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Exclusive prefix count of `flag` over the workgroup in thread order; *total gets the count.
@@ -96,6 +101,18 @@ __device__ __forceinline__ int classify(const ResolveArgs& a, int r, int64_t n, 
   return kDirectNone;
 }
 
+// Per-selection codes while a call runs (kept in registers when the request has at most kPer * threads
+// selections, else in the location array, which then doubles as scratch):
+//   >= 0              final location (a direct row or a hot hit)
+//   kCodeMiss         a missing position, before its claim is read back
+//   INT_MIN + f0      a repeated miss whose first occurrence is selection f0
+//   -2 - i            the first occurrence of distinct miss i (also stored at locs[f0] for repeats to read)
+constexpr int32_t kCodeMiss = -1;
+constexpr int kPer = 4;                                   // contiguous selections per thread per round
+constexpr int kSlotsPerThread = HSK_MAX_HOT_SLOTS / kResolveThreads;
+
+__device__ __forceinline__ bool is_claim(int32_t c) { return c <= INT_MIN + HSK_MAX_SELECTIONS_PER_REQUEST; }
+
 __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a) {
   __shared__ uint32_t s_hit[HSK_MAX_HOT_SLOTS / 32];
   __shared__ uint32_t s_vic[HSK_MAX_HOT_SLOTS / 32];
@@ -103,6 +120,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   __shared__ int32_t s_vic_pre[HSK_MAX_HOT_SLOTS / 32];
   __shared__ uint16_t s_order[HSK_MAX_HOT_SLOTS];
   __shared__ uint16_t s_victim[HSK_MAX_HOT_SLOTS];
+  __shared__ int32_t s_key[HSK_MAX_HOT_SLOTS];
   __shared__ int s_wsum[kResolveWaves];
   __shared__ int s_cnt[4];
 
@@ -125,15 +143,29 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   const int32_t* opt = a.m.opt ? a.m.opt + (int64_t)r * a.max_pages : nullptr;
   int32_t* ppos = a.m.plan_pos + (int64_t)r * a.plan_cap;
   int32_t* pdst = a.m.plan_dst + (int64_t)r * a.plan_cap;
+  const int64_t hot0 = (int64_t)r * B;
+  const int64_t stg0 = a.stg_base + (int64_t)r * a.S;
+  constexpr int per_round = kResolveThreads * kPer;
+  const int nrounds = (nsel + per_round - 1) / per_round;
+  const bool one_round = nrounds <= 1;
 
-  // ---- phase 0: slot order to LDS, clear bitmaps; validate every selected position --------------------
-  for (int q = tid; q < B; q += NT) s_order[q] = order[q];
+  // ---- phase 0: slot order and keys to LDS, clear bitmaps, validate every selected position ------------
+  for (int q = tid; q < B; q += NT) {
+    s_order[q] = order[q];
+    s_key[q] = key[q];
+  }
   for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
   if (tid < 4) s_cnt[tid] = 0;
   bool bad = !nq_ok;
-  for (int f = tid; f < nsel; f += NT) {
-    const int32_t p = sel[f];
-    bad |= (p < 0) || ((int64_t)p >= n);
+  int32_t pv[kPer];
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int f = fb + e;
+      pv[e] = f < nsel ? sel[f] : 0;
+      bad |= (pv[e] < 0) || ((int64_t)pv[e] >= n);
+    }
   }
   if (__syncthreads_or(bad)) {
     for (int f = tid; f < total; f += NT) locs[f] = -1;
@@ -150,43 +182,95 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   }
 
   // ---- phase 1: direct pass, page-table probe, hit bitmap, first-occurrence claims of misses ----------
-  int my_tail = 0, my_opt = 0;
-  for (int f = tid; f < nsel; f += NT) {
-    const int32_t p = sel[f];
-    int32_t loc;
-    const int c = classify(a, r, n, opt, p, &loc);
-    if (c == kDirectTail) { ++my_tail; continue; }
-    if (c == kDirectOpt) { ++my_opt; continue; }
-    const int32_t s = pt[p];
-    if (s >= 0) atomicOr(&s_hit[s >> 5], 1u << (s & 31));
-    else atomicMin(&pt[p], INT_MIN + f);
+  // A missing position p gets atomicMin(pt[p], INT_MIN + f) from each selection f naming it, so the word
+  // ends holding the first occurrence whatever the order of the atomics.
+  int my_tail = 0, my_opt = 0, my_hit_sel = 0, my_miss_sel = 0;
+  int32_t code[kPer];
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+    if (!one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) pv[e] = fb + e < nsel ? sel[fb + e] : 0;
+    }
+    int32_t ptv[kPer];
+    bool pend[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {  // classify and issue every page-table load before using any
+      const int f = fb + e;
+      pend[e] = false;
+      code[e] = -1;
+      ptv[e] = -1;
+      if (f < nsel) {
+        int32_t loc;
+        const int c = classify(a, r, n, opt, pv[e], &loc);
+        if (c == kDirectTail) { ++my_tail; code[e] = loc; }
+        else if (c == kDirectOpt) { ++my_opt; code[e] = loc; }
+        else { pend[e] = true; ptv[e] = pt[pv[e]]; }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (!pend[e]) continue;
+      const int32_t s = ptv[e];
+      if (s >= 0) {
+        ++my_hit_sel;
+        atomicOr(&s_hit[s >> 5], 1u << (s & 31));
+        code[e] = (int32_t)(hot0 + s);
+      } else {
+        ++my_miss_sel;
+        claim_min(&pt[pv[e]], INT_MIN + fb + e);
+        code[e] = kCodeMiss;
+      }
+    }
+    if (!one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (fb + e < nsel) locs[fb + e] = code[e];
+    }
   }
-  __threadfence();
   __syncthreads();
 
-  // ---- phase 2: distinct misses in first-occurrence order (rounds of NT selections, ascending f) -------
-  int my_hit_sel = 0, my_miss_sel = 0;
+  // ---- phase 2: distinct misses in first-occurrence order (ascending f) --------------------------------
   int m = 0;
-  for (int base = 0; base < nsel; base += NT) {
-    const int f = base + tid;
-    bool first = false;
-    int32_t p = 0;
-    if (f < nsel) {
-      p = sel[f];
-      int32_t loc;
-      if (classify(a, r, n, opt, p, &loc) == kDirectNone) {
-        const int32_t v = ld_agent(&pt[p]);
-        if (v >= 0) ++my_hit_sel;
-        else { ++my_miss_sel; first = (v == INT_MIN + f); }
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+    if (!one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        code[e] = fb + e < nsel ? locs[fb + e] : -1;
+        pv[e] = fb + e < nsel ? sel[fb + e] : 0;
+      }
+    }
+    bool first[kPer];
+    int nfirst = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      first[e] = false;
+      if (fb + e < nsel && code[e] == kCodeMiss) {
+        const int32_t v = rmw_read(&pt[pv[e]]);
+        first[e] = v == INT_MIN + fb + e;
+        if (!first[e]) code[e] = v;  // a repeat keeps the claim, i.e. its first occurrence
+        nfirst += first[e];
       }
     }
     int cnt;
-    const int idx = block_flag_scan(first, &cnt, s_wsum);
-    if (first) ppos[m + idx] = p;
+    int idx = m + block_sum_scan(nfirst, &cnt, s_wsum);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (first[e]) {
+        ppos[idx] = pv[e];
+        code[e] = -2 - idx;
+        locs[fb + e] = code[e];
+        ++idx;
+      } else if (!one_round && fb + e < nsel) {
+        locs[fb + e] = code[e];
+      }
+    }
     m += cnt;
   }
+  __syncthreads();
 
-  // ---- phase 3: hit count, victims over the slot order, staging overflow check -----------------------
+  // ---- phase 3: hit count, staging overflow check, victims over the slot order -----------------------
   int nhit = 0;
   {
     const int hw = tid < nwords ? __popc(s_hit[tid]) : 0;
@@ -197,9 +281,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   const int v = m < free_slots ? m : free_slots;
   const int over = m - v;
   if (over > a.S) {
-    __threadfence();
-    __syncthreads();
-    for (int i = tid; i < m; i += NT) st_agent(&pt[ppos[i]], -1);
+    for (int i = tid; i < m; i += NT) pt[ppos[i]] = -1;  // drop the claims
     for (int f = tid; f < total; f += NT) locs[f] = -1;
     if (tid == 0) {
       a.m.plan_n[r] = 0;
@@ -214,26 +296,32 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   }
   const int n_keep = free_slots - v;
   {
-    int nonhit_base = 0;
-    for (int base = 0; base < B; base += NT) {
-      const int q = base + tid;
-      bool nh = false;
-      int s = 0;
-      if (q < B) {
-        s = s_order[q];
-        nh = ((s_hit[s >> 5] >> (s & 31)) & 1u) == 0u;
+    // thread t walks order positions [t * per, t * per + per): one block scan ranks every non-hit slot
+    const int per = (B + NT - 1) / NT;
+    const int q0 = tid * per;
+    uint16_t sl[kSlotsPerThread];
+    int cnt_nh = 0;
+#pragma unroll
+    for (int e = 0; e < kSlotsPerThread; ++e) {
+      sl[e] = 0xFFFF;
+      if (e < per && q0 + e < B) {
+        const int s = s_order[q0 + e];
+        if (((s_hit[s >> 5] >> (s & 31)) & 1u) == 0u) { sl[e] = (uint16_t)s; ++cnt_nh; }
       }
-      int cnt;
-      const int rank = nonhit_base + block_flag_scan(nh, &cnt, s_wsum);
-      if (nh) {
-        if (rank < v) {
-          s_victim[rank] = (uint16_t)s;
-          atomicOr(&s_vic[s >> 5], 1u << (s & 31));
-        } else {
-          order[rank - v] = (uint16_t)s;  // unselected non-victims keep their relative order
-        }
+    }
+    int tot;
+    int rank = block_sum_scan(cnt_nh, &tot, s_wsum);
+#pragma unroll
+    for (int e = 0; e < kSlotsPerThread; ++e) {
+      if (sl[e] == 0xFFFF) continue;
+      const int s = sl[e];
+      if (rank < v) {
+        s_victim[rank] = (uint16_t)s;
+        atomicOr(&s_vic[s >> 5], 1u << (s & 31));
+      } else {
+        order[rank - v] = (uint16_t)s;  // unselected non-victims keep their relative order
       }
-      nonhit_base += cnt;
+      ++rank;
     }
   }
   __syncthreads();
@@ -261,40 +349,45 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     const int32_t p = ppos[i];
     if (i < v) {
       const int s = s_victim[i];
-      const int32_t old = key[s];
-      if (old >= 0) st_agent(&pt[old], -1);  // eviction: old is not selected in this call
+      const int32_t old = s_key[s];
+      if (old >= 0) pt[old] = -1;  // eviction: old is not pending in this call
       key[s] = p;
       rec[s] = e2;
-      st_agent(&pt[p], s);
-      pdst[i] = (int32_t)((int64_t)r * B + s);
+      pt[p] = s;
+      pdst[i] = (int32_t)(hot0 + s);
     } else {
-      st_agent(&pt[p], -2 - (i - v));  // staged: a transient code read back by the emit phase
-      pdst[i] = (int32_t)(a.stg_base + (int64_t)r * a.S + (i - v));
+      pt[p] = -1;  // staged rows stay outside the hot cache
+      pdst[i] = (int32_t)(stg0 + (i - v));
     }
   }
-  __threadfence();
-  __syncthreads();
 
   // ---- phase 5: publish locations in selection order ---------------------------------------------------
-  for (int f = tid; f < total; f += NT) {
-    int32_t loc = -1;
-    if (f < nsel) {
-      const int32_t p = sel[f];
-      if (classify(a, r, n, opt, p, &loc) == kDirectNone) {
-        const int32_t s = ld_agent(&pt[p]);
-        loc = s >= 0 ? (int32_t)((int64_t)r * B + s) : (int32_t)(a.stg_base + (int64_t)r * a.S + (-2 - s));
+  // A repeated miss reads its first occurrence's entry, which holds either -2 - i or, once that thread got
+  // here, the final location: both name the same row.
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int f = fb + e;
+      if (f >= nsel) continue;
+      int32_t c = one_round ? code[e] : locs[f];
+      if (is_claim(c)) c = rmw_read(&locs[c - INT_MIN]);
+      int32_t loc;
+      if (c >= 0) {
+        loc = c;
+      } else {
+        const int i = -2 - c;
+        loc = i < v ? (int32_t)(hot0 + s_victim[i]) : (int32_t)(stg0 + (i - v));
       }
+      locs[f] = loc;
     }
-    locs[f] = loc;
   }
+  for (int f = nsel + tid; f < total; f += NT) locs[f] = -1;
   atomicAdd(&s_cnt[0], my_tail);
   atomicAdd(&s_cnt[1], my_opt);
   atomicAdd(&s_cnt[2], my_hit_sel);
   atomicAdd(&s_cnt[3], my_miss_sel);
-  __threadfence();
   __syncthreads();
-  // staged rows stay outside the hot cache: clear their transient page-table codes
-  for (int i = v + tid; i < m; i += NT) st_agent(&pt[ppos[i]], -1);
   if (tid == 0) {
     a.m.plan_n[r] = m;
     if (a.stats) {
