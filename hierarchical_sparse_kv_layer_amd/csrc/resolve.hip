@@ -18,8 +18,8 @@
 //     that list, skipping hit slots, yields the oldest unselected slots in order -- no sort, no atomics;
 //   * the new order is written as [unselected non-victims in old order][fills by slot][hits by slot],
 //     which is exactly the ascending (rec, slot) order once fills get 2e and hits 2e+1 (epochs increase).
-// The host-to-device copies of the missing rows run in gather_kernel, a second launch whose grid scales
-// with the batch so that enough 16-byte host reads are in flight to fill the PCIe link.
+// The host-to-device copies of the missing rows run in gather_kernel, a second launch that spreads the rows
+// of all requests evenly over its waves so that enough 16-byte host reads are in flight to fill the PCIe link.
 #include <climits>
 
 #include "hsk_internal.h"
@@ -31,6 +31,9 @@ namespace hsk {
 // multi-XCD part an agent-scope fence would write back and invalidate the whole L2.  A value that another
 // thread changed with an atomic is read back with an atomic (it executes at L2), never a plain load that
 // could hit a line this CU cached before the atomic.
+// LDS writes of this wave complete, then a workgroup barrier; global stores stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int32_t rmw_read(int32_t* p) {
   return __hip_atomic_fetch_or(p, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -38,27 +41,8 @@ __device__ __forceinline__ void claim_min(int32_t* p, int32_t v) {
   __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Exclusive prefix count of `flag` over the workgroup in thread order; *total gets the count.
-// Uses wave ballots plus one LDS slot per wave.  Must be called by every thread of the block.
-__device__ __forceinline__ int block_flag_scan(bool flag, int* total, int* s_wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint64_t mask = __ballot(flag);
-  const int below = __popcll(mask & ((1ull << lane) - 1ull));
-  if (lane == 0) s_wsum[wave] = __popcll(mask);
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kResolveWaves; ++w) {
-    const int c = s_wsum[w];
-    base += (w < wave) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + below;
-}
-
-// Exclusive prefix sum of small non-negative ints over the workgroup in thread order.
+// Exclusive prefix sum of small non-negative ints over the workgroup in thread order (LDS-only barriers:
+// global stores of the caller stay in flight).  Must be called by every thread of the block.
 __device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
@@ -68,7 +52,7 @@ __device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
     if (lane >= o) x += y;
   }
   if (lane == 63) s_wsum[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < kResolveWaves; ++w) {
@@ -76,7 +60,7 @@ __device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
     base += (w < wave) ? c : 0;
     tot += c;
   }
-  __syncthreads();
+  lds_barrier();
   *total = tot;
   return base + x - v;
 }
@@ -120,6 +104,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   __shared__ int32_t s_vic_pre[HSK_MAX_HOT_SLOTS / 32];
   __shared__ uint16_t s_order[HSK_MAX_HOT_SLOTS];
   __shared__ uint16_t s_victim[HSK_MAX_HOT_SLOTS];
+  __shared__ uint16_t s_neworder[HSK_MAX_HOT_SLOTS];
   __shared__ int32_t s_key[HSK_MAX_HOT_SLOTS];
   __shared__ int s_wsum[kResolveWaves];
   __shared__ int s_cnt[4];
@@ -145,14 +130,31 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   int32_t* pdst = a.m.plan_dst + (int64_t)r * a.plan_cap;
   const int64_t hot0 = (int64_t)r * B;
   const int64_t stg0 = a.stg_base + (int64_t)r * a.S;
+  // Stores count in the same in-order counter as loads on this architecture, so a load issued after a
+  // burst of stores waits for all of them: every phase below does its loads before its stores, and the
+  // metadata stores come last.
   constexpr int per_round = kResolveThreads * kPer;
   const int nrounds = (nsel + per_round - 1) / per_round;
   const bool one_round = nrounds <= 1;
 
   // ---- phase 0: slot order and keys to LDS, clear bitmaps, validate every selected position ------------
-  for (int q = tid; q < B; q += NT) {
-    s_order[q] = order[q];
-    s_key[q] = key[q];
+  {
+    uint16_t ov_[kSlotsPerThread];
+    int32_t kv_[kSlotsPerThread];
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int q = tid + j * NT;
+      ov_[j] = q < B ? order[q] : 0;
+      kv_[j] = q < B ? key[q] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kSlotsPerThread; ++j) {
+      const int q = tid + j * NT;
+      if (q < B) {
+        s_order[q] = ov_[j];
+        s_key[q] = kv_[j];
+      }
+    }
   }
   for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
   if (tid < 4) s_cnt[tid] = 0;
@@ -192,20 +194,33 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
 #pragma unroll
       for (int e = 0; e < kPer; ++e) pv[e] = fb + e < nsel ? sel[fb + e] : 0;
     }
-    int32_t ptv[kPer];
+    // branch-free loads, all issued before any is used: the page-table word (and the optional-page map
+    // entry) of every selection, direct or not
+    int32_t ptv[kPer], ovv[kPer];
     bool pend[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {  // classify and issue every page-table load before using any
+    for (int e = 0; e < kPer; ++e) ptv[e] = pt[pv[e]];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t page = opt ? min((int64_t)(pv[e] / a.P), a.max_pages - 1) : 0;
+      ovv[e] = opt ? opt[page] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
       const int f = fb + e;
+      const int32_t p = pv[e];
       pend[e] = false;
       code[e] = -1;
-      ptv[e] = -1;
       if (f < nsel) {
-        int32_t loc;
-        const int c = classify(a, r, n, opt, pv[e], &loc);
-        if (c == kDirectTail) { ++my_tail; code[e] = loc; }
-        else if (c == kDirectOpt) { ++my_opt; code[e] = loc; }
-        else { pend[e] = true; ptv[e] = pt[pv[e]]; }
+        if (p >= n - a.T) {
+          ++my_tail;
+          code[e] = (int32_t)((int64_t)a.R * a.B + (int64_t)r * a.T + (p % a.T));
+        } else if (opt && (int64_t)(p / a.P) < n / a.P && ovv[e] >= 0) {
+          ++my_opt;
+          code[e] = (int32_t)(a.opt_base + (int64_t)ovv[e] * a.P + (p % a.P));
+        } else {
+          pend[e] = true;
+        }
       }
     }
 #pragma unroll
@@ -243,13 +258,15 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     }
     bool first[kPer];
     int nfirst = 0;
+    int32_t cv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) cv[e] = rmw_read(&pt[pv[e]]);  // branch-free: all issued together
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       first[e] = false;
       if (fb + e < nsel && code[e] == kCodeMiss) {
-        const int32_t v = rmw_read(&pt[pv[e]]);
-        first[e] = v == INT_MIN + fb + e;
-        if (!first[e]) code[e] = v;  // a repeat keeps the claim, i.e. its first occurrence
+        first[e] = cv[e] == INT_MIN + fb + e;
+        if (!first[e]) code[e] = cv[e];  // a repeat keeps the claim, i.e. its first occurrence
         nfirst += first[e];
       }
     }
@@ -269,6 +286,31 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     m += cnt;
   }
   __syncthreads();
+  // repeats of a miss look up their first occurrence's miss index now, before the stores of the next phases
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+    if (!one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) code[e] = fb + e < nsel ? locs[fb + e] : -1;
+    }
+    bool rep = false;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      if (fb + e < nsel && is_claim(code[e])) {
+        code[e] = rmw_read(&locs[code[e] - INT_MIN]);
+        rep = true;
+      }
+    }
+    if (!one_round && rep) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (fb + e < nsel) locs[fb + e] = code[e];
+    }
+  }
+
+  // the first two strided miss entries this thread will fill, read before the stores of phases 4 and 5
+  const int32_t pp0 = tid < m ? ppos[tid] : 0;
+  const int32_t pp1 = tid + NT < m ? ppos[tid + NT] : 0;
 
   // ---- phase 3: hit count, staging overflow check, victims over the slot order -----------------------
   int nhit = 0;
@@ -319,7 +361,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
         s_victim[rank] = (uint16_t)s;
         atomicOr(&s_vic[s >> 5], 1u << (s & 31));
       } else {
-        order[rank - v] = (uint16_t)s;  // unselected non-victims keep their relative order
+        s_neworder[rank - v] = (uint16_t)s;  // unselected non-victims keep their relative order
       }
       ++rank;
     }
@@ -333,20 +375,44 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   }
   __syncthreads();
 
-  // ---- phase 4: metadata update -- fills (2e) then hits (2e+1) at the most recent end ------------------
+  // ---- phase 4: publish locations in selection order ---------------------------------------------------
+  for (int rd = 0; rd < nrounds; ++rd) {
+    const int fb = rd * per_round + kPer * tid;
+    if (!one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) code[e] = fb + e < nsel ? locs[fb + e] : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int f = fb + e;
+      if (f >= nsel) continue;
+      const int32_t c = code[e];
+      int32_t loc;
+      if (c >= 0) {
+        loc = c;
+      } else {
+        const int i = -2 - c;
+        loc = i < v ? (int32_t)(hot0 + s_victim[i]) : (int32_t)(stg0 + (i - v));
+      }
+      locs[f] = loc;
+    }
+  }
+  for (int f = nsel + tid; f < total; f += NT) locs[f] = -1;
+
+  // ---- phase 5: metadata update -- fills (2e) then hits (2e+1) at the most recent end ------------------
   const uint32_t e2 = 2u * a.epoch;
   for (int s = tid; s < B; s += NT) {
     const int w = s >> 5;
     const uint32_t bit = 1u << (s & 31), below = bit - 1u;
     if (s_vic[w] & bit) {
-      order[n_keep + s_vic_pre[w] + __popc(s_vic[w] & below)] = (uint16_t)s;
+      s_neworder[n_keep + s_vic_pre[w] + __popc(s_vic[w] & below)] = (uint16_t)s;
     } else if (s_hit[w] & bit) {
-      order[n_keep + v + s_hit_pre[w] + __popc(s_hit[w] & below)] = (uint16_t)s;
+      s_neworder[n_keep + v + s_hit_pre[w] + __popc(s_hit[w] & below)] = (uint16_t)s;
       rec[s] = e2 + 1u;
     }
   }
   for (int i = tid; i < m; i += NT) {
-    const int32_t p = ppos[i];
+    const int32_t p = i == tid ? pp0 : i == tid + NT ? pp1 : ppos[i];
     if (i < v) {
       const int s = s_victim[i];
       const int32_t old = s_key[s];
@@ -360,34 +426,26 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       pdst[i] = (int32_t)(stg0 + (i - v));
     }
   }
-
-  // ---- phase 5: publish locations in selection order ---------------------------------------------------
-  // A repeated miss reads its first occurrence's entry, which holds either -2 - i or, once that thread got
-  // here, the final location: both name the same row.
-  for (int rd = 0; rd < nrounds; ++rd) {
-    const int fb = rd * per_round + kPer * tid;
+  lds_barrier();
+  for (int q = tid; q < B; q += NT) order[q] = s_neworder[q];
+  // class counts: wave sums first (1,024 same-address LDS atomics would serialise for microseconds)
+  {
+    int c0 = my_tail, c1 = my_opt, c2 = my_hit_sel, c3 = my_miss_sel;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int f = fb + e;
-      if (f >= nsel) continue;
-      int32_t c = one_round ? code[e] : locs[f];
-      if (is_claim(c)) c = rmw_read(&locs[c - INT_MIN]);
-      int32_t loc;
-      if (c >= 0) {
-        loc = c;
-      } else {
-        const int i = -2 - c;
-        loc = i < v ? (int32_t)(hot0 + s_victim[i]) : (int32_t)(stg0 + (i - v));
-      }
-      locs[f] = loc;
+    for (int o = 32; o > 0; o >>= 1) {
+      c0 += __shfl_xor(c0, o, 64);
+      c1 += __shfl_xor(c1, o, 64);
+      c2 += __shfl_xor(c2, o, 64);
+      c3 += __shfl_xor(c3, o, 64);
+    }
+    if ((tid & 63) == 0) {
+      atomicAdd(&s_cnt[0], c0);
+      atomicAdd(&s_cnt[1], c1);
+      atomicAdd(&s_cnt[2], c2);
+      atomicAdd(&s_cnt[3], c3);
     }
   }
-  for (int f = nsel + tid; f < total; f += NT) locs[f] = -1;
-  atomicAdd(&s_cnt[0], my_tail);
-  atomicAdd(&s_cnt[1], my_opt);
-  atomicAdd(&s_cnt[2], my_hit_sel);
-  atomicAdd(&s_cnt[3], my_miss_sel);
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     a.m.plan_n[r] = m;
     if (a.stats) {
@@ -429,24 +487,84 @@ __device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32
   }
 }
 
-// Host -> device gather of a miss plan (HiSparse section 3.4 phase 4, section 3.5 replay): every wave
-// copies whole rows from pinned host memory (zero-copy 16-byte loads over PCIe) into their pool rows.
-// Grid: (blocks per request, requests); each request's rows are spread over its blocks' waves.
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs g) {
-  const int r = blockIdx.y;
+// Host -> device gather of a miss plan (HiSparse section 3.4 phase 4 "GPU-assisted IO", section 3.5
+// replay): 16-byte zero-copy loads from pinned host memory over PCIe into the pool rows.
+// Rows are numbered globally in request order (rows of earlier requests first) and wave w of the 1-D grid
+// copies the rows whose number is w modulo the number of waves, so every wave gets the same share however
+// the misses are spread over requests.  A wave first lists its rows (host and pool addresses) in LDS, 64
+// requests at a time with one request per lane, then copies the listed rows as one stream of 16-byte chunks
+// over its 64 lanes, kDepth loads in flight per lane before the stores.
+constexpr int kGatherWaves = kGatherThreads / 64;
+constexpr int kGatherList = 64;
+
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs g, int32_t R) {
+  __shared__ const char* s_src[kGatherWaves][kGatherList];
+  __shared__ char* s_dst[kGatherWaves][kGatherList];
+  constexpr int kDepth = 8;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  constexpr int kWaves = kGatherThreads / 64;
-  const int m = g.plan_n[r];
-  const int chunks = g.row_bytes >> 4;
-  const char* hbase = g.host + (int64_t)r * g.host_req_stride;
-  const int32_t* pp = g.plan_pos + (int64_t)r * g.plan_cap;
-  const int32_t* pd = g.plan_dst + (int64_t)r * g.plan_cap;
-  for (int i = blockIdx.x * kWaves + wave; i < m; i += gridDim.x * kWaves) {
-    const u32x4* src = (const u32x4*)(hbase + (int64_t)pp[i] * g.row_bytes);
-    u32x4* dst = (u32x4*)(g.pool + (int64_t)pd[i] * g.row_bytes);
-    wave_copy_row(src, dst, chunks, lane);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * kGatherWaves;
+  const int64_t gw = (int64_t)blockIdx.x * kGatherWaves + wave;
+  const int cpr = g.row_bytes >> 4;  // 16-byte chunks per row
+  const uint64_t below = (1ull << lane) - 1ull;
+  int nl = 0;
+
+  auto flush = [&]() {
+    const int total = nl * cpr;
+    for (int x0 = 0; x0 < total; x0 += 64 * kDepth) {
+      u32x4 buf[kDepth];
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int x = x0 + d * 64 + lane;
+        if (x < total) {
+          const int row = x / cpr;
+          buf[d] = __builtin_nontemporal_load((const u32x4*)s_src[wave][row] + (x - row * cpr));
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) {
+        const int x = x0 + d * 64 + lane;
+        if (x < total) {
+          const int row = x / cpr;
+          ((u32x4*)s_dst[wave][row])[x - row * cpr] = buf[d];
+        }
+      }
+    }
+    nl = 0;
+  };
+
+  int64_t C = 0;  // rows of the requests before this group of 64
+  for (int r0 = 0; r0 < R; r0 += 64) {
+    const int r = r0 + lane;
+    const int m = r < R ? g.plan_n[r] : 0;
+    int64_t incl = m;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int64_t Cr = C + incl - m;
+    const int64_t i0 = ((gw - Cr) % nw + nw) % nw;  // first row of request r that falls to this wave
+    const int cnt = i0 < m ? (int)((m - 1 - i0) / nw + 1) : 0;
+    const char* hbase = g.host + (int64_t)r * g.host_req_stride;
+    const int32_t* pp = g.plan_pos + (int64_t)r * g.plan_cap;
+    const int32_t* pd = g.plan_dst + (int64_t)r * g.plan_cap;
+    for (int k = 0; __ballot(k < cnt); ++k) {
+      const bool has = k < cnt;
+      const uint64_t mask = __ballot(has);
+      const int nnew = __popcll(mask);
+      if (nl + nnew > kGatherList) flush();
+      if (has) {
+        const int slot = nl + __popcll(mask & below);
+        const int64_t i = i0 + (int64_t)k * nw;
+        s_src[wave][slot] = hbase + (int64_t)pp[i] * g.row_bytes;
+        s_dst[wave][slot] = g.pool + (int64_t)pd[i] * g.row_bytes;
+      }
+      nl += nnew;
+    }
+    C += __shfl(incl, 63, 64);
   }
+  if (nl) flush();
 }
 
 // Tail rows [n_r - T, n_r) of every request: host -> pool row R*B + r*T + (p mod T).
@@ -518,8 +636,8 @@ hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks_per_req, hipStream_t s) {
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks_per_req, R), dim3(kGatherThreads), 0, s, g);
+hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s) {
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kGatherThreads), 0, s, g, R);
   return hipGetLastError();
 }
 
