@@ -62,8 +62,10 @@ struct AttnArgs {
 //
 // Rows are gathered by their locations straight from the pool into LDS with 16-byte LDS-DMA loads, three
 // tiles in flight.  A tile is stored as 9 groups of 8 chunks (16 bytes each) per row, and the chunk position
-// inside a row's 128-byte group is XOR-swizzled by a function of the row so that the 16-row A-operand reads
-// and the transposing V reads are both free of LDS bank conflicts.
+// inside a row's 128-byte group is XOR-swizzled by f(a) = ((a & 3) << 1) | (a >> 2), a = (row / 2) mod 8:
+// f is a bijection (16-row A-operand reads hit 16 distinct 16-byte bank groups) and f(a) / 2 takes four
+// different values on each run of four a (the transposing V reads of 32 lanes, 8 rows x 4 column chunks,
+// hit 32 distinct 8-byte bank pairs).
 // ------------------------------------------------------------------------------------------------------
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -95,9 +97,12 @@ struct MlaArgs {
 };
 
 // byte offset in a tile of 16-byte chunk c (values 8c..8c+7) of tile row t
-__device__ __forceinline__ int tile_off(int t, int c) {
+__device__ __forceinline__ int tile_swz(int t) {
   const int a = (t >> 1) & 7;
-  const int f = (a >> 1) | ((a & 1) << 2);
+  return ((a & 3) << 1) | (a >> 2);
+}
+__device__ __forceinline__ int tile_off(int t, int c) {
+  const int f = tile_swz(t);
   return (((c >> 3) << 8) + (t << 3) + ((c & 7) ^ f)) << 4;
 }
 
@@ -190,9 +195,7 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
   for (int v = 0; v < NTOK; ++v) {
     tok[v] = 8 * ((wave + NW * v) & 3) + (lane >> 3);
-    const int aa = (tok[v] >> 1) & 7;
-    const int f = (aa >> 1) | ((aa & 1) << 2);
-    swz[v] = (((lane & 7) ^ f) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
+    swz[v] = (((lane & 7) ^ tile_swz(tok[v])) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
   }
 
   auto issue = [&](int T, int b) {
@@ -282,31 +285,70 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m_run[hb], tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[hb] - mn);
+      // The reference maximum moves only when a score exceeds it by more than 2^8 (log2 units 8): until
+      // then the weights exp2(s - m) stay below 256, exact enough in bf16 and fp32, and the 128 output
+      // accumulators need no rescaling.  The first tile always moves it (from -inf).
+      if (__ballot(tmax > m_run[hb] + 8.f)) {
+        const float mn = fmaxf(m_run[hb], tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[hb] - mn);
+        l_run[hb] *= alpha;
+        m_run[hb] = mn;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[cb][hb] *= alpha;
+      }
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sv[i] - mn);
+        const float p = __builtin_amdgcn_exp2f(sv[i] - m_run[hb]);
         psum += p;
         pf[hb][i] = (__bf16)p;
       }
-      l_run[hb] = l_run[hb] * alpha + psum;
-      m_run[hb] = mn;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) oacc[cb][hb] *= alpha;
+      l_run[hb] += psum;
     }
 
-    // O^T += V^T P over this wave's half of the value columns
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const HSK_LDS char* p0 = tile + v_base[cb & 3] + (cb >> 2) * kGroup * 2;
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSK_LDS i16x4*)p0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HSK_LDS i16x4*)(p0 + 2048));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb)
-        oacc[cb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[hb], oacc[cb][hb], 0, 0, 0);
+    // O^T += V^T P over this wave's half of the value columns.  The transposing reads are issued from
+    // inline assembly with immediate offsets from four per-tile base addresses (column block cb = 4 u + w
+    // reads base w + u * 4096, rows 16..31 2048 bytes further), two column blocks ahead of their products.
+    {
+      const uint32_t tb0 = (uint32_t)(uintptr_t)tile;
+      const uint32_t vb0 = tb0 + v_base[0], vb1 = tb0 + v_base[1], vb2 = tb0 + v_base[2], vb3 = tb0 + v_base[3];
+      i16x4 vlo[3], vhi[3];
+#define HSK_TR_READ(CB)                                                                                   \
+  {                                                                                                      \
+    const uint32_t vb_ = ((CB)&3) == 0 ? vb0 : ((CB)&3) == 1 ? vb1 : ((CB)&3) == 2 ? vb2 : vb3;        \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"                                                   \
+                 : "=v"(vlo[(CB) % 3]) : "v"(vb_), "i"(((CB) >> 2) * 4096) : "memory");                 \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"                                                   \
+                 : "=v"(vhi[(CB) % 3]) : "v"(vb_), "i"(((CB) >> 2) * 4096 + 2048) : "memory");          \
+  }
+#define HSK_PV_STEP(CB, WAIT)                                                                             \
+  {                                                                                                      \
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vlo[(CB) % 3]), "+v"(vhi[(CB) % 3]) : "i"(WAIT));      \
+    const bf16x8 vf = __builtin_bit_cast(                                                                \
+        bf16x8, __builtin_shufflevector(vlo[(CB) % 3], vhi[(CB) % 3], 0, 1, 2, 3, 4, 5, 6, 7));         \
+    _Pragma("unroll") for (int hb = 0; hb < NHB; ++hb) oacc[CB][hb] =                                   \
+        __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[hb], oacc[CB][hb], 0, 0, 0);                     \
+  }
+      HSK_TR_READ(0) HSK_TR_READ(1)
+      HSK_TR_READ(2) HSK_PV_STEP(0, 4)
+      HSK_TR_READ(3) HSK_PV_STEP(1, 4)
+      HSK_TR_READ(4) HSK_PV_STEP(2, 4)
+      HSK_TR_READ(5) HSK_PV_STEP(3, 4)
+      HSK_TR_READ(6) HSK_PV_STEP(4, 4)
+      HSK_TR_READ(7) HSK_PV_STEP(5, 4)
+      HSK_TR_READ(8) HSK_PV_STEP(6, 4)
+      HSK_TR_READ(9) HSK_PV_STEP(7, 4)
+      HSK_TR_READ(10) HSK_PV_STEP(8, 4)
+      HSK_TR_READ(11) HSK_PV_STEP(9, 4)
+      HSK_TR_READ(12) HSK_PV_STEP(10, 4)
+      HSK_TR_READ(13) HSK_PV_STEP(11, 4)
+      HSK_TR_READ(14) HSK_PV_STEP(12, 4)
+      HSK_TR_READ(15) HSK_PV_STEP(13, 4)
+      HSK_PV_STEP(14, 2)
+      HSK_PV_STEP(15, 0)
+#undef HSK_TR_READ
+#undef HSK_PV_STEP
+      static_assert(CB == 16, "the unrolled P.V sequence covers 16 column blocks");
     }
   }
 
