@@ -432,31 +432,70 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------------
-// combine: grid (RQ, H), 128 threads
+// combine: one wave per (query, head), 4 waves per block.  Lane l owns float4 chunks l and l + 64 of the
+// dv output values (dv <= 512); the partitions' weights e^{m_s - M} / L come from a lane-parallel max and
+// sum over the partitions, and the partial outputs are read four partitions at a time.
 // ------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a, int dv) {
-  const int rq = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t RQ = (int64_t)a.R * a.Qmax;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+  if (item >= RQ * a.H) return;
+  const int rq = (int)(item / a.H), h = (int)(item % a.H);
   if (a.nq) {
     const int r = rq / a.Qmax, j = rq % a.Qmax;
     if (j >= a.nq[r]) return;
   }
+  const int S = a.split;
+  const int64_t p0 = (int64_t)rq * S * a.H + h;  // partition s of (rq, h) is p0 + s * H
   float M = -INFINITY;
-  for (int s = 0; s < a.split; ++s) M = fmaxf(M, a.pm[((int64_t)rq * a.split + s) * a.H + h]);
+  for (int s0 = 0; s0 < S; s0 += 64)
+    if (s0 + lane < S) M = fmaxf(M, a.pm[p0 + (int64_t)(s0 + lane) * a.H]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   float L = 0.f;
-  for (int s = 0; s < a.split; ++s) {
-    const int64_t ps = ((int64_t)rq * a.split + s) * a.H + h;
-    const float m = a.pm[ps];
-    L += (m == -INFINITY) ? 0.f : __expf(m - M) * a.pl[ps];
-  }
-  const float invL = 1.f / L;
-  for (int c = threadIdx.x; c < dv; c += 128) {
-    float acc = 0.f;
-    for (int s = 0; s < a.split; ++s) {
-      const int64_t ps = ((int64_t)rq * a.split + s) * a.H + h;
-      const float m = a.pm[ps];
-      if (m != -INFINITY) acc += __expf(m - M) * a.po[ps * dv + c];
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    if (s0 + lane < S) {
+      const float m = a.pm[p0 + (int64_t)(s0 + lane) * a.H];
+      if (m != -INFINITY) L += __expf(m - M) * a.pl[p0 + (int64_t)(s0 + lane) * a.H];
     }
-    a.out[((int64_t)rq * a.H + h) * dv + c] = f2bf16(acc * invL);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+  const float invL = 1.f / L;
+  const int nchunk = dv >> 2;
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float w[4];
+    f32x4 v[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sidx = s0 + u;
+      const float m = sidx < S ? a.pm[p0 + (int64_t)sidx * a.H] : -INFINITY;
+      w[u] = m == -INFINITY ? 0.f : __expf(m - M) * invL;
+      const f32x4* po = (const f32x4*)(a.po + (p0 + (int64_t)(sidx < S ? sidx : 0) * a.H) * dv);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int x = lane + 64 * c;
+        v[u][c] = (sidx < S && x < nchunk) ? po[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[c] += v[u][c] * w[u];
+  }
+  uint16_t* out = a.out + ((int64_t)rq * a.H + h) * dv;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int x = lane + 64 * c;
+    if (x < nchunk) {
+      u32x2 o;
+      o.x = (uint32_t)f2bf16(acc[c][0]) | ((uint32_t)f2bf16(acc[c][1]) << 16);
+      o.y = (uint32_t)f2bf16(acc[c][2]) | ((uint32_t)f2bf16(acc[c][3]) << 16);
+      *(u32x2*)(out + 4 * x) = o;
+    }
   }
 }
 
@@ -581,7 +620,7 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
                        dim3(64 * (d->heads / d->kv_heads)), 0, s, a);
     HSK_HIP(hipGetLastError());
   }
-  hipLaunchKernelGGL(combine_kernel, dim3(RQ, d->heads), dim3(128), 0, s, a, d->dv);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((RQ * d->heads + 3) / 4)), dim3(256), 0, s, a, d->dv);
   HSK_HIP(hipGetLastError());
   return HSK_OK;
 }
