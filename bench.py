@@ -185,6 +185,245 @@ def memcpy_ceiling(nbytes: int = 1 << 28, reps: int = 8) -> dict:
     return {"bytes": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
+# ------------------------------------------------------------------------------------------------------
+# other workloads (python bench.py --workload verify|adaptive|quest): one JSON line each, for the record of
+# every hot-path step; the default run is the 100K batch-64 decode above
+# ------------------------------------------------------------------------------------------------------
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def run_verify(hsk, synth, w, steps: int) -> dict:
+    """Speculative verification: W queries per request share rows; each distinct missing row is copied once
+    and unions beyond the free hot slots go to staging rows (Adaptive DHiSparse section 3.3)."""
+    import torch
+    R, Q, k, L = w.requests, w.queries, w.top_k, w.layers
+    st = hsk.KVStore(requests=R, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
+                     tail_rows=w.tail_rows, ctx=w.ctx, max_queries=Q, top_k=k, staging_rows=w.staging_rows)
+    t0 = time.perf_counter()
+    for s_ in range(w.sources):
+        for r in range(R):
+            synth.fill_kv_rows(st.host_ptr(s_, r), w, s_, r, 0, w.ctx)
+    st.commit_prefill()
+    log(f"[verify] host rows filled in {time.perf_counter() - t0:.1f} s")
+    sels = [torch.from_numpy(synth.selection_stream(w, l, steps=steps)).cuda() for l in range(L)]
+    ad = hsk.mla_desc(requests=R, max_queries=Q, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k, row_elems=w.row_elems,
+                      scale=w.scale)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = [torch.from_numpy(synth.queries(w, l, 0).view(np.int16)).cuda() for l in range(L)]
+    out = torch.empty((R, Q, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    locs = [torch.empty((R, Q, k), dtype=torch.int32, device="cuda") for _ in range(L)]
+    stats = [hsk.stats_tensor(R) for _ in range(L)]
+    pools = [st.pool_base(l) for l in range(L)]
+    res_ms, att_ms, agg = [], [], {"sel": 0, "miss_sel": 0, "miss": 0, "staged": 0}
+    stream = torch.cuda.current_stream()
+    t_all = 0.0
+    for t in range(steps):
+        evs = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(L):
+            e = [_ev() for _ in range(3)]
+            e[0].record(stream)
+            st.resolve_step(l, t + 1, sels[l][t], locs[l], stats[l])
+            e[1].record(stream)
+            hsk.sparse_decode_attn(ad, q[l], pools[l], locs[l], None, out, scratch, nb)
+            e[2].record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if t > 0:
+            t_all += dt
+            for e in evs:
+                res_ms.append(e[0].elapsed_time(e[1]))
+                att_ms.append(e[1].elapsed_time(e[2]))
+            for l in range(L):
+                sn = hsk.stats_to_numpy(stats[l])
+                agg["sel"] += int(sn["n_sel"].sum()); agg["miss_sel"] += int(sn["n_miss_sel"].sum())
+                agg["miss"] += int(sn["n_miss"].sum()); agg["staged"] += int(sn["n_staged"].sum())
+    status = st.sync_status()
+    st.close()
+    rows = R * Q * k * L * (steps - 1)
+    flops = 2.0 * w.heads * (w.dk + w.dv) * R * Q * k
+    att = float(np.mean(att_ms))
+    return {"workload": f"verify: {R} requests x {Q} queries, {L} layers, context {w.ctx}, top-k {k} per query, "
+                        f"60% shared, 75% kept, staging {w.staging_rows} rows", "steps_timed": steps - 1,
+            "rows_per_s": rows / t_all, "steps_per_s": (steps - 1) / t_all, "resolve_ms": float(np.mean(res_ms)),
+            "attention_ms": att, "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
+            "attention_frac_mfma_bf16": flops / (att * 1e-3) / 2.5e15,
+            "dedup_ratio": agg["miss_sel"] / max(1, agg["miss"]), "fetched_fraction": agg["miss"] / agg["sel"],
+            "staged_rows_per_layer_step": agg["staged"] / (L * (steps - 1)), "status": status}
+
+
+def run_adaptive(hsk, synth, w, steps: int) -> dict:
+    """Load-adaptive residency: optional-history pages resolve directly; a reclaim of whole requests (Eq. 4)
+    mid-run drops them and the host-fetch fraction rises (Adaptive DHiSparse section 3.1)."""
+    import torch
+    R, k, L, P = w.requests, w.top_k, w.layers, w.page_rows
+    frac = synth.residency_fractions(w)
+    n_pages = w.ctx // P
+    page_ids, nxt = [], 0
+    for r in range(R):
+        ids = np.full(n_pages, -1, np.int32)
+        pages = synth.resident_pages(w, r, float(frac[r]))
+        ids[pages] = nxt + np.arange(pages.size, dtype=np.int32)
+        nxt += pages.size
+        page_ids.append(ids)
+    st = hsk.KVStore(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=w.hot_slots, tail_rows=w.tail_rows,
+                     ctx=w.ctx, page_rows=P, opt_pool_pages=nxt, max_queries=1, top_k=k)
+    t0 = time.perf_counter()
+    for r in range(R):
+        synth.fill_kv_rows(st.host_ptr(0, r), w, 0, r, 0, w.ctx)
+    st.commit_prefill()
+    for r in range(R):
+        st.residency_set(0, r, page_ids[r])
+    torch.cuda.synchronize()
+    log(f"[adaptive] host rows filled, {nxt} optional pages resident, in {time.perf_counter() - t0:.1f} s")
+    sels = [torch.from_numpy(synth.selection_stream(w, l, steps=steps)).cuda() for l in range(L)]
+    ad = hsk.mla_desc(requests=R, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k, row_elems=w.row_elems,
+                      scale=w.scale)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = [torch.from_numpy(synth.queries(w, l, 0).view(np.int16)).cuda() for l in range(L)]
+    out = torch.empty((R, 1, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    locs = torch.empty((R, 1, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(R)
+    pool = st.pool_base(0)
+    stream = torch.cuda.current_stream()
+    per_step, res_ms, att_ms, t_all = [], [], [], 0.0
+    reclaimed = None
+    for t in range(steps):
+        if t == w.reclaim_step:
+            held = np.array([int((ids >= 0).sum()) for ids in page_ids], np.int64)
+            holders = np.nonzero(held > 0)[0][:w.reclaim_requests]
+            deficit = int(held[holders].sum())
+            qn = hsk.reclaim_plan(held, deficit)
+            for r in range(qn):
+                if held[r] > 0:
+                    st.residency_set(0, r, np.full(n_pages, -1, np.int32))
+            reclaimed = {"requests_walked": qn, "pages_dropped": deficit}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        miss = sel = opt = 0
+        evs = []
+        for l in range(L):
+            e = [_ev() for _ in range(3)]
+            e[0].record(stream)
+            st.resolve_step(0, L * t + l + 1, sels[l][t], locs, stats)   # both layers read the one shared source
+            e[1].record(stream)
+            hsk.sparse_decode_attn(ad, q[l], pool, locs, None, out, scratch, nb)
+            e[2].record(stream)
+            evs.append(e)
+            sn = hsk.stats_to_numpy(stats)
+            miss += int(sn["n_miss"].sum()); sel += int(sn["n_sel"].sum()); opt += int(sn["n_opt"].sum())
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        if t > 0:
+            t_all += dt
+            for e in evs:
+                res_ms.append(e[0].elapsed_time(e[1]))
+                att_ms.append(e[1].elapsed_time(e[2]))
+        per_step.append({"step": t, "host_fetch_fraction": miss / sel, "optional_fraction": opt / sel,
+                         "ms": dt * 1e3})
+    status = st.sync_status()
+    st.close()
+    before = [x["host_fetch_fraction"] for x in per_step[1:w.reclaim_step]]
+    after = [x["host_fetch_fraction"] for x in per_step[w.reclaim_step:]]
+    return {"workload": f"adaptive: {R} requests, {L} layers on one shared source, context {w.ctx}, 64-row optional "
+                        f"pages at 0/50/100% per request, reclaim of {w.reclaim_requests} requests at step "
+                        f"{w.reclaim_step}, top-k {k}", "optional_pages": nxt, "reclaim": reclaimed,
+            "rows_per_s": R * k * L * (steps - 1) / t_all, "steps_per_s": (steps - 1) / t_all,
+            "resolve_ms": float(np.mean(res_ms)), "attention_ms": float(np.mean(att_ms)),
+            "host_fetch_fraction_before_reclaim": float(np.mean(before)),
+            "host_fetch_fraction_after_reclaim": float(np.mean(after)), "per_step": per_step, "status": status}
+
+
+def run_quest(hsk, synth, w, steps: int) -> dict:
+    """Page-level GQA: layer 0 resolves the shared page selection; layers 1..7 replay its miss plan on a side
+    stream while the previous layer's attention runs (HiSparse section 3.5)."""
+    import torch
+    U, k, L = w.units, w.top_k, w.layers
+    st = hsk.KVStore(requests=U, sources=L, row_bytes=w.row_bytes, hot_slots=w.hot_slots, tail_rows=0, ctx=w.ctx,
+                     max_queries=1, top_k=k, host_alias=True)
+    t0 = time.perf_counter()
+    for u in range(U):
+        synth.fill_kv_rows(st.host_ptr(0, u), w, 0, u, 0, w.ctx)
+    log(f"[quest] host pages filled in {time.perf_counter() - t0:.1f} s")
+    sel = torch.from_numpy(synth.selection_stream(w, 0, steps=steps)).cuda()
+    ad = hsk.gqa_desc(requests=w.requests, heads=w.heads, kv_heads=w.kv_heads, dh=w.dk, top_k=k,
+                      page_tokens=w.page_tokens, scale=w.scale)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = [torch.from_numpy(synth.queries(w, l, 0).view(np.int16)).cuda() for l in range(L)]
+    out = torch.empty((w.requests, w.heads, w.dk), dtype=torch.int16, device="cuda")
+    locs = torch.empty((U, 1, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(U)
+    pools = [st.pool_base(l) for l in range(L)]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def step(t, overlap: bool, evs=None):
+        st.resolve_step(0, t + 1, sel[t], locs, stats)
+        if evs is not None:
+            evs["res"][1].record(main)
+        done = []
+        if overlap:
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side.wait_event(ev)
+            for l in range(1, L):
+                st.replay_plan(0, l, stream=side)
+                e = torch.cuda.Event()
+                e.record(side)
+                done.append(e)
+        for l in range(L):
+            if l and overlap:
+                main.wait_event(done[l - 1])
+            elif l:
+                st.replay_plan(0, l, stream=main)
+            if evs is not None:
+                evs["att"][l][0].record(main)
+            hsk.sparse_decode_attn(ad, q[l], pools[l], locs, None, out, scratch, nb)
+            if evs is not None:
+                evs["att"][l][1].record(main)
+
+    res = {}
+    for mode, overlap in (("sequential", False), ("side_stream", True)):
+        tt, att = 0.0, []
+        for t in range(steps):
+            evs = {"res": [_ev(), _ev()], "att": [[_ev(), _ev()] for _ in range(L)]}
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            evs["res"][0].record(main)
+            step(t, overlap, evs)
+            torch.cuda.synchronize()
+            if t > 0:
+                tt += time.perf_counter() - t0
+                att += [a.elapsed_time(b) for a, b in evs["att"]]
+        res[mode] = {"ms_per_step": tt * 1e3 / (steps - 1), "gqa_attention_ms": float(np.mean(att))}
+        if mode == "sequential":
+            st.close()
+            st = hsk.KVStore(requests=U, sources=L, row_bytes=w.row_bytes, hot_slots=w.hot_slots, tail_rows=0,
+                             ctx=w.ctx, max_queries=1, top_k=k, host_alias=True)
+            for u in range(U):
+                synth.fill_kv_rows(st.host_ptr(0, u), w, 0, u, 0, w.ctx)
+            pools = [st.pool_base(l) for l in range(L)]
+    misses = int(hsk.stats_to_numpy(stats)["n_miss"].sum())
+    status = st.sync_status()
+    st.close()
+    att = res["side_stream"]["gqa_attention_ms"]
+    nbytes = U * k * w.row_bytes + w.requests * w.heads * w.dk * 2 * 2 + U * k * 4
+    return {"workload": f"quest: {w.requests} requests x {w.kv_heads} KV heads, {L} layers, {w.ctx} pages of "
+                        f"{w.page_tokens} tokens, top-{k} pages shared by all layers, {w.hot_slots} page slots",
+            "note": "layers 1..7 read layer 0's host payload (one 17 GB host copy instead of 137 GB); the bytes "
+                    "moved per layer are the same", "modes": res,
+            "overlap_gain": res["sequential"]["ms_per_step"] / res["side_stream"]["ms_per_step"],
+            "gqa_algorithmic_bytes_per_layer": nbytes, "gqa_achieved_GBps": nbytes / (att * 1e-3) / 1e9,
+            "gqa_frac_hbm": nbytes / (att * 1e-3) / 1e9 / HBM_PEAK_GBS, "last_step_misses": misses,
+            "status": status}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,7 +431,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the hits-only, misses-only and memcpy runs")
-    ap.add_argument("--workload", default="dsa100k")
+    ap.add_argument("--workload", default="dsa100k", choices=["dsa100k", "verify", "adaptive", "quest"])
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -221,9 +460,15 @@ def main() -> int:
     import synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.workload != "dsa100k":
+        torch.cuda.set_device(0)
+        fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest}[args.workload]
+        steps = args.steps if args.steps != 32 else w.steps
+        print(json.dumps(fn(hsk, synth, w, steps)), flush=True)
+        return 0
     assert w.kind == "mla" and w.queries == 1, "the benchmark line is the single-query MLA decode"
     K, W = args.steps, args.warmup
-    total_steps = K + W
+    total_steps = W + K + min(K, 16)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_setup = time.perf_counter()
@@ -267,18 +512,24 @@ def main() -> int:
     if store.sync_status() != 0:
         log("[bench] device-side error during warmup")
         return 1
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.layers)] for _ in range(K)]
     misses = []
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        run_step(W + i, events[i])
+        run_step(W + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # per-call durations on the launch stream, from HIP events, over K more steps (events between the calls
+    # would add small gaps to the throughput pass above)
+    KE = min(K, 16)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(w.layers)] for _ in range(KE)]
+    for i in range(KE):
+        run_step(W + K + i, events[i])
+    torch.cuda.synchronize()
     status = store.sync_status()
     res_ms, att_ms = [], []
-    for i in range(K):
+    for i in range(KE):
         for l in range(w.layers):
             a, b, c = events[i][l]
             res_ms.append(a.elapsed_time(b))
