@@ -412,7 +412,7 @@ def run_quest(hsk, synth, w, steps: int) -> dict:
     misses = int(hsk.stats_to_numpy(stats)["n_miss"].sum())
     status = st.sync_status()
     st.close()
-    att = res["side_stream"]["gqa_attention_ms"]
+    att = res["sequential"]["gqa_attention_ms"]  # on one stream the events bracket the kernels alone
     nbytes = U * k * w.row_bytes + w.requests * w.heads * w.dk * 2 * 2 + U * k * 4
     return {"workload": f"quest: {w.requests} requests x {w.kv_heads} KV heads, {L} layers, {w.ctx} pages of "
                         f"{w.page_tokens} tokens, top-{k} pages shared by all layers, {w.hot_slots} page slots",

@@ -384,50 +384,137 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------------
-// GQA pages: grid (split, R * Hkv), 64 x (H / Hkv) threads: one wave per query head, each lane owns two of
-// the 128 head dims; scores are wave reductions, values accumulate per lane.
+// GQA pages (Quest-style page selection): 4 FLOP per byte, so this kernel is built for HBM bandwidth, not for
+// the matrix cores.  Grid (split, request x KV head), 4 waves.  Tiles of 64 tokens (4 pages of 16) are
+// gathered by page location into LDS with LDS-DMA loads, double-buffered; every wave takes one query head
+// of the group:
+//   scores:  lane t owns token t and takes the dot product of its key with the head's query held in
+//            registers (v_dot2_f32_bf16 on bf16 pairs); the 16 key chunks of a token are XOR-swizzled by
+//            the token so that 16 lanes reading chunk i hit 16 different bank groups;
+//   softmax: online, fp32, exp2 domain, reference maximum moved only when exceeded by 2^8;
+//   P.V:     lane l owns value dims 2l, 2l+1 and walks the 64 tokens, each weight broadcast from its lane.
 // ------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void gqa_attn_kernel(AttnArgs a) {
+constexpr int kGqaTok = 64;                    // tokens per tile
+constexpr int kGqaTokBytes = 512;              // one token: K 128 bf16 | V 128 bf16
+constexpr int kGqaTileBytes = kGqaTok * kGqaTokBytes;  // 32 KB
+constexpr int kGqaDma = kGqaTileBytes / 1024;  // 32 wave-wide loads per tile
+
+struct GqaArgs {
+  const uint16_t* q;
+  const char* pool;
+  const int32_t* locs;
+  uint16_t* out;
+  float* po;
+  float* pm;
+  float* pl;
+  int32_t H, Hkv, k, page_tokens, row_bytes, split, pages_per_split;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
+  __shared__ __attribute__((aligned(1024))) char s_tile[2][kGqaTileBytes];
   const int sp = blockIdx.x, unit = blockIdx.y;
-  const int r = unit / a.Hkv, g = unit % a.Hkv;
-  const int gsize = a.H / a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = g * gsize + wave;
-  const int dh = a.dk;            // 128: two dims per lane
-  const int i0 = sp * a.rows_per_split;
-  const int i1 = min(a.k, i0 + a.rows_per_split);
-  const uint16_t* qh = a.q + ((int64_t)r * a.H + h) * dh;
-  const uint32_t qw = *(const uint32_t*)(qh + 2 * lane);
-  const float q0 = bf16lo(qw), q1 = bf16hi(qw);
-  const int32_t* locs = a.locs + (int64_t)unit * a.k;
-  const int row_bytes = a.row_elems * 2;
-  const int tok_bytes = 4 * dh;
-  float m_run = -INFINITY, l_run = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int i = i0; i < i1; ++i) {
-    const char* page = a.pool + (int64_t)locs[i] * row_bytes;
-    for (int t = 0; t < a.page_tokens; ++t) {
-      const char* tok = page + (int64_t)t * tok_bytes;
-      const uint32_t kw = *(const uint32_t*)(tok + 4 * lane);
-      const uint32_t vw = *(const uint32_t*)(tok + 2 * dh + 4 * lane);
-      float s = q0 * bf16lo(kw) + q1 * bf16hi(kw);
+  const int r = unit / a.Hkv, grp = unit % a.Hkv;
+  const int hg = a.H / a.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pt = a.page_tokens;
+  const int p0 = sp * a.pages_per_split;
+  const int npages = max(0, min(a.k, p0 + a.pages_per_split) - p0);
+  const int ntok = npages * pt;
+  const int ntiles = (ntok + kGqaTok - 1) / kGqaTok;
+  const int32_t* locs = a.locs + (int64_t)unit * a.k + p0;
+  const bool active = wave < hg;
+  const int head = grp * hg + (active ? wave : 0);
+
+  // query of this wave's head: 64 bf16 pairs, the same in every lane
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 qv[64];
+  {
+    const uint32_t* qh = (const uint32_t*)(a.q + ((int64_t)r * a.H + head) * 128);
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-      s *= a.scale;
-      const float m_new = fmaxf(m_run, s);
-      const float alpha = __expf(m_run - m_new);
-      const float p = __expf(s - m_new);
-      l_run = l_run * alpha + p;
-      o0 = o0 * alpha + p * bf16lo(vw);
-      o1 = o1 * alpha + p * bf16hi(vw);
-      m_run = m_new;
+    for (int i = 0; i < 64; ++i) qv[i] = __builtin_bit_cast(bf16x2, qh[i]);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
+  // DMA: wave-wide load j covers tile tokens 2j, 2j+1; lane l copies 16-byte slot l & 31 of token 2j + l / 32:
+  // slots 0..15 are the key chunks, stored at position chunk ^ (token & 15), slots 16..31 the value chunks
+  auto issue = [&](int T, int b) {
+#pragma unroll
+    for (int u = 0; u < kGqaDma / 4; ++u) {
+      const int j = wave + 4 * u;
+      const int t = 2 * j + (lane >> 5);
+      const int pos = lane & 31;
+      int tok = T * kGqaTok + t;
+      tok = tok < ntok ? tok : 0;  // past the end: re-read token 0 (masked)
+      const int chunk_off = pos < 16 ? ((pos ^ (t & 15)) << 4) : 256 + ((pos - 16) << 4);
+      const char* src = a.pool + (int64_t)locs[tok / pt] * a.row_bytes + (tok % pt) * kGqaTokBytes + chunk_off;
+      const uint32_t m0 = lds0 + b * kGqaTileBytes + j * 1024;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+    }
+  };
+
+  float m_run = -INFINITY, l_lane = 0.f, o0 = 0.f, o1 = 0.f;
+  if (ntiles > 0) issue(0, 0);
+  for (int T = 0; T < ntiles; ++T) {
+    const int b = T & 1;
+    // tile T landed (this wave's loads, then every wave's) and every wave is done with tile T - 1, whose
+    // buffer then takes tile T + 1 while tile T is computed
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (T + 1 < ntiles) issue(T + 1, b ^ 1);
+    const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[b][0];
+    if (active) {
+      // scores: lane = token
+      const HSK_LDS char* kt = tile + lane * kGqaTokBytes;
+      const int x = lane & 15;
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const HSK_LDS uint32_t* w = (const HSK_LDS uint32_t*)(kt + ((i ^ x) << 4));
+        const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), qv[4 * i + 0], acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), qv[4 * i + 1], acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), qv[4 * i + 2], acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), qv[4 * i + 3], acc, false);
+      }
+      const float sc = T * kGqaTok + lane < ntok ? acc * a.scale_log2 : -INFINITY;
+      float tmax = sc;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+      if (tmax > m_run + 8.f) {  // wave-uniform: the reference maximum moves (always on the first tile)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
+        l_lane *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
+        m_run = tmax;
+      }
+      const float p = __builtin_amdgcn_exp2f(sc - m_run);
+      l_lane += p;
+      // P.V: lane = value dims 2 lane, 2 lane + 1
+      const HSK_LDS char* vt = tile + 256 + 4 * lane;
+#pragma unroll
+      for (int t = 0; t < kGqaTok; ++t) {
+        const float pt_ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t));
+        const uint32_t vw = *(const HSK_LDS uint32_t*)(vt + t * kGqaTokBytes);
+        o0 = fmaf(pt_, bf16lo(vw), o0);
+        o1 = fmaf(pt_, bf16hi(vw), o1);
+      }
     }
   }
-  const int64_t ps = ((int64_t)r * a.split + sp) * a.H + h;  // GQA: RQ index = request
-  a.po[ps * dh + 2 * lane] = o0;
-  a.po[ps * dh + 2 * lane + 1] = o1;
+  if (!active) return;
+  float l = l_lane;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  if (a.split == 1) {
+    const float inv = 1.f / l;
+    const uint32_t w = (uint32_t)f2bf16(o0 * inv) | ((uint32_t)f2bf16(o1 * inv) << 16);
+    *(uint32_t*)(a.out + ((int64_t)r * a.H + head) * 128 + 2 * lane) = w;
+    return;
+  }
+  const int64_t ps = ((int64_t)r * a.split + sp) * a.H + head;
+  *(float2*)(a.po + ps * 128 + 2 * lane) = make_float2(o0, o1);
   if (lane == 0) {
-    a.pm[ps] = m_run;
-    a.pl[ps] = l_run;
+    a.pm[ps] = m_run * kLn2;  // natural-log units, as the combine expects
+    a.pl[ps] = l;
   }
 }
 
@@ -544,8 +631,9 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
     if (d->split > 0) {
       p->split = d->split;
     } else {
+      // about four workgroups per CU (a workgroup holds 64 KB of LDS)
       const int64_t base = (int64_t)d->num_requests * d->kv_heads;
-      int64_t s = (2048 + base - 1) / base;
+      int64_t s = (1024 + base - 1) / base;
       s = s < 1 ? 1 : s;
       p->split = (int)(s > k ? k : s);
     }
@@ -554,7 +642,7 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
     return false;
   }
   const int64_t parts = RQ * p->split * d->heads;
-  const bool partials = !(d->kind == HSK_ATTN_MLA && p->split == 1);
+  const bool partials = p->split > 1;
   p->po_bytes = partials ? (parts * d->dv * 4 + 255) / 256 * 256 : 0;
   p->pm_bytes = partials ? (parts * 4 + 255) / 256 * 256 : 0;
   p->scratch = p->po_bytes + 2 * p->pm_bytes;
@@ -616,9 +704,14 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
     HSK_HIP(hipGetLastError());
     if (p.split == 1) return HSK_OK;
   } else {
-    hipLaunchKernelGGL(gqa_attn_kernel, dim3(a.split, (int64_t)d->num_requests * d->kv_heads),
-                       dim3(64 * (d->heads / d->kv_heads)), 0, s, a);
+    GqaArgs gq;
+    gq.q = a.q; gq.pool = a.pool; gq.locs = a.locs; gq.out = a.out; gq.po = a.po; gq.pm = a.pm; gq.pl = a.pl;
+    gq.H = d->heads; gq.Hkv = d->kv_heads; gq.k = d->top_k; gq.page_tokens = d->page_tokens;
+    gq.row_bytes = d->row_elems * 2; gq.split = p.split; gq.pages_per_split = p.rows_per_split;
+    gq.scale_log2 = d->scale * kLog2e;
+    hipLaunchKernelGGL(gqa_attn_kernel, dim3(p.split, (int64_t)d->num_requests * d->kv_heads), dim3(256), 0, s, gq);
     HSK_HIP(hipGetLastError());
+    if (p.split == 1) return HSK_OK;
   }
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((RQ * d->heads + 3) / 4)), dim3(256), 0, s, a, d->dv);
   HSK_HIP(hipGetLastError());

@@ -272,7 +272,7 @@ hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t defi
 
 static int32_t gather_blocks_for(const hsk_store* st) {
   if (st->d.gather_blocks > 0) return st->d.gather_blocks;
-  return 1024;  // 4,096 waves: rows are spread evenly over them whatever the batch
+  return 384;  // 1,536 waves: rows are spread evenly over them whatever the batch (PCIe rate plateaus from ~256)
 }
 
 hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, const int32_t* d_nq,

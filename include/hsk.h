@@ -88,7 +88,7 @@ typedef struct hsk_desc {
   int64_t max_ctx;             /* rows of host history reserved per request and source */
   const int64_t* ctx_len;      /* host array [R]: n_r, 1 <= n_r <= max_ctx, n_r < 2^31 */
   int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
-  int32_t gather_blocks;       /* workgroups (of 4 waves) of the gather kernel; 0 = automatic (1,024) */
+  int32_t gather_blocks;       /* workgroups (of 4 waves) of the gather kernel; 0 = automatic (384) */
 } hsk_desc;
 
 /* Per-request result of one resolve call (device memory, written by hsk_resolve_step). */

@@ -103,3 +103,41 @@ def test_mla_rejects_unsupported_shapes():
         args.update(kw)
         with pytest.raises(hsk.HskError):
             hsk.attn_scratch_bytes(hsk.mla_desc(**args))
+
+
+def _run_gqa(R, H, Hkv, k, n_pages, page_tokens=16, split=0, seed=0, q_scale=1.0):
+    rng = np.random.default_rng(seed)
+    row_elems = page_tokens * 2 * 128
+    pages = _bf16(rng.standard_normal((n_pages, row_elems)))
+    q = _bf16(q_scale * rng.standard_normal((R, H, 128)))
+    locs = rng.integers(0, n_pages, size=(R * Hkv, 1, k)).astype(np.int32)
+    ad = hsk.gqa_desc(requests=R, heads=H, kv_heads=Hkv, dh=128, top_k=k, page_tokens=page_tokens,
+                      scale=128 ** -0.5, split=split)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    pool = torch.from_numpy(pages.view(np.int16)).cuda()
+    out = torch.full((R, H, 128), 77, dtype=torch.int16, device="cuda")
+    print(f"[gqa] R={R} H={H} Hkv={Hkv} k={k} pages={n_pages} page_tokens={page_tokens} split={split}", flush=True)
+    hsk.sparse_decode_attn(ad, torch.from_numpy(q.view(np.int16)).cuda(), pool.data_ptr(),
+                           torch.from_numpy(locs).cuda(), None, out, scratch, nb)
+    torch.cuda.synchronize()
+    got = synth.bf16_to_f32(out.cpu().numpy().view(np.uint16)).astype(np.float64)
+    gs = H // Hkv
+    for u in range(R * Hkv):
+        r, g = divmod(u, Hkv)
+        ref = oracle.gqa_attention(q[r, g * gs:(g + 1) * gs], pages[locs[u, 0]], page_tokens, 128, 128 ** -0.5)
+        err = np.abs(got[r, g * gs:(g + 1) * gs] - ref)
+        assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"unit {u}: max abs err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("k,split", [(1, 0), (7, 1), (7, 3), (256, 0), (256, 1), (100, 6)])
+def test_gqa_pages_split_and_ragged(k, split):
+    """GQA page attention: one page, ragged last tiles (k*16 not a multiple of 64 tokens), forced and
+    automatic splits, partitions holding no page."""
+    _run_gqa(R=3, H=32, Hkv=8, k=k, n_pages=600, split=split, seed=k * 10 + split)
+
+
+@pytest.mark.parametrize("H,Hkv,pt", [(8, 8, 16), (16, 8, 16), (32, 8, 8), (32, 8, 32)])
+def test_gqa_group_sizes_and_page_sizes(H, Hkv, pt):
+    """1, 2 and 4 query heads per KV head; pages of 8 and 32 tokens; a large score range."""
+    _run_gqa(R=2, H=H, Hkv=Hkv, k=40, n_pages=300, page_tokens=pt, seed=H + pt, q_scale=3.0)
