@@ -544,8 +544,8 @@ def main() -> int:
     res_avg = float(np.mean(res_ms))
     attn_bytes = attn_algorithmic_bytes(w)
     achieved = attn_bytes / (att_avg * 1e-3) / 1e9
-    traffic = counter_traffic("mla_attention", os.path.join(ROOT, "hierarchical_sparse_kv_layer_amd", "csrc",
-                                                            "attention.hip"))
+    traffic = counter_traffic("mla_attention_call", os.path.join(ROOT, "hierarchical_sparse_kv_layer_amd", "csrc",
+                                                                 "attention.hip"))
     result = {
         "metric": "selected KV rows resolved+attended/s; decode steps/s at 100K ctx, batch 64",
         "value": value, "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms_per_step,
@@ -556,7 +556,7 @@ def main() -> int:
                                f"{w.heads} heads, dk {w.dk}, dv {w.dv}, 80% kept + Zipf(1.1)",
                    "global_batch": w.requests, "seq_len": w.ctx, "parallelism": "none (1 GPU)"},
         "steps_per_s": K / elapsed,
-        "roofline": {"bound": "hbm", "kernel": "sparse_decode_attn (mla_attn_kernel + combine_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "hsk_sparse_decode_attn call (mla_mfma_kernel + combine_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,
                      "avg_launch_ms": att_avg},
