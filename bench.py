@@ -434,6 +434,9 @@ def main() -> int:
     ap.add_argument("--workload", default="dsa100k", choices=["dsa100k", "verify", "adaptive", "quest"])
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
+    ap.add_argument("--path", default="separate", choices=["separate", "fused"],
+                    help="separate: hsk_resolve_step then hsk_sparse_decode_attn per layer; fused: "
+                         "hsk_resolve_attend per layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 4 device-to-device copies of 1 GiB (the known-size kernel that scales the "
                          "HBM byte counters of a profile)")
@@ -495,14 +498,22 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     log(f"[bench] inputs resident ({time.perf_counter() - t_setup:.1f} s); warmup {W} steps")
 
+    fused = args.path == "fused"
+
     def run_step(t, ev=None):
         for l in range(w.layers):
             if ev is not None:
                 ev[l][0].record(stream)
-            store.resolve_step(l, t + 1, d_sel[l][t], d_locs[l], d_stats[l])
-            if ev is not None:
-                ev[l][1].record(stream)
-            hsk.sparse_decode_attn(ad, d_q[l][t], pools[l], d_locs[l], None, out, scratch, nscratch)
+            if fused:
+                store.resolve_attend(l, t + 1, d_sel[l][t], d_locs[l], ad, d_q[l][t], out, scratch,
+                                     stats=d_stats[l])
+                if ev is not None:
+                    ev[l][1].record(stream)
+            else:
+                store.resolve_step(l, t + 1, d_sel[l][t], d_locs[l], d_stats[l])
+                if ev is not None:
+                    ev[l][1].record(stream)
+                hsk.sparse_decode_attn(ad, d_q[l][t], pools[l], d_locs[l], None, out, scratch, nscratch)
             if ev is not None:
                 ev[l][2].record(stream)
 
@@ -554,7 +565,8 @@ def main() -> int:
         "config": {"workload": f"{w.name}: {w.requests} requests x 1 query, {w.layers} layers with own payloads, "
                                f"context {w.ctx}, B={w.hot_slots}, tail {w.tail_rows}, top-k {w.top_k}, "
                                f"{w.heads} heads, dk {w.dk}, dv {w.dv}, 80% kept + Zipf(1.1)",
-                   "global_batch": w.requests, "seq_len": w.ctx, "parallelism": "none (1 GPU)"},
+                   "global_batch": w.requests, "seq_len": w.ctx, "parallelism": "none (1 GPU)",
+                   "path": args.path},
         "steps_per_s": K / elapsed,
         "roofline": {"bound": "hbm", "kernel": "hsk_sparse_decode_attn call (mla_mfma_kernel + combine_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

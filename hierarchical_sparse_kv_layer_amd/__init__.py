@@ -65,6 +65,8 @@ _sig = {
     "hsk_pool_base": (_i32, [_vp, _i32, _P(_vp)]),
     "hsk_attn_scratch_bytes": (_i32, [_P(AttnDesc), _P(ctypes.c_size_t)]),
     "hsk_sparse_decode_attn": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "hsk_resolve_attend": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _P(AttnDesc), _vp, _vp, _vp, ctypes.c_size_t,
+                                  _vp]),
     "hsk_snapshot": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_read_plan": (_i32, [_vp, _i32, _i32, _vp, _vp, _i32, _P(_i32)]),
     "hsk_sync_status": (_i32, [_vp, _vp]),
@@ -176,6 +178,13 @@ def sparse_decode_attn(adesc: AttnDesc, q, pool, locs, nq, out, scratch, scratch
                                        _ptr(scratch), int(scratch_bytes), _stream(stream)), "hsk_sparse_decode_attn")
 
 
+def resolve_attend(store: int, source: int, epoch: int, sel, locs, stats, adesc: AttnDesc, q, out, scratch,
+                   scratch_bytes: int, stream=None) -> None:
+    _check(_lib.hsk_resolve_attend(store, source, int(epoch), _ptr(sel), _ptr(locs), _ptr(stats), ctypes.byref(adesc),
+                                   _ptr(q), _ptr(out), _ptr(scratch), int(scratch_bytes), _stream(stream)),
+           "hsk_resolve_attend")
+
+
 def snapshot(store: int, source: int, req: int, B: int, n_rows: int, page_rows: int) -> dict:
     key = np.zeros(B, np.int32)
     rec = np.zeros(B, np.uint32)
@@ -248,6 +257,11 @@ class KVStore:
 
     def resolve_step(self, source: int, epoch: int, sel, locs, stats=None, nq=None, stream=None):
         resolve_step(self.handle, source, epoch, sel, nq, locs, stats, stream)
+
+    def resolve_attend(self, source: int, epoch: int, sel, locs, adesc: AttnDesc, q, out, scratch, stats=None,
+                       stream=None):
+        resolve_attend(self.handle, source, epoch, sel, locs, stats, adesc, q, out, scratch,
+                       scratch.numel() * scratch.element_size(), stream)
 
     def replay_plan(self, plan_source: int, dst_source: int, stream=None):
         replay_plan(self.handle, plan_source, dst_source, stream)

@@ -80,6 +80,7 @@ constexpr int kTileBytes = kTile * kMlaDk * 2;   // 36,864
 constexpr int kDmaPerTile = kTileBytes / 1024;   // 36 wave-wide 16-byte loads
 constexpr int kBufs = 3;
 constexpr int kMaxSplitRows = 2048;
+constexpr int kMaxFusedRows = 1024;  // rows per partition of the fused kernel (two location arrays in LDS)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -92,6 +93,9 @@ struct MlaArgs {
   float* po;
   float* pm;
   float* pl;
+  const int32_t* fill;  // fused resolve + attend: per-selection host source (-1 resident, else 2 p + first)
+  const char* host;     // fused: device-visible pinned host rows of request 0 of the source
+  int64_t host_req_stride;
   int32_t Qmax, H, k, row_bytes, split, rows_per_split;
   float scale_log2;  // softmax scale * log2(e)
 };
@@ -132,7 +136,11 @@ __device__ __forceinline__ void wait_tile_barrier_n(int n) {
 // LDS writes of this wave complete, then a workgroup barrier (no wait on global loads)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int NHB, int NPAIR>
+// FUSED: rows fetched from host in this call are read straight from pinned host memory (PCIe, zero copy)
+// and the first occurrence of each is written from the LDS tile into its pool row; the kernel is then
+// bound by the host link, so it waits for each tile's loads one tile ahead only (stores share the in-order
+// memory counter with the loads, which rules out the deeper fixed-count waits).
+template <int NHB, int NPAIR, bool FUSED>
 __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   constexpr int NW = 2 * NPAIR;
   constexpr int NT = 64 * NW;
@@ -142,7 +150,8 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   constexpr int kGroup = 2048;          // half the bytes of one 8-chunk group of the 32 tile rows
   __shared__ __attribute__((aligned(1024))) char s_tile[kBufs][kTileBytes];
   __shared__ f32x4 s_x[NW][2 * NHB][64];
-  __shared__ int32_t s_loc[kMaxSplitRows];
+  __shared__ int32_t s_loc[FUSED ? kMaxFusedRows : kMaxSplitRows];
+  __shared__ int32_t s_fill[FUSED ? kMaxFusedRows : 1];
 
   const int sp = blockIdx.x, hgrp = blockIdx.y, rq = blockIdx.z;
   if (a.nq) {
@@ -160,7 +169,11 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   const int my_dma = (kDmaPerTile - wave + NW - 1) / NW;
 
   const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
-  for (int x = tid; x < nrows; x += NT) s_loc[x] = locs[x];
+  for (int x = tid; x < nrows; x += NT) {
+    s_loc[x] = locs[x];
+    if constexpr (FUSED) s_fill[x] = a.fill[(int64_t)rq * a.k + i0 + x];
+  }
+  const char* hostr = FUSED ? a.host + (int64_t)(rq / a.Qmax) * a.host_req_stride : nullptr;
 
   bf16x8 qf[NHB][KS];
   {
@@ -205,7 +218,13 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
     for (int v = 0; v < NTOK; ++v) {
       const int x = tb + tok[v] < nrows ? tb + tok[v] : 0;   // rows past the end re-read row 0 (masked)
-      rp[v] = a.pool + (int64_t)s_loc[x] * a.row_bytes + swz[v];
+      const int32_t loc = s_loc[x];
+      if (FUSED && s_fill[x] >= 0) {
+        rp[v] = hostr + (int64_t)(s_fill[x] >> 1) * a.row_bytes + swz[v];
+      } else {
+        // the locations of a request the resolve rejected are -1: the fused kernel reads row 0 for them
+        rp[v] = a.pool + (int64_t)(FUSED && loc < 0 ? 0 : loc) * a.row_bytes + swz[v];
+      }
     }
 #pragma unroll
     for (int u = 0; u < (kDmaPerTile + NW - 1) / NW; ++u) {
@@ -230,12 +249,34 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   for (int hb = 0; hb < NHB; ++hb) { m_run[hb] = -INFINITY; l_run[hb] = 0.f; }
 
   if (ntiles > 0) issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
+  if (!FUSED && ntiles > 1) issue(1, 1);
   for (int T = 0; T < ntiles; ++T) {
     const int b = T % kBufs;
-    if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
-    if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
+    if (FUSED) {
+      wait_tile_barrier<0>();
+      if (T + 1 < ntiles) issue(T + 1, (T + 1) % kBufs);
+    } else {
+      if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
+      if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
+    }
     const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[b][0];
+    const int rem = nrows - T * kTile;
+    if constexpr (FUSED) {
+      // the rows this call fetched for the first time go from the tile into their pool rows
+      uint32_t wb;
+      {
+        const int x = T * kTile + (lane & 31);
+        wb = (uint32_t)__ballot(hgrp == 0 && (lane & 31) < rem && (s_fill[x < nrows ? x : 0] & 1));
+      }
+      for (uint32_t mm = wb; mm; mm &= mm - 1) {
+        const int row = __builtin_ctz(mm);
+        if (tid < kMlaDk / 8) {
+          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+          const u32x4_t v = *(const HSK_LDS u32x4_t*)(tile + tile_off(row, tid));
+          *(u32x4_t*)(a.pool + (int64_t)s_loc[T * kTile + row] * a.row_bytes + tid * 16) = v;
+        }
+      }
+    }
 
     // partial scores over this wave's half of the key dims
     f32x4 sacc[2][NHB];
@@ -268,7 +309,6 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
       for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] += s_x[wave ^ 1][tb * NHB + hb][lane];
 
     // online softmax; lane holds head hbase + 16 hb + jl, rows 16 tb + 4 g + v
-    const int rem = nrows - T * kTile;
     bf16x8 pf[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -593,7 +633,8 @@ struct AttnPlan {
   int64_t po_bytes, pm_bytes, scratch;
 };
 
-static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
+// max_rows bounds the rows of one partition (the fused kernel keeps two location arrays in LDS).
+static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSplitRows) {
   if (!d || d->num_requests < 1 || d->max_queries < 1 || d->heads < 1 || d->top_k < 1 || d->split < 0) return false;
   const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
   const int k = d->top_k;
@@ -605,11 +646,11 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
     const int units = d->heads / (16 * p->nhb);
     p->npair = units % 4 == 0 ? 4 : units % 2 == 0 ? 2 : 1;
     p->hgroups = units / p->npair;
-    const int min_split = (k + kMaxSplitRows - 1) / kMaxSplitRows;
+    const int min_split = (k + max_rows - 1) / max_rows;
     if (d->split > 0) {
       p->split = d->split;
       p->rows_per_split = (k + p->split - 1) / p->split;
-      if (p->rows_per_split > kMaxSplitRows) return false;
+      if (p->rows_per_split > max_rows) return false;
     } else {
       // about one workgroup per compute unit (a workgroup fills a CU's LDS), tiles of whole 32-row blocks
       const int64_t base = RQ * p->hgroups;
@@ -619,7 +660,7 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
       s = s < min_split ? min_split : s;
       int rps = (int)((k + s - 1) / s);
       if (s > 1) rps = (rps + kTile - 1) / kTile * kTile;
-      if (rps > kMaxSplitRows) rps = kMaxSplitRows;
+      if (rps > max_rows) rps = max_rows;
       p->rows_per_split = rps;
       p->split = (k + rps - 1) / rps;
     }
@@ -650,9 +691,10 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p) {
   return true;
 }
 
-template <int NHB, int NPAIR>
+template <int NHB, int NPAIR, bool FUSED = false>
 static void launch_mla(const MlaArgs& m, const AttnPlan& p, int64_t RQ, hipStream_t s) {
-  hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR>), dim3(p.split, p.hgroups, RQ), dim3(128 * NPAIR), 0, s, m);
+  hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR, FUSED>), dim3(p.split, p.hgroups, RQ), dim3(128 * NPAIR), 0, s,
+                     m);
 }
 
 }  // namespace hsk
@@ -662,9 +704,12 @@ using namespace hsk;
 extern "C" {
 
 hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* d, size_t* bytes) {
-  AttnPlan p;
+  AttnPlan p, pf;
   if (!bytes || !plan_attn(d, &p)) return HSK_EINVAL;
   *bytes = (size_t)p.scratch;
+  // enough for the fused resolve + attend as well, whose partitions hold at most kMaxFusedRows rows
+  if (d->kind == HSK_ATTN_MLA && d->max_queries == 1 && plan_attn(d, &pf, kMaxFusedRows) && pf.scratch > p.scratch)
+    *bytes = (size_t)pf.scratch;
   return HSK_OK;
 }
 
@@ -697,6 +742,7 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
     m.Qmax = d->max_queries; m.H = d->heads; m.k = d->top_k; m.row_bytes = d->row_elems * 2;
     m.split = p.split; m.rows_per_split = p.rows_per_split;
     m.scale_log2 = d->scale * kLog2e;
+    m.fill = nullptr; m.host = nullptr; m.host_req_stride = 0;
     if (p.nhb == 2 && p.npair == 4) launch_mla<2, 4>(m, p, RQ, s);
     else if (p.nhb == 2 && p.npair == 2) launch_mla<2, 2>(m, p, RQ, s);
     else if (p.nhb == 2) launch_mla<2, 1>(m, p, RQ, s);
@@ -719,3 +765,49 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
 }
 
 }  // extern "C"
+
+namespace hsk {
+
+hsk_status check_mla_fused(const hsk_attn_desc* d, const void* scratch, size_t scratch_bytes) {
+  AttnPlan p;
+  if (!d || !scratch || !plan_attn(d, &p, kMaxFusedRows) || d->kind != HSK_ATTN_MLA || d->max_queries != 1)
+    return HSK_EINVAL;
+  if (scratch_bytes < (size_t)p.scratch || ((uintptr_t)scratch % 256)) return HSK_EINVAL;
+  return HSK_OK;
+}
+
+hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* pool, const int32_t* locs,
+                            const int32_t* fill, const char* host, int64_t host_req_stride, void* out,
+                            void* scratch, size_t scratch_bytes, hipStream_t s) {
+  AttnPlan p;
+  if (check_mla_fused(d, scratch, scratch_bytes) != HSK_OK || !q || !pool || !locs || !fill || !host || !out)
+    return HSK_EINVAL;
+  plan_attn(d, &p, kMaxFusedRows);
+  const int64_t RQ = d->num_requests;
+  MlaArgs m;
+  m.q = (const uint16_t*)q; m.pool = pool; m.locs = locs; m.nq = nullptr; m.out = (uint16_t*)out;
+  m.po = (float*)scratch;
+  m.pm = (float*)((char*)scratch + p.po_bytes);
+  m.pl = (float*)((char*)scratch + p.po_bytes + p.pm_bytes);
+  m.fill = fill; m.host = host; m.host_req_stride = host_req_stride;
+  m.Qmax = 1; m.H = d->heads; m.k = d->top_k; m.row_bytes = d->row_elems * 2;
+  m.split = p.split; m.rows_per_split = p.rows_per_split;
+  m.scale_log2 = d->scale * kLog2e;
+  if (p.nhb == 2 && p.npair == 4) launch_mla<2, 4, true>(m, p, RQ, s);
+  else if (p.nhb == 2 && p.npair == 2) launch_mla<2, 2, true>(m, p, RQ, s);
+  else if (p.nhb == 2) launch_mla<2, 1, true>(m, p, RQ, s);
+  else launch_mla<1, 1, true>(m, p, RQ, s);
+  HSK_HIP(hipGetLastError());
+  if (p.split == 1) return HSK_OK;
+  AttnArgs a;
+  a.q = m.q; a.pool = pool; a.locs = locs; a.nq = nullptr; a.out = m.out;
+  a.R = d->num_requests; a.Qmax = 1; a.H = d->heads; a.Hkv = 1;
+  a.dk = d->dk; a.dv = d->dv; a.k = d->top_k; a.row_elems = d->row_elems; a.page_tokens = 1;
+  a.split = p.split; a.rows_per_split = p.rows_per_split; a.scale = d->scale;
+  a.po = m.po; a.pm = m.pm; a.pl = m.pl;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((RQ * d->heads + 3) / 4)), dim3(256), 0, s, a, d->dv);
+  HSK_HIP(hipGetLastError());
+  return HSK_OK;
+}
+
+}  // namespace hsk

@@ -35,7 +35,7 @@ struct SourceMeta {
 
 // Byte offsets of every region of the workspace.
 struct WorkspaceLayout {
-  int64_t ctx, err, total;
+  int64_t ctx, err, fill, total;
   std::vector<int64_t> key, rec, order, pt, opt, plan_n, plan_pos, plan_dst;
 };
 
@@ -54,6 +54,7 @@ struct ResolveArgs {
   int64_t max_pages;
   int64_t opt_base;   // first optional row: R*B + R*T
   int64_t stg_base;   // first staging row: R*B + R*T + opt_pool_pages*page_rows
+  int32_t* fill;       // nullable: per-selection host source for a fused resolve + attend (see resolve.hip)
   int32_t plan_cap;
   int32_t R, B, T, P, S, Qmax, k, row_bytes;
   uint32_t epoch;
@@ -85,6 +86,13 @@ hipError_t launch_tail_copy(const char* host, int64_t host_req_stride, char* poo
 hipError_t launch_copy_runs(const char* host, char* pool, const CopyRun* runs, int32_t n, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
+// MLA attention that reads the rows this call fetches straight from pinned host memory (fill codes of the
+// resolve kernel) and writes each of them once into its pool row; defined in attention.hip.
+hsk_status check_mla_fused(const hsk_attn_desc* d, const void* scratch, size_t scratch_bytes);
+hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* pool, const int32_t* locs,
+                            const int32_t* fill, const char* host, int64_t host_req_stride, void* out,
+                            void* scratch, size_t scratch_bytes, hipStream_t s);
+
 }  // namespace hsk
 
 struct hsk_store {
@@ -99,6 +107,7 @@ struct hsk_store {
   char* pool = nullptr;
   int64_t* d_ctx = nullptr;
   int32_t* d_err = nullptr;
+  int32_t* d_fill = nullptr;                // [R][Qmax][k] per-selection host source of a fused call
   std::vector<hsk::SourceMeta> meta;
   std::vector<char*> host;                  // pinned host rows per host source
   std::vector<uint32_t> last_epoch;         // per source

@@ -85,6 +85,10 @@ __device__ __forceinline__ int classify(const ResolveArgs& a, int r, int64_t n, 
   return kDirectNone;
 }
 
+// Fused resolve + attend: when a.fill is set, fill[f] tells the attention kernel where selection f's row
+// comes from in this call: -1 if it is resident (pool row locs[f]), else 2 p + first for a row copied from
+// host position p in this call, first = 1 on the first occurrence (the one that writes it into locs[f]);
+// positions stay below 2^30 on this path.
 // Per-selection codes while a call runs (kept in registers when the request has at most kPer * threads
 // selections, else in the location array, which then doubles as scratch):
 //   >= 0              final location (a direct row or a hot hit)
@@ -169,8 +173,12 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       bad |= (pv[e] < 0) || ((int64_t)pv[e] >= n);
     }
   }
+  int32_t* fill = a.fill ? a.fill + (int64_t)r * total : nullptr;
   if (__syncthreads_or(bad)) {
-    for (int f = tid; f < total; f += NT) locs[f] = -1;
+    for (int f = tid; f < total; f += NT) {
+      locs[f] = -1;
+      if (fill) fill[f] = -1;
+    }
     if (tid == 0) {
       a.m.plan_n[r] = 0;
       if (a.stats) {
@@ -270,6 +278,12 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
         nfirst += first[e];
       }
     }
+    if (fill) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (fb + e < nsel)
+          fill[fb + e] = (code[e] == kCodeMiss || is_claim(code[e])) ? 2 * pv[e] + (first[e] ? 1 : 0) : -1;
+    }
     int cnt;
     int idx = m + block_sum_scan(nfirst, &cnt, s_wsum);
 #pragma unroll
@@ -324,7 +338,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   const int over = m - v;
   if (over > a.S) {
     for (int i = tid; i < m; i += NT) pt[ppos[i]] = -1;  // drop the claims
-    for (int f = tid; f < total; f += NT) locs[f] = -1;
+    for (int f = tid; f < total; f += NT) {
+      locs[f] = -1;
+      if (fill) fill[f] = -1;
+    }
     if (tid == 0) {
       a.m.plan_n[r] = 0;
       if (a.stats) {
@@ -397,7 +414,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       locs[f] = loc;
     }
   }
-  for (int f = nsel + tid; f < total; f += NT) locs[f] = -1;
+  for (int f = nsel + tid; f < total; f += NT) {
+    locs[f] = -1;
+    if (fill) fill[f] = -1;
+  }
 
   // ---- phase 5: metadata update -- fills (2e) then hits (2e+1) at the most recent end ------------------
   const uint32_t e2 = 2u * a.epoch;

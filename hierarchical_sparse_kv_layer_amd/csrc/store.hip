@@ -1,7 +1,8 @@
 // Host runtime of libhsk.so: store lifetime, workspace layout, residency, resolve/attention entry points.
 //
 // Data layout in HBM (caller-owned):
-//   workspace: per request context lengths, a sticky error word, then per source
+//   workspace: per request context lengths, a sticky error word, the per-selection host sources of a fused
+//              resolve + attend [R][Qmax][k] i32, then per source
 //              key[R][B] i32, rec[R][B] u32, order[R][B] u16, pt[R][max_ctx] i32, opt[R][max_pages] i32,
 //              plan_n[R] i32, plan_pos[R][Qmax*k] i32, plan_dst[R][Qmax*k] i32 (each region 256-B aligned)
 //   pool:      per source rows_per_source rows of row_bytes: [R*B hot | R*T tail | optional pages | R*S staging]
@@ -46,6 +47,8 @@ bool layout_workspace(const hsk_desc& d, WorkspaceLayout* L) {
   int64_t off = 0;
   L->ctx = off; off = align_up(off + 8 * R);
   L->err = off; off = align_up(off + 4);
+  // fill codes of the fused resolve + attend, which serves stores with one query per request
+  L->fill = off; off = align_up(off + (d.max_queries == 1 ? 4 * R * cap : 0));
   L->key.clear(); L->rec.clear(); L->order.clear(); L->pt.clear(); L->opt.clear();
   L->plan_n.clear(); L->plan_pos.clear(); L->plan_dst.clear();
   for (int32_t s = 0; s < d.num_sources; ++s) {
@@ -124,6 +127,7 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   layout_workspace(*desc, &L);
   st->d_ctx = (int64_t*)(st->ws + L.ctx);
   st->d_err = (int32_t*)(st->ws + L.err);
+  st->d_fill = (int32_t*)(st->ws + L.fill);
   for (int32_t k = 0; k < desc->num_sources; ++k) {
     SourceMeta m;
     m.key = (int32_t*)(st->ws + L.key[k]);
@@ -275,14 +279,11 @@ static int32_t gather_blocks_for(const hsk_store* st) {
   return 384;  // 1,536 waves: rows are spread evenly over them whatever the batch (PCIe rate plateaus from ~256)
 }
 
-hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, const int32_t* d_nq,
-                            int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream) {
-  if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs) return HSK_EINVAL;
-  if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
-  hipStream_t s = (hipStream_t)stream;
+static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel,
+                                const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats) {
   ResolveArgs a;
   a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats; a.ctx = st->d_ctx; a.m = st->meta[source];
-  a.err = st->d_err; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
+  a.err = st->d_err; a.fill = nullptr; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
   const int64_t R = st->d.num_requests;
   a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
   a.stg_base = a.opt_base + st->d.opt_pool_pages * st->d.page_rows;
@@ -290,6 +291,15 @@ hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const
   a.R = st->d.num_requests; a.B = st->d.hot_slots; a.T = st->d.tail_rows; a.P = st->d.page_rows;
   a.S = st->d.staging_rows; a.Qmax = st->d.max_queries; a.k = st->d.top_k; a.row_bytes = st->d.row_bytes;
   a.epoch = epoch;
+  return a;
+}
+
+hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, const int32_t* d_nq,
+                            int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs) return HSK_EINVAL;
+  if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
+  hipStream_t s = (hipStream_t)stream;
+  const ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
   HSK_HIP(launch_resolve(a, s));
   st->last_epoch[source] = epoch;
   if (st->d.gather_mode == HSK_GATHER_ZEROCOPY) {
@@ -304,6 +314,33 @@ hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const
     HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
   }
   return HSK_OK;
+}
+
+hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, int32_t* d_locs,
+                              hsk_stats* d_stats, const hsk_attn_desc* desc, const void* d_q, void* d_out,
+                              void* d_scratch, size_t scratch_bytes, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs || !desc || !d_q || !d_out ||
+      !d_scratch)
+    return HSK_EINVAL;
+  // one query per request, host rows copied on the device, positions that fit the fill codes, and an
+  // attention shape that reads this store's rows, whole (the kernel writes back the dk columns it loads)
+  if (st->d.gather_mode != HSK_GATHER_ZEROCOPY || st->d.max_queries != 1 || st->d.max_ctx >= (1 << 30) ||
+      desc->kind != HSK_ATTN_MLA || desc->num_requests != st->d.num_requests || desc->max_queries != 1 ||
+      desc->top_k != st->d.top_k || (int64_t)desc->row_elems * 2 != st->d.row_bytes || desc->row_elems != desc->dk)
+    return HSK_EINVAL;
+  if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
+  hipStream_t s = (hipStream_t)stream;
+  ResolveArgs a = resolve_args(st, source, epoch, d_sel, nullptr, d_locs, d_stats);
+  a.fill = st->d_fill;
+  void* pool;
+  hsk_pool_base(st, source, &pool);
+  const int32_t hs = st->d.host_alias_sources ? 0 : source;
+  // the attention shape is checked before anything is queued, so a rejected call leaves the store as it was
+  if (check_mla_fused(desc, d_scratch, scratch_bytes) != HSK_OK) return HSK_EINVAL;
+  HSK_HIP(launch_resolve(a, s));
+  st->last_epoch[source] = epoch;
+  return launch_mla_fused(desc, d_q, (const char*)pool, d_locs, st->d_fill, st->host[hs],
+                          st->d.max_ctx * (int64_t)st->d.row_bytes, d_out, d_scratch, scratch_bytes, s);
 }
 
 hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {

@@ -187,7 +187,8 @@ typedef struct hsk_attn_desc {
   float scale;           /* softmax scale, e.g. 1/sqrt(dk) */
 } hsk_attn_desc;
 
-/* Device scratch (bytes) that hsk_sparse_decode_attn needs for split-k partial results. */
+/* Device scratch (bytes) that hsk_sparse_decode_attn and hsk_resolve_attend need for split-k partial
+ * results. */
 hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* desc, size_t* scratch_bytes);
 
 /*
@@ -203,6 +204,27 @@ hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* desc, size_t* scratch_byt
 hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* desc, const void* d_q, const void* d_pool,
                                   const int32_t* d_locs, const int32_t* d_nq, void* d_out, void* d_scratch,
                                   size_t scratch_bytes, hsk_stream_t stream);
+
+/*
+ * Resolve (HiSparse section 3.4) and MLA sparse decode attention (Adaptive DHiSparse Eq. 1) in one call,
+ * for stores with max_queries = 1 in HSK_GATHER_ZEROCOPY mode.  The attention kernel reads the rows this
+ * call fetches straight from the pinned host rows and writes each of them once into its pool row, so the
+ * host reads overlap the attention over resident rows instead of preceding it (the overlap of IO with
+ * computation of HiSparse section 3.5, within one layer).  Locations, statistics, pool contents and the
+ * miss plan are those of hsk_resolve_step; d_out is that of hsk_sparse_decode_attn at the same locations
+ * (bit-identical when both plan the same partitions, which they do whenever hsk_sparse_decode_attn's
+ * partitions hold at most 1,024 rows).
+ *   d_sel, d_locs, d_stats: as hsk_resolve_step with Qmax = 1 (no query counts).
+ *   desc: an HSK_ATTN_MLA descriptor with num_requests, top_k and row_elems * 2 equal to the store's
+ *         requests, top_k and row_bytes, row_elems = dk, max_queries = 1; its partitions hold at most
+ *         1,024 rows.
+ *   d_q, d_out, d_scratch, scratch_bytes: as hsk_sparse_decode_attn (hsk_attn_scratch_bytes covers both).
+ * EINVAL (nothing queued) for another store or descriptor shape, or max_ctx >= 2^30; EEPOCH as
+ * hsk_resolve_step.  Outputs of a request that the resolve rejects (status in its stats) are NaN.
+ */
+hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
+                              int32_t* d_locs, hsk_stats* d_stats, const hsk_attn_desc* desc, const void* d_q,
+                              void* d_out, void* d_scratch, size_t scratch_bytes, hsk_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------------------- */
 /* Inspection (tests) and lifetime                                                                     */

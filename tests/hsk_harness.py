@@ -111,7 +111,8 @@ class Harness:
         return q, dropped
 
     # ------------------------------------------------------------------------------------------------
-    def resolve(self, layer: int, step: int, check: bool = True, meta_reqs=None):
+    def resolve(self, layer: int, step: int, check: bool = True, meta_reqs=None, fused: bool = False):
+        """One resolve call (fused: hsk_resolve_attend, whose attention output is kept as res["out"])."""
         w = self.w
         src = self.source_of(layer)
         e = self.epoch_of(layer, step)
@@ -119,11 +120,17 @@ class Harness:
         d_sel = torch.from_numpy(sel).cuda()
         d_locs = torch.full_like(d_sel, -7)
         d_stats = hsk.stats_tensor(self.U)
-        self.store.resolve_step(src, e, d_sel, d_locs, d_stats)
+        out = None
+        if fused:
+            q, ad, out, scratch = self._attn_inputs(layer, step)
+            self.store.resolve_attend(src, e, d_sel, d_locs, ad, q, out, scratch, stats=d_stats)
+        else:
+            self.store.resolve_step(src, e, d_sel, d_locs, d_stats)
         locs = d_locs.cpu().numpy()
         stats = hsk.stats_to_numpy(d_stats)
         st = self.store.sync_status()
-        res = {"sel": sel, "d_sel": d_sel, "d_locs": d_locs, "locs": locs, "stats": stats, "src": src, "status": st}
+        res = {"sel": sel, "d_sel": d_sel, "d_locs": d_locs, "locs": locs, "stats": stats, "src": src, "status": st,
+               "out": out}
         self.host_fetch.append((step, layer, int(stats["n_miss"].sum()), int(stats["n_sel"].sum())))
         if not check:
             return res
@@ -166,11 +173,8 @@ class Harness:
             assert np.array_equal(got, want), f"pool bytes differ from host rows for request {r}"
 
     # ------------------------------------------------------------------------------------------------
-    def attention(self, layer: int, step: int, res, samples=None, source: int | None = None):
-        """Run the HIP attention on the resolved locations and compare sampled queries with the fp64
-        oracle computed from host rows at the selected positions.  Returns (max_abs, max_rel)."""
+    def _attn_inputs(self, layer: int, step: int):
         w = self.w
-        src = res["src"] if source is None else source
         q_np = synth.queries(w, layer, step)
         q = torch.from_numpy(q_np.view(np.int16)).cuda()
         if w.kind == "mla":
@@ -181,10 +185,29 @@ class Harness:
             ad = hsk.gqa_desc(requests=w.requests, heads=w.heads, kv_heads=w.kv_heads, dh=w.dk, top_k=w.top_k,
                               page_tokens=w.page_tokens, scale=w.scale)
             out = torch.zeros((w.requests, w.heads, w.dk), dtype=torch.int16, device="cuda")
-        nbytes = hsk.attn_scratch_bytes(ad)
-        scratch = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-        hsk.sparse_decode_attn(ad, q, self.store.pool_base(src), res["d_locs"], None, out, scratch, nbytes)
+        scratch = torch.empty(hsk.attn_scratch_bytes(ad), dtype=torch.uint8, device="cuda")
+        return q, ad, out, scratch
+
+    def run_attention(self, layer: int, step: int, res, source: int | None = None):
+        """hsk_sparse_decode_attn on the resolved locations; returns the bf16 output (int16 view)."""
+        src = res["src"] if source is None else source
+        q, ad, out, scratch = self._attn_inputs(layer, step)
+        hsk.sparse_decode_attn(ad, q, self.store.pool_base(src), res["d_locs"], None, out, scratch, scratch.numel())
         torch.cuda.synchronize()
+        return out
+
+    def attention(self, layer: int, step: int, res, samples=None, source: int | None = None):
+        """Run the HIP attention on the resolved locations and compare sampled queries with the fp64
+        oracle computed from host rows at the selected positions.  Returns (max_abs, max_rel)."""
+        out = self.run_attention(layer, step, res, source)
+        return self.check_attention(layer, step, res, out, samples, source)
+
+    def check_attention(self, layer: int, step: int, res, out, samples=None, source: int | None = None):
+        """Compare a bf16 attention output with the fp64 oracle on sampled queries (MLA: (request, query)
+        pairs; GQA: units).  Returns (max_abs, max_rel)."""
+        w = self.w
+        src = res["src"] if source is None else source
+        q_np = synth.queries(w, layer, step)
         got = synth.bf16_to_f32(out.cpu().numpy().view(np.uint16)).astype(np.float64)
         sel = res["sel"]
         host_src = 0 if w.host_alias else src

@@ -54,9 +54,12 @@ def test_workspace_and_pool_sizes(hsk, name):
     ws, pool = hsk.workspace_bytes(d)
     rows = w.units * w.hot_slots + w.units * w.tail_rows + opt_pages * page_rows + w.units * w.staging_rows
     assert pool == rows * w.sources * w.row_bytes
-    # metadata: key, rec (4 B), order (2 B) per slot, page table (4 B) per row, maps, plans
+    # metadata: key, rec (4 B), order (2 B) per slot, page table (4 B) per row, maps, plans; one fill code
+    # (4 B) per selection for the fused resolve + attend when requests carry one query
     per_src = w.units * w.hot_slots * 10 + w.units * w.ctx * 4 + 2 * 4 * w.units * w.queries * w.top_k
-    assert per_src * w.sources <= ws <= per_src * w.sources + w.units * (w.ctx // 64 + 64) * 4 * w.sources + (1 << 20)
+    fill = 4 * w.units * w.top_k if w.queries == 1 else 0
+    lo = per_src * w.sources + fill
+    assert lo <= ws <= lo + w.units * (w.ctx // 64 + 64) * 4 * w.sources + (1 << 20)
 
 
 def test_invalid_descriptions_rejected(hsk):

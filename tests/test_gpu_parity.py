@@ -211,21 +211,27 @@ def test_optional_pages_and_reclaim_small():
 
 
 def test_dsa100k_full_size_sampled_attention():
-    """The 100K-context batch-64 decode at full size (4 layers), in the launch configuration the
-    benchmark times: resolution bit-exact on every call, pool bytes checked on every call, attention
-    on sampled (request, layer, step) triples."""
+    """The 100K-context batch-64 decode at full size (4 layers), in the launch configurations the
+    benchmark times: resolve + gather + attention and the fused resolve + attend, alternating over
+    (step, layer) on the same stores.  Resolution bit-exact on every call, pool bytes checked on every
+    call, attention on sampled (request, layer, step) triples."""
     w = synth.WORKLOADS["dsa100k"]
-    h = Harness(w, steps=3, check_meta_every=2)
+    h = Harness(w, steps=4, check_meta_every=2)
     rng = np.random.default_rng(5)
     for t in range(h.steps):
         for layer in range(w.layers):
-            res = h.resolve(layer, t, meta_reqs=range(0, w.requests, 9) if t % 2 == 0 else [])
+            fused = (t + layer) % 2 == 1
+            res = h.resolve(layer, t, meta_reqs=range(0, w.requests, 9) if t % 2 == 0 else [], fused=fused)
             h.check_bytes(res)
             samples = [(int(r), 0) for r in rng.choice(w.requests, size=2, replace=False)]
-            err = h.attention(layer, t, res, samples=samples)
+            if fused:
+                err = h.check_attention(layer, t, res, res["out"], samples=samples)
+            else:
+                err = h.attention(layer, t, res, samples=samples)
             st = res["stats"]
-            log(f"[dsa100k] step {t} layer {layer}: hit_sel={int(st['n_hit_sel'].sum())} "
-                f"miss={int(st['n_miss'].sum())} tail={int(st['n_tail'].sum())} attn err {err[0]:.2e}")
+            log(f"[dsa100k] step {t} layer {layer} {'fused' if fused else 'separate'}: "
+                f"hit_sel={int(st['n_hit_sel'].sum())} miss={int(st['n_miss'].sum())} "
+                f"tail={int(st['n_tail'].sum())} attn err {err[0]:.2e}")
     h.close()
 
 
