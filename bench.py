@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PCIE_PEAK_GBS = 63.0
+MFMA_BF16_PEAK = 2.5e15
 
 
 def log(msg: str) -> None:
@@ -127,10 +128,14 @@ def hits_only(hsk, w, store, sels, d_q, d_locs, d_stats, ad, scratch, nscratch, 
     nbytes = resolve_algorithmic_bytes(w) + attn_algorithmic_bytes(w)
     gbs = nbytes / (both * 1e-3) / 1e9
     rows = w.requests * w.top_k
+    flops = 2.0 * w.heads * (w.dk + w.dv) * rows
     return {"ms_per_layer_step": both, "resolve_ms": res_ms, "attention_ms": att_ms, "misses": misses,
             "algorithmic_bytes_per_layer_step": nbytes, "achieved_GBps": gbs, "hbm_peak_GBps": HBM_PEAK_GBS,
             "frac_hbm": gbs / HBM_PEAK_GBS, "rows_per_s": rows / (both * 1e-3),
-            "steps_per_s": 1.0 / (both * 1e-3 * w.layers)}
+            "steps_per_s": 1.0 / (both * 1e-3 * w.layers),
+            "resolve_fraction": res_ms / both, "attention_fraction": att_ms / both,
+            "attention_TFLOPs": flops / (att_ms * 1e-3) / 1e12,
+            "attention_frac_mfma_bf16": flops / (att_ms * 1e-3) / MFMA_BF16_PEAK}
 
 
 def misses_only(hsk, synth, w, gather_blocks: int, calls: int = 12) -> dict:
@@ -166,6 +171,97 @@ def misses_only(hsk, synth, w, gather_blocks: int, calls: int = 12) -> dict:
     return {"bytes_per_call": fetched, "ms_per_call": ms, "achieved_GBps": gbs, "host_link_peak_GBps": PCIE_PEAK_GBS,
             "frac_host_link": gbs / PCIE_PEAK_GBS, "status": status,
             "note": "resolve kernel + zero-copy gather per call; bytes = distinct misses x 1152"}
+
+
+def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) -> dict:
+    """Fig. 8a analog with W queries per request: every call selects rows no earlier call selected, and the
+    W queries of a request share all of their k rows, half of them, or none, so the distinct missing rows per
+    request are k, (W + 1) k / 2 or W k.  Each distinct row is copied once (the shared ones dedup); the
+    slope of time against copied bytes is the achieved host-link rate."""
+    import torch
+    R, k, n = w.requests, w.top_k, w.ctx
+    S = W * k - k
+    st = hsk.KVStore(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=k, tail_rows=0, ctx=n, max_queries=W,
+                     top_k=k, staging_rows=S, gather_blocks=gather_blocks)
+    for r in range(R):
+        synth.fill_kv_rows(st.host_ptr(0, r), w, 0, r, 0, n)
+    g = np.random.default_rng([w.seed, 98])
+    perms = [g.permutation(n).astype(np.int32) for _ in range(R)]
+    cursor = [0] * R
+
+    def take(r, m):
+        a = perms[r][cursor[r]:cursor[r] + m]
+        cursor[r] += m
+        assert a.size == m, "context exhausted"
+        return a
+
+    locs = torch.empty((R, W, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(R)
+    stream = torch.cuda.current_stream()
+    points, epoch = {}, 1
+    for mode, shared in (("shared", k), ("half_shared", k // 2), ("disjoint", 0)):
+        times, byts = [], []
+        for c in range(calls + 1):
+            sel = np.empty((R, W, k), np.int32)
+            for r in range(R):
+                common = take(r, shared)
+                for j in range(W):
+                    sel[r, j, :shared] = common
+                    sel[r, j, shared:] = take(r, k - shared)
+            d = torch.from_numpy(sel).cuda()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st.resolve_step(0, epoch, d, locs, stats)
+            b.record(stream)
+            torch.cuda.synchronize()
+            epoch += 1
+            if c:   # the first call of each mode warms up
+                times.append(a.elapsed_time(b))
+                byts.append(int(hsk.stats_to_numpy(stats)["fetched_bytes"].sum()))
+        points[mode] = {"bytes_per_call": float(np.mean(byts)), "ms_per_call": float(np.mean(times))}
+    status = st.sync_status()
+    st.close()
+    x = np.array([v["bytes_per_call"] for v in points.values()])
+    y = np.array([v["ms_per_call"] for v in points.values()]) * 1e-3
+    slope, icpt = np.polyfit(x, y, 1)
+    gbs = 1.0 / slope / 1e9
+    return {"W": W, "points": points, "fit_GBps": gbs, "fit_intercept_us": icpt * 1e6,
+            "host_link_peak_GBps": PCIE_PEAK_GBS, "frac_host_link": gbs / PCIE_PEAK_GBS, "status": status,
+            "note": f"{R} requests x {W} queries x top-{k}; hot slots = k, staging {S} rows per request"}
+
+
+def no_io_bound(hsk, synth, w, sels, d_q, ad, scratch, nscratch, steps: int) -> dict:
+    """The no-IO bound (HiSparse section 4.6): layer 0's selection stream resolved by a store whose copies
+    from host are skipped (pool rows stale), then attention; timing only, never a correct result."""
+    import torch
+    R, k = w.requests, w.top_k
+    st = hsk.KVStore(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=w.hot_slots, tail_rows=w.tail_rows,
+                     ctx=w.ctx, max_queries=1, top_k=k, gather_mode=hsk.GATHER_NO_IO)
+    st.commit_prefill()
+    locs = torch.empty((R, 1, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(R)
+    out = torch.empty((R, 1, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    pool = st.pool_base(0)
+    stream = torch.cuda.current_stream()
+    d_sel = [torch.from_numpy(np.ascontiguousarray(sels[0][t])).cuda() for t in range(steps)]
+    ev = []
+    for t in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        st.resolve_step(0, t + 1, d_sel[t], locs, stats)
+        e[1].record(stream)
+        hsk.sparse_decode_attn(ad, d_q[0][t], pool, locs, None, out, scratch, nscratch)
+        e[2].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    status = st.sync_status()
+    st.close()
+    ev = ev[2:]
+    res = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    both = float(np.mean([a.elapsed_time(c) for a, _, c in ev]))
+    return {"ms_per_layer_step": both, "resolve_ms": res, "rows_per_s": R * k / (both * 1e-3),
+            "steps_per_s": 1.0 / (both * 1e-3 * w.layers), "status": status,
+            "note": "layer 0's selection stream; host copies skipped (pool rows stale)"}
 
 
 def memcpy_ceiling(nbytes: int = 1 << 28, reps: int = 8) -> dict:
@@ -582,6 +678,9 @@ def main() -> int:
         result["hits_only"] = hits_only(hsk, w, store, sels, d_q, d_locs, d_stats, ad, scratch, nscratch, pools,
                                         first_epoch=total_steps + 1)
         result["misses_only"] = misses_only(hsk, synth, w, args.gather_blocks)
+        result["misses_sweep_w8"] = misses_sweep(hsk, synth, w, args.gather_blocks)
+        result["no_io_bound"] = no_io_bound(hsk, synth, w, sels, d_q, ad, scratch, nscratch,
+                                            steps=min(total_steps, 12))
         result["host_link_ceiling"] = memcpy_ceiling()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")

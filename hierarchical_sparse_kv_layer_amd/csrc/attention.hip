@@ -37,9 +37,9 @@ struct AttnArgs {
   const int32_t* locs;
   const int32_t* nq;
   uint16_t* out;
-  float* po;   // [RQ][split][H][dv]
-  float* pm;   // [RQ][split][H]
-  float* pl;   // [RQ][split][H]
+  uint16_t* po;  // [RQ][split][H][dv] bf16 partial outputs, each normalised by its own sum
+  float* pm;     // [RQ][split][H] partial maxima (natural-log units)
+  float* pl;     // [RQ][split][H] partial sums of e^(s - m)
   int32_t R, Qmax, H, Hkv, dk, dv, k, row_elems, page_tokens, split, rows_per_split;
   float scale;
 };
@@ -90,14 +90,16 @@ struct MlaArgs {
   const int32_t* locs;
   const int32_t* nq;
   uint16_t* out;
-  float* po;
+  uint16_t* po;
   float* pm;
   float* pl;
   const int32_t* fill;  // fused resolve + attend: per-selection host source (-1 resident, else 2 p + first)
   const char* host;     // fused: device-visible pinned host rows of request 0 of the source
   int64_t host_req_stride;
   int32_t Qmax, H, k, row_bytes, split, rows_per_split;
-  float scale_log2;  // softmax scale * log2(e)
+  int32_t hgroups, RQ;
+  int32_t xcd_groups;  // > 0: the split x hgroups workgroups of one query share an XCD (see mla_block)
+  float scale_log2;    // softmax scale * log2(e)
 };
 
 // byte offset in a tile of 16-byte chunk c (values 8c..8c+7) of tile row t
@@ -120,7 +122,7 @@ __device__ __forceinline__ void dma16(const char* gsrc, const HSK_LDS char* ldst
 
 template <int N>
 __device__ __forceinline__ void wait_tile_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void wait_tile_barrier_n(int n) {
@@ -140,6 +142,28 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // and the first occurrence of each is written from the LDS tile into its pool row; the kernel is then
 // bound by the host link, so it waits for each tile's loads one tile ahead only (stores share the in-order
 // memory counter with the loads, which rules out the deeper fixed-count waits).
+// Workgroup id -> (partition, head group, query).  Workgroups are handed to the 8 XCDs in turn (id mod 8),
+// and each XCD has its own L2: with xcd_groups = G > 0 the G = split x hgroups workgroups of query rq get
+// ids 8 (G (rq / 8) + g) + rq mod 8, all on one XCD and dispatched together, so the query's Q block (read by
+// every partition) and, across head groups, its rows come from that L2 after the first read.  Ids past the
+// last query exit at once.  xcd_groups = 0 keeps the plain order (few queries: spreading them over the
+// XCDs matters more).
+__device__ __forceinline__ bool mla_block(const MlaArgs& a, int id, int* sp, int* hgrp, int* rq) {
+  int g, q;
+  if (a.xcd_groups > 0) {
+    const int x = id & 7, j = id >> 3;
+    g = j % a.xcd_groups;
+    q = (j / a.xcd_groups) * 8 + x;
+  } else {
+    g = id % (a.split * a.hgroups);
+    q = id / (a.split * a.hgroups);
+  }
+  *sp = g % a.split;
+  *hgrp = g / a.split;
+  *rq = q;
+  return q < a.RQ;
+}
+
 template <int NHB, int NPAIR, bool FUSED>
 __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   constexpr int NW = 2 * NPAIR;
@@ -153,7 +177,8 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   __shared__ int32_t s_loc[FUSED ? kMaxFusedRows : kMaxSplitRows];
   __shared__ int32_t s_fill[FUSED ? kMaxFusedRows : 1];
 
-  const int sp = blockIdx.x, hgrp = blockIdx.y, rq = blockIdx.z;
+  int sp, hgrp, rq;
+  if (!mla_block(a, blockIdx.x, &sp, &hgrp, &rq)) return;
   if (a.nq) {
     const int r = rq / a.Qmax, qi = rq % a.Qmax;
     if (qi >= a.nq[r]) return;
@@ -219,11 +244,15 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     for (int v = 0; v < NTOK; ++v) {
       const int x = tb + tok[v] < nrows ? tb + tok[v] : 0;   // rows past the end re-read row 0 (masked)
       const int32_t loc = s_loc[x];
+      // an opaque copy of the lane offset: otherwise the compiler keeps pool + offset as a 64-bit value
+      // live across the whole loop
+      int sw = swz[v];
+      asm volatile("" : "+v"(sw));
       if (FUSED && s_fill[x] >= 0) {
-        rp[v] = hostr + (int64_t)(s_fill[x] >> 1) * a.row_bytes + swz[v];
+        rp[v] = hostr + ((int64_t)(s_fill[x] >> 1) * a.row_bytes + sw);
       } else {
         // the locations of a request the resolve rejected are -1: the fused kernel reads row 0 for them
-        rp[v] = a.pool + (int64_t)(FUSED && loc < 0 ? 0 : loc) * a.row_bytes + swz[v];
+        rp[v] = a.pool + ((int64_t)(FUSED && loc < 0 ? 0 : loc) * a.row_bytes + sw);
       }
     }
 #pragma unroll
@@ -248,38 +277,13 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) { m_run[hb] = -INFINITY; l_run[hb] = 0.f; }
 
-  if (ntiles > 0) issue(0, 0);
-  if (!FUSED && ntiles > 1) issue(1, 1);
-  for (int T = 0; T < ntiles; ++T) {
-    const int b = T % kBufs;
-    if (FUSED) {
-      wait_tile_barrier<0>();
-      if (T + 1 < ntiles) issue(T + 1, (T + 1) % kBufs);
-    } else {
-      if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
-      if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
-    }
-    const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[b][0];
-    const int rem = nrows - T * kTile;
-    if constexpr (FUSED) {
-      // the rows this call fetched for the first time go from the tile into their pool rows
-      uint32_t wb;
-      {
-        const int x = T * kTile + (lane & 31);
-        wb = (uint32_t)__ballot(hgrp == 0 && (lane & 31) < rem && (s_fill[x < nrows ? x : 0] & 1));
-      }
-      for (uint32_t mm = wb; mm; mm &= mm - 1) {
-        const int row = __builtin_ctz(mm);
-        if (tid < kMlaDk / 8) {
-          typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-          const u32x4_t v = *(const HSK_LDS u32x4_t*)(tile + tile_off(row, tid));
-          *(u32x4_t*)(a.pool + (int64_t)s_loc[T * kTile + row] * a.row_bytes + tid * 16) = v;
-        }
-      }
-    }
-
+  // Tile phases.  score_phase(T): this wave's partial scores over its half of the key dims, written to
+  // s_x for the partner.  pv_phase(T): the partner's partials (visible after a barrier) completed into
+  // scores, online softmax, then O += P V over this wave's half of the value columns.
+  f32x4 sacc[2][NHB];
+  auto score_phase = [&](int T) {
+    const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[T % kBufs][0];
     // partial scores over this wave's half of the key dims
-    f32x4 sacc[2][NHB];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -302,7 +306,11 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) s_x[wave][tb * NHB + hb][lane] = sacc[tb][hb];
-    lds_barrier();
+  };
+  auto pv_phase = [&](int T) {
+    const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[T % kBufs][0];
+    const int rem = nrows - T * kTile;
+    // the partner's partial blocks complete the scores
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -390,6 +398,38 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #undef HSK_PV_STEP
       static_assert(CB == 16, "the unrolled P.V sequence covers 16 column blocks");
     }
+  };
+
+  if (ntiles > 0) issue(0, 0);
+  if (!FUSED && ntiles > 1) issue(1, 1);
+  for (int T = 0; T < ntiles; ++T) {
+    if (FUSED) {
+      wait_tile_barrier<0>();
+      if (T + 1 < ntiles) issue(T + 1, (T + 1) % kBufs);
+    } else {
+      if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
+      if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
+    }
+    if constexpr (FUSED) {
+      const HSK_LDS char* tile = (const HSK_LDS char*)&s_tile[T % kBufs][0];
+      const int rem = nrows - T * kTile;
+      // the rows this call fetched for the first time go from the tile into their pool rows
+      uint32_t wb;
+      {
+        const int x = T * kTile + (lane & 31);
+        wb = (uint32_t)__ballot(hgrp == 0 && (lane & 31) < rem && (s_fill[x < nrows ? x : 0] & 1));
+      }
+      for (uint32_t mm = wb; mm; mm &= mm - 1) {
+        const int row = __builtin_ctz(mm);
+        if (tid < kMlaDk / 8) {
+          const u32x4 v = *(const HSK_LDS u32x4*)(tile + tile_off(row, tid));
+          *(u32x4*)(a.pool + (int64_t)s_loc[T * kTile + row] * a.row_bytes + tid * 16) = v;
+        }
+      }
+    }
+    score_phase(T);
+    lds_barrier();
+    pv_phase(T);
   }
 
   // epilogue: lane holds head hbase + 16 hb + jl, columns 256 half + 16 cb + 4 g + v
@@ -399,26 +439,22 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const int head = hbase + 16 * hb + jl;
-    if (a.split == 1) {
-      const float inv = 1.f / l;
-      uint16_t* o = a.out + ((int64_t)rq * a.H + head) * kMlaDv + 256 * half + 4 * g;
+    // the output (one partition) or the partition's output normalised by its own sum, in bf16
+    const float inv = 1.f / l;
+    const int64_t ps = ((int64_t)rq * a.split + sp) * a.H + head;
+    uint16_t* o = (a.split == 1 ? a.out + ((int64_t)rq * a.H + head) * kMlaDv : a.po + ps * kMlaDv) +
+                  256 * half + 4 * g;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const f32x4 v = oacc[cb][hb] * inv;
-        u32x2 w;
-        w.x = (uint32_t)f2bf16(v[0]) | ((uint32_t)f2bf16(v[1]) << 16);
-        w.y = (uint32_t)f2bf16(v[2]) | ((uint32_t)f2bf16(v[3]) << 16);
-        *(u32x2*)(o + 16 * cb) = w;
-      }
-    } else {
-      const int64_t ps = ((int64_t)rq * a.split + sp) * a.H + head;
-      float* po = a.po + ps * kMlaDv + 256 * half + 4 * g;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) *(f32x4*)(po + 16 * cb) = oacc[cb][hb];
-      if (half == 0 && g == 0) {
-        a.pm[ps] = m_run[hb] * kLn2;   // natural-log units, as the combine expects
-        a.pl[ps] = l;
-      }
+    for (int cb = 0; cb < CB; ++cb) {
+      const f32x4 v = oacc[cb][hb] * inv;
+      u32x2 w;
+      w.x = (uint32_t)f2bf16(v[0]) | ((uint32_t)f2bf16(v[1]) << 16);
+      w.y = (uint32_t)f2bf16(v[2]) | ((uint32_t)f2bf16(v[3]) << 16);
+      *(u32x2*)(o + 16 * cb) = w;
+    }
+    if (a.split > 1 && half == 0 && g == 0) {
+      a.pm[ps] = m_run[hb] * kLn2;   // natural-log units, as the combine expects
+      a.pl[ps] = l;
     }
   }
 }
@@ -444,7 +480,7 @@ struct GqaArgs {
   const char* pool;
   const int32_t* locs;
   uint16_t* out;
-  float* po;
+  uint16_t* po;
   float* pm;
   float* pl;
   int32_t H, Hkv, k, page_tokens, row_bytes, split, pages_per_split;
@@ -544,14 +580,14 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
   float l = l_lane;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  const float inv = 1.f / l;
+  const uint32_t w = (uint32_t)f2bf16(o0 * inv) | ((uint32_t)f2bf16(o1 * inv) << 16);
   if (a.split == 1) {
-    const float inv = 1.f / l;
-    const uint32_t w = (uint32_t)f2bf16(o0 * inv) | ((uint32_t)f2bf16(o1 * inv) << 16);
     *(uint32_t*)(a.out + ((int64_t)r * a.H + head) * 128 + 2 * lane) = w;
     return;
   }
   const int64_t ps = ((int64_t)r * a.split + sp) * a.H + head;
-  *(float2*)(a.po + ps * 128 + 2 * lane) = make_float2(o0, o1);
+  *(uint32_t*)(a.po + ps * 128 + 2 * lane) = w;  // normalised by this partition's sum
   if (lane == 0) {
     a.pm[ps] = m_run * kLn2;  // natural-log units, as the combine expects
     a.pl[ps] = l;
@@ -559,9 +595,10 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------------
-// combine: one wave per (query, head), 4 waves per block.  Lane l owns float4 chunks l and l + 64 of the
-// dv output values (dv <= 512); the partitions' weights e^{m_s - M} / L come from a lane-parallel max and
-// sum over the partitions, and the partial outputs are read four partitions at a time.
+// combine: one wave per (query, head), 4 waves per block.  Partition s holds its output normalised by its
+// own sum l_s, in bf16, with its maximum m_s: out = sum_s w_s o_s with w_s = l_s e^(m_s - M) / L and
+// L = sum_s l_s e^(m_s - M).  The weights come from a lane-parallel max and sum over the partitions; lane
+// x owns the 16-byte chunk x (8 values) of the dv outputs (dv <= 512), read four partitions at a time.
 // ------------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
   const int lane = threadIdx.x & 63;
@@ -591,38 +628,36 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
   const float invL = 1.f / L;
-  const int nchunk = dv >> 2;
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bool mine = lane < (dv >> 3);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 4) {
     float w[4];
-    f32x4 v[4][2];
+    u32x4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int sidx = s0 + u;
-      const float m = sidx < S ? a.pm[p0 + (int64_t)sidx * a.H] : -INFINITY;
-      w[u] = m == -INFINITY ? 0.f : __expf(m - M) * invL;
-      const f32x4* po = (const f32x4*)(a.po + (p0 + (int64_t)(sidx < S ? sidx : 0) * a.H) * dv);
+      const int64_t ps = p0 + (int64_t)(sidx < S ? sidx : 0) * a.H;
+      const float m = sidx < S ? a.pm[ps] : -INFINITY;
+      w[u] = m == -INFINITY ? 0.f : __expf(m - M) * a.pl[ps] * invL;
+      v[u] = (sidx < S && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int x = lane + 64 * c;
-        v[u][c] = (sidx < S && x < nchunk) ? po[x] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(x[e] << 16) * w[u];
+        acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u) * w[u];
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) acc[c] += v[u][c] * w[u];
   }
-  uint16_t* out = a.out + ((int64_t)rq * a.H + h) * dv;
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int x = lane + 64 * c;
-    if (x < nchunk) {
-      u32x2 o;
-      o.x = (uint32_t)f2bf16(acc[c][0]) | ((uint32_t)f2bf16(acc[c][1]) << 16);
-      o.y = (uint32_t)f2bf16(acc[c][2]) | ((uint32_t)f2bf16(acc[c][3]) << 16);
-      *(u32x2*)(out + 4 * x) = o;
-    }
+  if (mine) {
+    u32x4 o;
+    o.x = (uint32_t)f2bf16(acc[0]) | ((uint32_t)f2bf16(acc[1]) << 16);
+    o.y = (uint32_t)f2bf16(acc[2]) | ((uint32_t)f2bf16(acc[3]) << 16);
+    o.z = (uint32_t)f2bf16(acc[4]) | ((uint32_t)f2bf16(acc[5]) << 16);
+    o.w = (uint32_t)f2bf16(acc[6]) | ((uint32_t)f2bf16(acc[7]) << 16);
+    *(u32x4*)(a.out + ((int64_t)rq * a.H + h) * dv + 8 * lane) = o;
   }
 }
 
@@ -664,6 +699,8 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
       p->rows_per_split = rps;
       p->split = (k + rps - 1) / rps;
     }
+    // one-dimensional grid: its work-items must stay below 2^31
+    if ((int64_t)p->split * p->hgroups * (RQ + 8) * 128 * p->npair >= (int64_t(1) << 31)) return false;
   } else if (d->kind == HSK_ATTN_GQA) {
     if (d->max_queries != 1 || d->kv_heads < 1 || d->heads % d->kv_heads || d->heads / d->kv_heads > 4 ||
         d->dk != 128 || d->dv != 128 || d->page_tokens < 1 || d->row_elems != d->page_tokens * 2 * d->dk)
@@ -684,17 +721,22 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
   }
   const int64_t parts = RQ * p->split * d->heads;
   const bool partials = p->split > 1;
-  p->po_bytes = partials ? (parts * d->dv * 4 + 255) / 256 * 256 : 0;
+  p->po_bytes = partials ? (parts * d->dv * 2 + 255) / 256 * 256 : 0;
   p->pm_bytes = partials ? (parts * 4 + 255) / 256 * 256 : 0;
   p->scratch = p->po_bytes + 2 * p->pm_bytes;
   if (p->scratch < 256) p->scratch = 256;
   return true;
 }
 
+// Fills the launch fields of m (head groups, queries, XCD grouping) and launches the MLA kernel.
 template <int NHB, int NPAIR, bool FUSED = false>
-static void launch_mla(const MlaArgs& m, const AttnPlan& p, int64_t RQ, hipStream_t s) {
-  hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR, FUSED>), dim3(p.split, p.hgroups, RQ), dim3(128 * NPAIR), 0, s,
-                     m);
+static void launch_mla(MlaArgs m, const AttnPlan& p, int64_t RQ, hipStream_t s) {
+  const int64_t G = (int64_t)p.split * p.hgroups;
+  m.hgroups = p.hgroups;
+  m.RQ = (int32_t)RQ;
+  m.xcd_groups = (G > 1 && RQ >= 8) ? (int32_t)G : 0;
+  const int64_t blocks = m.xcd_groups ? 8 * G * ((RQ + 7) / 8) : G * RQ;
+  hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR, FUSED>), dim3((unsigned)blocks), dim3(128 * NPAIR), 0, s, m);
 }
 
 }  // namespace hsk
@@ -732,7 +774,7 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
   a.split = p.split;
   a.rows_per_split = p.rows_per_split;
   a.scale = d->scale;
-  a.po = (float*)d_scratch;
+  a.po = (uint16_t*)d_scratch;
   a.pm = (float*)((char*)d_scratch + p.po_bytes);
   a.pl = (float*)((char*)d_scratch + p.po_bytes + p.pm_bytes);
   if (d->kind == HSK_ATTN_MLA) {
@@ -786,7 +828,7 @@ hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* p
   const int64_t RQ = d->num_requests;
   MlaArgs m;
   m.q = (const uint16_t*)q; m.pool = pool; m.locs = locs; m.nq = nullptr; m.out = (uint16_t*)out;
-  m.po = (float*)scratch;
+  m.po = (uint16_t*)scratch;
   m.pm = (float*)((char*)scratch + p.po_bytes);
   m.pl = (float*)((char*)scratch + p.po_bytes + p.pm_bytes);
   m.fill = fill; m.host = host; m.host_req_stride = host_req_stride;
