@@ -120,6 +120,15 @@ __device__ __forceinline__ void dma16(const char* gsrc, const HSK_LDS char* ldst
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gsrc) : "memory", "m0");
 }
 
+// max of x over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows), without LDS: permlane32_swap
+// pairs each lane with lane ^ 32, permlane16_swap with lane ^ 16
+__device__ __forceinline__ float max_across_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_tile_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
@@ -229,25 +238,21 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   // with 2 waves the loads alternate between two rows.
   constexpr int NTOK = NW >= 4 ? 1 : 2;
   const uint32_t lds_tile0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
-  int tok[NTOK], swz[NTOK];
-#pragma unroll
-  for (int v = 0; v < NTOK; ++v) {
-    tok[v] = 8 * ((wave + NW * v) & 3) + (lane >> 3);
-    swz[v] = (((lane & 7) ^ tile_swz(tok[v])) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
-  }
-
   auto issue = [&](int T, int b) {
     const int tb = T * kTile;
     const uint32_t lbase = lds_tile0 + b * kTileBytes + wave * 1024;
+    // the row and lane offset are recomputed from the lane id at every issue (a few VALU operations) rather
+    // than kept live across the loop, where registers are short
+    // (volatile, so that the compiler cannot hoist it and its uses out of the loop again)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const char* rp[NTOK];
 #pragma unroll
     for (int v = 0; v < NTOK; ++v) {
-      const int x = tb + tok[v] < nrows ? tb + tok[v] : 0;   // rows past the end re-read row 0 (masked)
+      const int tok = 8 * ((wave + NW * v) & 3) + (ln >> 3);
+      const int sw = (((ln & 7) ^ tile_swz(tok)) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
+      const int x = tb + tok < nrows ? tb + tok : 0;   // rows past the end re-read row 0 (masked)
       const int32_t loc = s_loc[x];
-      // an opaque copy of the lane offset: otherwise the compiler keeps pool + offset as a 64-bit value
-      // live across the whole loop
-      int sw = swz[v];
-      asm volatile("" : "+v"(sw));
       if (FUSED && s_fill[x] >= 0) {
         rp[v] = hostr + ((int64_t)(s_fill[x] >> 1) * a.row_bytes + sw);
       } else {
@@ -316,23 +321,26 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) sacc[tb][hb] += s_x[wave ^ 1][tb * NHB + hb][lane];
 
-    // online softmax; lane holds head hbase + 16 hb + jl, rows 16 tb + 4 g + v
+    // online softmax; lane holds head hbase + 16 hb + jl, rows 16 tb + 4 g + v.  The maximum is taken over
+    // the unscaled scores (the scale is positive) and the scale is applied inside the exponent's FMA;
+    // only the last tile of a partition masks rows.
+    const bool full = rem >= kTile;
     bf16x8 pf[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       float sv[8];
-      float tmax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float x = sacc[tb][hb][v] * a.scale_log2;
-          if (16 * tb + 4 * g + v >= rem) x = -INFINITY;
-          sv[4 * tb + v] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        for (int v = 0; v < 4; ++v) sv[4 * tb + v] = sacc[tb][hb][v];
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (16 * (i >> 2) + 4 * g + (i & 3) >= rem) sv[i] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      tmax = max_across_row_groups(tmax) * a.scale_log2;
       // The reference maximum moves only when a score exceeds it by more than 2^8 (log2 units 8): until
       // then the weights exp2(s - m) stay below 256, exact enough in bf16 and fp32, and the 128 output
       // accumulators need no rescaling.  The first tile always moves it (from -inf).
@@ -344,10 +352,11 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) oacc[cb][hb] *= alpha;
       }
+      const float mneg = -m_run[hb];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sv[i] - m_run[hb]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, mneg));
         psum += p;
         pf[hb][i] = (__bf16)p;
       }
