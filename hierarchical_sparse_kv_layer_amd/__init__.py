@@ -62,6 +62,9 @@ _sig = {
     "hsk_reclaim_plan": (_i32, [_vp, _i32, _i64, _P(_i32)]),
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
+    "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
+    "hsk_context_rows": (_i32, [_vp, _i32, _i32, _P(_i64)]),
+    "hsk_completed_rows": (_i32, [_i64, _i64, _i32, _P(_i64), _P(_i64)]),
     "hsk_pool_base": (_i32, [_vp, _i32, _P(_vp)]),
     "hsk_attn_scratch_bytes": (_i32, [_P(AttnDesc), _P(ctypes.c_size_t)]),
     "hsk_sparse_decode_attn": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -157,6 +160,25 @@ def resolve_step(store: int, source: int, epoch: int, sel, nq, locs, stats, stre
                                  _stream(stream)), "hsk_resolve_step")
 
 
+def append_rows(store: int, source: int, rows, count: int, stream=None, backup_stream=None) -> None:
+    _check(_lib.hsk_append_rows(store, source, _ptr(rows), int(count), _stream(stream),
+                                _stream(backup_stream if backup_stream is not None else stream)),
+           "hsk_append_rows")
+
+
+def context_rows(store: int, source: int, req: int) -> int:
+    n = _i64()
+    _check(_lib.hsk_context_rows(store, source, req, ctypes.byref(n)), "hsk_context_rows")
+    return n.value
+
+
+def completed_rows(n_before: int, n_after: int, m: int):
+    first, count = _i64(), _i64()
+    _check(_lib.hsk_completed_rows(int(n_before), int(n_after), int(m), ctypes.byref(first), ctypes.byref(count)),
+           "hsk_completed_rows")
+    return first.value, count.value
+
+
 def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> None:
     _check(_lib.hsk_replay_plan(store, plan_source, dst_source, _stream(stream)), "hsk_replay_plan")
 
@@ -185,12 +207,13 @@ def resolve_attend(store: int, source: int, epoch: int, sel, locs, stats, adesc:
            "hsk_resolve_attend")
 
 
-def snapshot(store: int, source: int, req: int, B: int, n_rows: int, page_rows: int) -> dict:
+def snapshot(store: int, source: int, req: int, B: int, n_rows: int, page_rows: int, n_import: int) -> dict:
+    """n_rows: the source's context rows now (hsk_context_rows); n_import: ctx_len[req] at creation."""
     key = np.zeros(B, np.int32)
     rec = np.zeros(B, np.uint32)
     order = np.zeros(B, np.uint16)
     pt = np.zeros(n_rows, np.int32)
-    opt = np.zeros(max(1, n_rows // page_rows) if page_rows else 1, np.int32)
+    opt = np.zeros(max(1, n_import // page_rows) if page_rows else 1, np.int32)
     _check(_lib.hsk_snapshot(store, source, req, _ptr(key), _ptr(rec), _ptr(order), _ptr(pt), _ptr(opt)),
            "hsk_snapshot")
     return {"key": key, "rec": rec, "order": order.astype(np.int32), "pt": pt,
@@ -263,6 +286,12 @@ class KVStore:
         resolve_attend(self.handle, source, epoch, sel, locs, stats, adesc, q, out, scratch,
                        scratch.numel() * scratch.element_size(), stream)
 
+    def append_rows(self, source: int, rows, count: int, stream=None, backup_stream=None):
+        append_rows(self.handle, source, rows, count, stream, backup_stream)
+
+    def context_rows(self, source: int, req: int) -> int:
+        return context_rows(self.handle, source, req)
+
     def replay_plan(self, plan_source: int, dst_source: int, stream=None):
         replay_plan(self.handle, plan_source, dst_source, stream)
 
@@ -275,7 +304,8 @@ class KVStore:
         return self.pool[off: off + self.rows_per_source * self.row_bytes].view(self.rows_per_source, self.row_bytes)
 
     def snapshot(self, source: int, req: int) -> dict:
-        return snapshot(self.handle, source, req, self.B, int(self.ctx[req]), self.page_rows)
+        return snapshot(self.handle, source, req, self.B, self.context_rows(source, req), self.page_rows,
+                        int(self.ctx[req]))
 
     def read_plan(self, source: int, req: int):
         return read_plan(self.handle, source, req, self.max_queries * self.top_k)

@@ -35,7 +35,7 @@ struct SourceMeta {
 
 // Byte offsets of every region of the workspace.
 struct WorkspaceLayout {
-  int64_t ctx, err, fill, total;
+  int64_t ctx, wt_pos, err, fill, total;   // ctx [S][R] i64, wt_pos [S][2][R] i32
   std::vector<int64_t> key, rec, order, pt, opt, plan_n, plan_pos, plan_dst;
 };
 
@@ -84,6 +84,11 @@ hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStre
 hipError_t launch_tail_copy(const char* host, int64_t host_req_stride, char* pool, const int64_t* d_ctx,
                             int32_t R, int32_t B, int32_t T, int32_t row_bytes, hipStream_t s);
 hipError_t launch_copy_runs(const char* host, char* pool, const CopyRun* runs, int32_t n, hipStream_t s);
+// decode-loop append: rows -> tail ring, context grows (stream); tail ring -> host rows (backup stream)
+hipError_t launch_append_tail(const char* rows, char* pool, int64_t* ctx, int32_t* wt_pos, int32_t R, int32_t B,
+                              int32_t T, int32_t count, int32_t row_bytes, hipStream_t s);
+hipError_t launch_write_through(const char* pool, char* host, int64_t host_req_stride, const int32_t* wt_pos,
+                                int32_t R, int32_t B, int32_t T, int32_t count, int32_t row_bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 // MLA attention that reads the rows this call fetches straight from pinned host memory (fill codes of the
@@ -97,7 +102,8 @@ hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* p
 
 struct hsk_store {
   hsk_desc d;
-  std::vector<int64_t> ctx;
+  std::vector<int64_t> ctx;                 // [source * R + r] rows of each request's context, per source
+  std::vector<int64_t> n_import;            // [R] imported (prefill) history: what optional pages may cover
   int64_t max_pages = 0;
   int32_t plan_cap = 0;
   int64_t rows_per_src = 0;
@@ -105,7 +111,12 @@ struct hsk_store {
   int32_t device = 0;
   char* ws = nullptr;
   char* pool = nullptr;
-  int64_t* d_ctx = nullptr;
+  int64_t* d_ctx = nullptr;                 // [S][R]
+  int32_t* d_wt_pos = nullptr;              // [S][2][R] first position of the last two appends per source
+  std::vector<hipEvent_t> wt_done;          // [S][2] write-through of the last two appends per source
+  std::vector<uint8_t> wt_pending;          // [S][2] event recorded and not yet waited for
+  std::vector<hipEvent_t> tail_done;        // [S] tail writes of the last append
+  std::vector<int32_t> append_parity;       // [S]
   int32_t* d_err = nullptr;
   int32_t* d_fill = nullptr;                // [R][Qmax][k] per-selection host source of a fused call
   std::vector<hsk::SourceMeta> meta;

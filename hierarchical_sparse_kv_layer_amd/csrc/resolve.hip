@@ -605,6 +605,47 @@ __global__ __launch_bounds__(kGatherThreads) void tail_copy_kernel(const char* h
   }
 }
 
+// Decode-loop append (HiSparse section 3.3 step 4; Adaptive DHiSparse section 3.2): one block per request
+// copies its `count` new rows into the tail ring (row R*B + r*T + (p mod T) for p = n_r, ..), records n_r for
+// the write-through and advances n_r.
+__global__ __launch_bounds__(kGatherThreads) void append_tail_kernel(const char* rows, char* pool, int64_t* ctx,
+                                                                     int32_t* wt_pos, int32_t R, int32_t B,
+                                                                     int32_t T, int32_t count, int32_t row_bytes) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGatherThreads / 64;
+  const int64_t n = ctx[r];
+  for (int i = wave; i < count; i += kWaves) {
+    const u32x4* src = (const u32x4*)(rows + ((int64_t)r * count + i) * row_bytes);
+    u32x4* dst = (u32x4*)(pool + ((int64_t)R * B + (int64_t)r * T + ((n + i) % T)) * row_bytes);
+    wave_copy_row(src, dst, row_bytes >> 4, lane);
+  }
+  __syncthreads();  // every thread has read n_r
+  if (threadIdx.x == 0) {
+    wt_pos[r] = (int32_t)n;
+    ctx[r] = n + count;
+  }
+}
+
+// Write-through of an append: tail ring rows of positions wt_pos[r] .. + count - 1 -> the request's pinned
+// host rows (device stores over the host link).
+__global__ __launch_bounds__(kGatherThreads) void write_through_kernel(const char* pool, char* host, int64_t stride,
+                                                                       const int32_t* wt_pos, int32_t R, int32_t B,
+                                                                       int32_t T, int32_t count,
+                                                                       int32_t row_bytes) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGatherThreads / 64;
+  const int64_t p0 = wt_pos[r];
+  for (int i = wave; i < count; i += kWaves) {
+    const u32x4* src = (const u32x4*)(pool + ((int64_t)R * B + (int64_t)r * T + ((p0 + i) % T)) * row_bytes);
+    u32x4* dst = (u32x4*)(host + r * stride + (p0 + i) * row_bytes);
+    wave_copy_row(src, dst, row_bytes >> 4, lane);
+  }
+}
+
 // Contiguous byte runs host -> pool (optional-history population); one block per run.
 __global__ __launch_bounds__(kGatherThreads) void copy_runs_kernel(const char* host, char* pool, const CopyRun* runs) {
   const CopyRun run = runs[blockIdx.x];
@@ -666,6 +707,20 @@ hipError_t launch_tail_copy(const char* host, int64_t stride, char* pool, const 
   const int blocks = (T + 3) / 4 < 64 ? (T + 3) / 4 : 64;
   hipLaunchKernelGGL(tail_copy_kernel, dim3(blocks > 0 ? blocks : 1, R), dim3(kGatherThreads), 0, s, host, stride,
                      pool, d_ctx, R, B, T, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_tail(const char* rows, char* pool, int64_t* ctx, int32_t* wt_pos, int32_t R, int32_t B,
+                              int32_t T, int32_t count, int32_t row_bytes, hipStream_t s) {
+  hipLaunchKernelGGL(append_tail_kernel, dim3(R), dim3(kGatherThreads), 0, s, rows, pool, ctx, wt_pos, R, B, T, count,
+                     row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_through(const char* pool, char* host, int64_t stride, const int32_t* wt_pos, int32_t R,
+                                int32_t B, int32_t T, int32_t count, int32_t row_bytes, hipStream_t s) {
+  hipLaunchKernelGGL(write_through_kernel, dim3(R), dim3(kGatherThreads), 0, s, pool, host, stride, wt_pos, R, B, T,
+                     count, row_bytes);
   return hipGetLastError();
 }
 

@@ -45,7 +45,8 @@ bool layout_workspace(const hsk_desc& d, WorkspaceLayout* L) {
   const int64_t max_pages = d.page_rows ? d.max_ctx / d.page_rows : 0;
   const int64_t cap = (int64_t)d.max_queries * d.top_k;
   int64_t off = 0;
-  L->ctx = off; off = align_up(off + 8 * R);
+  L->ctx = off; off = align_up(off + 8 * R * d.num_sources);
+  L->wt_pos = off; off = align_up(off + 4 * 2 * R * d.num_sources);
   L->err = off; off = align_up(off + 4);
   // fill codes of the fused resolve + attend, which serves stores with one query per request
   L->fill = off; off = align_up(off + (d.max_queries == 1 ? 4 * R * cap : 0));
@@ -97,6 +98,10 @@ hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, si
 void hsk_kv_store_destroy(hsk_store* st) {
   if (!st) return;
   (void)hipDeviceSynchronize();
+  for (hipEvent_t e : st->wt_done)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->tail_done)
+    if (e) (void)hipEventDestroy(e);
   for (char* h : st->host)
     if (h) (void)hipHostFree(h);
   if (st->h_stage) (void)hipHostFree(st->h_stage);
@@ -113,9 +118,11 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   hsk_store* st = new (std::nothrow) hsk_store();
   if (!st) return HSK_ENOMEM;
   st->d = *desc;
-  st->ctx.assign(desc->ctx_len, desc->ctx_len + desc->num_requests);
-  st->d.ctx_len = st->ctx.data();
+  st->n_import.assign(desc->ctx_len, desc->ctx_len + desc->num_requests);
+  st->d.ctx_len = st->n_import.data();
   const int32_t R = desc->num_requests, B = desc->hot_slots;
+  st->ctx.clear();
+  for (int32_t k = 0; k < desc->num_sources; ++k) st->ctx.insert(st->ctx.end(), st->n_import.begin(), st->n_import.end());
   st->max_pages = desc->page_rows ? desc->max_ctx / desc->page_rows : 0;
   st->plan_cap = desc->max_queries * desc->top_k;
   st->rows_per_src = rows_per_source(*desc);
@@ -126,6 +133,15 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   WorkspaceLayout L;
   layout_workspace(*desc, &L);
   st->d_ctx = (int64_t*)(st->ws + L.ctx);
+  st->d_wt_pos = (int32_t*)(st->ws + L.wt_pos);
+  st->wt_done.assign(2 * (size_t)desc->num_sources, nullptr);
+  st->wt_pending.assign(2 * (size_t)desc->num_sources, 0);
+  st->tail_done.assign((size_t)desc->num_sources, nullptr);
+  st->append_parity.assign((size_t)desc->num_sources, 0);
+  for (hipEvent_t& e : st->wt_done)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
+  for (hipEvent_t& e : st->tail_done)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
   st->d_err = (int32_t*)(st->ws + L.err);
   st->d_fill = (int32_t*)(st->ws + L.fill);
   for (int32_t k = 0; k < desc->num_sources; ++k) {
@@ -161,7 +177,8 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
     return HSK_ENOMEM;
   }
   // metadata: empty caches, slot order 0..B-1
-  if (hipMemcpyAsync(st->d_ctx, st->ctx.data(), sizeof(int64_t) * R, hipMemcpyHostToDevice, s) != hipSuccess ||
+  if (hipMemcpyAsync(st->d_ctx, st->ctx.data(), sizeof(int64_t) * st->ctx.size(), hipMemcpyHostToDevice, s) !=
+          hipSuccess ||
       launch_fill_i32(st->d_err, 1, 0, s) != hipSuccess) {
     hsk_kv_store_destroy(st);
     return HSK_EHIP;
@@ -202,8 +219,9 @@ hsk_status hsk_commit_prefill(hsk_store* st, hsk_stream_t stream) {
     void* pool;
     hsk_pool_base(st, k, &pool);
     const int32_t hs = st->d.host_alias_sources ? 0 : k;
-    HSK_HIP(launch_tail_copy(st->host[hs], stride, (char*)pool, st->d_ctx, st->d.num_requests, st->d.hot_slots,
-                             st->d.tail_rows, st->d.row_bytes, (hipStream_t)stream));
+    HSK_HIP(launch_tail_copy(st->host[hs], stride, (char*)pool, st->d_ctx + (size_t)k * st->d.num_requests,
+                             st->d.num_requests, st->d.hot_slots, st->d.tail_rows, st->d.row_bytes,
+                             (hipStream_t)stream));
   }
   return HSK_OK;
 }
@@ -212,7 +230,9 @@ hsk_status hsk_residency_set(hsk_store* st, int32_t source, int32_t req, const i
                              int64_t n_pages, hsk_stream_t stream) {
   if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;
   if (st->d.page_rows == 0) return HSK_ESTATE;
-  const int64_t complete = st->ctx[req] / st->d.page_rows;
+  // optional residency covers complete pages of the imported history only (Adaptive DHiSparse section 3.1:
+  // rows generated during decoding stay under the tail and hot-cache rules)
+  const int64_t complete = st->n_import[req] / st->d.page_rows;
   if (n_pages < 0 || n_pages > complete || (n_pages > 0 && !h_page_ids)) return HSK_EINVAL;
   for (int64_t g = 0; g < n_pages; ++g)
     if (h_page_ids[g] < -1 || h_page_ids[g] >= st->d.opt_pool_pages) return HSK_EINVAL;
@@ -282,7 +302,8 @@ static int32_t gather_blocks_for(const hsk_store* st) {
 static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel,
                                 const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats) {
   ResolveArgs a;
-  a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats; a.ctx = st->d_ctx; a.m = st->meta[source];
+  a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats;
+  a.ctx = st->d_ctx + (size_t)source * st->d.num_requests; a.m = st->meta[source];
   a.err = st->d_err; a.fill = nullptr; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
   const int64_t R = st->d.num_requests;
   a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
@@ -343,6 +364,57 @@ hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, con
                           st->d.max_ctx * (int64_t)st->d.row_bytes, d_out, d_scratch, scratch_bytes, s);
 }
 
+hsk_status hsk_append_rows(hsk_store* st, int32_t source, const void* d_rows, int32_t count, hsk_stream_t stream,
+                           hsk_stream_t backup_stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_rows || count < 1 || 2 * count > st->d.tail_rows ||
+      st->d.host_alias_sources)
+    return HSK_EINVAL;
+  const int32_t R = st->d.num_requests;
+  int64_t* hctx = st->ctx.data() + (size_t)source * R;
+  for (int32_t r = 0; r < R; ++r)
+    if (hctx[r] + count > st->d.max_ctx) return HSK_EINVAL;
+  hipStream_t s = (hipStream_t)stream, b = (hipStream_t)backup_stream;
+  const int par = st->append_parity[source];
+  const size_t ev = 2 * (size_t)source + par;
+  void* pool;
+  hsk_pool_base(st, source, &pool);
+  int32_t* wt_pos = st->d_wt_pos + ((size_t)source * 2 + par) * R;
+  // The write-through of the append before last (same parity) reads tail rows that this append may overwrite,
+  // and its rows can leave the tail from this append on: the stream waits for it.  The last append's rows stay
+  // in the tail (2 count <= T), so its write-through keeps running beside the stream.
+  if (st->wt_pending[ev]) {
+    HSK_HIP(hipStreamWaitEvent(s, st->wt_done[ev], 0));
+    st->wt_pending[ev] = 0;
+  }
+  HSK_HIP(launch_append_tail((const char*)d_rows, (char*)pool, st->d_ctx + (size_t)source * R, wt_pos, R,
+                             st->d.hot_slots, st->d.tail_rows, count, st->d.row_bytes, s));
+  if (b != s) {
+    HSK_HIP(hipEventRecord(st->tail_done[source], s));
+    HSK_HIP(hipStreamWaitEvent(b, st->tail_done[source], 0));
+  }
+  HSK_HIP(launch_write_through((const char*)pool, st->host[source], st->d.max_ctx * (int64_t)st->d.row_bytes, wt_pos,
+                               R, st->d.hot_slots, st->d.tail_rows, count, st->d.row_bytes, b));
+  HSK_HIP(hipEventRecord(st->wt_done[ev], b));
+  st->wt_pending[ev] = 1;
+  st->append_parity[source] = par ^ 1;
+  for (int32_t r = 0; r < R; ++r) hctx[r] += count;
+  return HSK_OK;
+}
+
+hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int64_t* first, int64_t* count) {
+  if (!first || !count || m < 1 || n_before < 0 || n_after < n_before) return HSK_EINVAL;
+  *first = n_before / m;
+  *count = n_after / m - n_before / m;
+  return HSK_OK;
+}
+
+hsk_status hsk_context_rows(hsk_store* st, int32_t source, int32_t req, int64_t* n_rows) {
+  if (!st || !n_rows || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests)
+    return HSK_EINVAL;
+  *n_rows = st->ctx[(size_t)source * st->d.num_requests + req];
+  return HSK_OK;
+}
+
 hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
   if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
       dst_source >= st->d.num_sources)
@@ -370,9 +442,10 @@ hsk_status hsk_snapshot(hsk_store* st, int32_t source, int32_t req, int32_t* key
   if (key) HSK_HIP(hipMemcpy(key, m.key + req * B, 4 * B, hipMemcpyDeviceToHost));
   if (rec) HSK_HIP(hipMemcpy(rec, m.rec + req * B, 4 * B, hipMemcpyDeviceToHost));
   if (order) HSK_HIP(hipMemcpy(order, m.order + req * B, 2 * B, hipMemcpyDeviceToHost));
-  if (pt) HSK_HIP(hipMemcpy(pt, m.pt + (size_t)req * st->d.max_ctx, 4 * (size_t)st->ctx[req], hipMemcpyDeviceToHost));
+  const size_t n_r = (size_t)st->ctx[(size_t)source * st->d.num_requests + req];
+  if (pt) HSK_HIP(hipMemcpy(pt, m.pt + (size_t)req * st->d.max_ctx, 4 * n_r, hipMemcpyDeviceToHost));
   if (opt && st->max_pages) {
-    const size_t np = (size_t)(st->ctx[req] / st->d.page_rows);
+    const size_t np = (size_t)(st->n_import[req] / st->d.page_rows);
     if (np) HSK_HIP(hipMemcpy(opt, m.opt + (size_t)req * st->max_pages, 4 * np, hipMemcpyDeviceToHost));
   }
   return HSK_OK;

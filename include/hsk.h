@@ -86,7 +86,8 @@ typedef struct hsk_desc {
   int32_t staging_rows;        /* S >= 0: per request and source */
   int32_t host_alias_sources;  /* 1: every source reads source 0's host rows (one host payload) */
   int64_t max_ctx;             /* rows of host history reserved per request and source */
-  const int64_t* ctx_len;      /* host array [R]: n_r, 1 <= n_r <= max_ctx, n_r < 2^31 */
+  const int64_t* ctx_len;      /* host array [R]: n_r at creation (the imported history, every source),
+                                  1 <= n_r <= max_ctx, n_r < 2^31; hsk_append_rows grows it per source */
   int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
   int32_t gather_blocks;       /* workgroups (of 4 waves) of the gather kernel; 0 = automatic (384) */
 } hsk_desc;
@@ -125,7 +126,8 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
 hsk_status hsk_host_rows(hsk_store* store, int32_t source, int32_t req, void** h_rows, int64_t* n_rows);
 
 /* Copy every request's tail rows (positions [n_r - T, n_r)) of every source from host to pool.  HiSparse
- * section 3.3 (1): prefill writes each layer's KV to the host pool; the newest rows stay on device. */
+ * section 3.3 (1): prefill writes each layer's KV to the host pool; the newest rows stay on device.  Call
+ * it once, after the host rows are written and before any append. */
 hsk_status hsk_commit_prefill(hsk_store* store, hsk_stream_t stream);
 
 /* Set the optional-history map of complete pages [0, n_pages) of (source, request): h_page_ids[g] is the
@@ -133,8 +135,9 @@ hsk_status hsk_commit_prefill(hsk_store* store, hsk_stream_t stream);
  * pages are copied from host first and their map entries published after the copy, in stream order;
  * dropped entries are cleared in stream order, after earlier readers on the stream (Adaptive DHiSparse
  * section 3.1: ready locations tracked apart from allocated pages, reclaim after earlier readers).
- * Only complete pages of history may be mapped: n_pages <= n_r / page_rows.  A call that copies rows
- * waits for its copies before returning. */
+ * Only complete pages of the imported history may be mapped: n_pages <= ctx_len[r] / page_rows (rows
+ * generated during decoding stay under the tail and hot-cache rules, section 3.1).  A call that copies
+ * rows waits for its copies before returning. */
 hsk_status hsk_residency_set(hsk_store* store, int32_t source, int32_t req, const int32_t* h_page_ids,
                              int64_t n_pages, hsk_stream_t stream);
 
@@ -157,6 +160,33 @@ hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t defi
  */
 hsk_status hsk_resolve_step(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
                             const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream);
+
+/*
+ * Decode-loop append (HiSparse section 3.3, step 4 "write-through of generated KV"; Adaptive DHiSparse
+ * section 3.2, the tail): every request of `source` takes `count` new rows, d_rows [R][count][row_bytes]
+ * (device, e.g. the layer's KV of the tokens just generated), as positions n_r .. n_r + count - 1.
+ *   On `stream`: the rows are written into the request's tail ring (pool row R*B + r*T + (p mod T)) and
+ *   n_r grows, so the newest positions resolve directly for the following resolve calls; the row that
+ *   leaves the tail (position n_r - T) becomes history, resolved through the hot cache and fetched from
+ *   its host copy.
+ *   On `backup_stream` (may equal `stream`): after an event on `stream`, the new rows are written through
+ *   from the tail ring to the pinned host rows [r][n_r ..].  The stream waits for that copy at the
+ *   second-next append of the source, which is also the first after which those rows can leave the tail
+ *   (2 count <= T), so the host copy is complete before any fetch can reference it.
+ * d_rows may be reused once `stream` passes the call.  EINVAL (nothing queued): count < 1, 2 count > T,
+ * n_r + count > max_ctx for some request, or a store with host_alias_sources.
+ */
+hsk_status hsk_append_rows(hsk_store* store, int32_t source, const void* d_rows, int32_t count,
+                           hsk_stream_t stream, hsk_stream_t backup_stream);
+
+/* Rows of (source, request) context after the appends issued so far (host bookkeeping, no device access). */
+hsk_status hsk_context_rows(hsk_store* store, int32_t source, int32_t req, int64_t* n_rows);
+
+/* Adaptive DHiSparse Eq. 8 (pure host function): for a source that packs m consecutive token positions into
+ * each stored row, the rows completed when a request's tokens grow from n_before to n_after are
+ * [first, first + count) with first = floor(n_before / m) and first + count = floor(n_after / m); an
+ * incomplete last row stays in the tail until it is complete. */
+hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int64_t* first, int64_t* count);
 
 /* Plan replay (HiSparse section 3.5, plan-then-IO): copy the rows listed in plan_source's last miss plan
  * from dst_source's host rows into dst_source's pool, at the same pool rows.  A layer that shares its
@@ -231,8 +261,9 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
 /* ---------------------------------------------------------------------------------------------------- */
 /* Synchronous copy of (source, request) metadata into caller host buffers (any may be NULL):
  * key[B] (position held, -1 empty), rec[B] (2e+1 after a hit at epoch e, 2e after a fill, 0 empty),
- * order[B] (slots in ascending (rec, slot) order), pt[n_r] (slot of a position or -1),
- * opt[n_r / page_rows] (optional page id or -1).  Waits for all work on the device. */
+ * order[B] (slots in ascending (rec, slot) order), pt[n_r] (slot of a position or -1; n_r of the source
+ * after its appends, hsk_context_rows), opt[ctx_len[r] / page_rows] (optional page id or -1).  Waits for all
+ * work on the device. */
 hsk_status hsk_snapshot(hsk_store* store, int32_t source, int32_t req, int32_t* key, uint32_t* rec,
                         uint16_t* order, int32_t* pt, int32_t* opt);
 

@@ -56,7 +56,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
         L = ctypes.CDLL(LIB_PATH)
         i32, i64, u32, vp, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double
-        L.ora_create.argtypes = [i32, vp, i32, i32, i32, i64, i32, i32]
+        L.ora_create.argtypes = [i32, vp, i64, i32, i32, i32, i64, i32, i32]
         L.ora_create.restype = vp
         L.ora_destroy.argtypes = [vp]
         L.ora_destroy.restype = None
@@ -80,6 +80,12 @@ def lib():
         L.ora_bf16_from_f64.restype = None
         L.ora_reclaim_plan.argtypes = [vp, i32, i64]
         L.ora_reclaim_plan.restype = i32
+        L.ora_append.argtypes = [vp, i32]
+        L.ora_append.restype = i32
+        L.ora_context_rows.argtypes = [vp, i32]
+        L.ora_context_rows.restype = i64
+        L.ora_completed_rows.argtypes = [i64, i64, i32, vp, vp]
+        L.ora_completed_rows.restype = i32
         L.ora_ring_rows.argtypes = [i64, i64, i64]
         L.ora_ring_rows.restype = i64
         L.ora_ring_addr.argtypes = [i64, i64, i64]
@@ -98,13 +104,14 @@ class Source:
     """One payload source: R requests' hot caches (B slots), tails (T rows), optional-history page maps
     and staging rows, with a pool model of which host row each pool row holds."""
 
-    def __init__(self, R, ctx, B, T, page_rows=0, opt_pool_pages=0, staging_rows=0, row_bytes=1152):
+    def __init__(self, R, ctx, B, T, page_rows=0, opt_pool_pages=0, staging_rows=0, row_bytes=1152, max_ctx=None):
         self.R, self.B, self.T = int(R), int(B), int(T)
         self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, dtype=np.int64), (self.R,)))
+        self.max_ctx = int(self.ctx.max() if max_ctx is None else max_ctx)
         self.page_rows, self.opt_pool_pages, self.staging_rows = int(page_rows), int(opt_pool_pages), int(staging_rows)
         self.row_bytes = int(row_bytes)
-        self._h = lib().ora_create(self.R, _p(self.ctx), self.B, self.T, self.page_rows, self.opt_pool_pages,
-                                   self.staging_rows, self.row_bytes)
+        self._h = lib().ora_create(self.R, _p(self.ctx), self.max_ctx, self.B, self.T, self.page_rows,
+                                   self.opt_pool_pages, self.staging_rows, self.row_bytes)
         if not self._h:
             raise ValueError("ora_create rejected the shape")
 
@@ -124,6 +131,13 @@ class Source:
     def residency_set(self, r: int, page_ids) -> int:
         ids = np.ascontiguousarray(np.asarray(page_ids, dtype=np.int32))
         return int(lib().ora_residency_set(self._h, int(r), _p(ids), ids.size))
+
+    def append(self, count: int) -> int:
+        """Every request's next `count` rows join the context through the tail (HiSparse 3.3 step 4)."""
+        return int(lib().ora_append(self._h, int(count)))
+
+    def context_rows(self, r: int) -> int:
+        return int(lib().ora_context_rows(self._h, int(r)))
 
     def resolve(self, epoch: int, sel: np.ndarray, nq=None) -> dict:
         """sel int32 [R][Qmax][k].  Returns locs, cls, stats, plan (per request: positions and pool rows in
@@ -150,12 +164,12 @@ class Source:
         return out
 
     def snapshot(self, r: int) -> dict:
-        n = int(self.ctx[r])
+        n = self.context_rows(r)
         key = np.zeros(self.B, np.int32)
         rec = np.zeros(self.B, np.uint32)
         order = np.zeros(self.B, np.int32)
         pt = np.zeros(n, np.int32)
-        opt = np.zeros(max(1, n // self.page_rows) if self.page_rows else 1, np.int32)
+        opt = np.zeros(max(1, int(self.ctx[r]) // self.page_rows) if self.page_rows else 1, np.int32)
         lib().ora_snapshot(self._h, int(r), _p(key), _p(rec), _p(order), _p(pt), _p(opt))
         if not self.page_rows:
             opt = np.zeros(0, np.int32)
@@ -200,6 +214,14 @@ def bf16_from_f64(x) -> np.ndarray:
 def reclaim_plan(pages_held, deficit: int) -> int:
     a = np.ascontiguousarray(np.asarray(pages_held, dtype=np.int64))
     return int(lib().ora_reclaim_plan(_p(a), a.size, int(deficit)))
+
+
+def completed_rows(n_before: int, n_after: int, m: int):
+    """Adaptive DHiSparse Eq. 8: (first, count) of the packed rows a round completes, or None if invalid."""
+    first, count = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().ora_completed_rows(int(n_before), int(n_after), int(m), ctypes.addressof(first),
+                                  ctypes.addressof(count))
+    return None if rc else (first.value, count.value)
 
 
 def ring_rows(window: int, page_rows: int, k_max: int) -> int:

@@ -28,7 +28,9 @@
 struct ora_source {
   int32_t R, B, T, P, S, row_bytes;
   int64_t opt_pool_pages;
-  int64_t* ctx;       /* [R] */
+  int64_t* ctx;       /* [R] rows of the context, grown by appends */
+  int64_t* n_import;  /* [R] imported history (context at creation) */
+  int64_t max_ctx;    /* rows reserved per request */
   int32_t* key;       /* [R][B] position held by a hot slot, -1 = empty */
   uint32_t* rec;      /* [R][B] recency stamp, 0 = empty */
   int32_t** pt;       /* [R] -> [ctx_r] page table: hot slot of a position or -1 */
@@ -51,32 +53,36 @@ static int64_t stg_loc(const ora_source* s, int32_t r, int64_t c) {
 }
 static int64_t pool_tag(int32_t r, int64_t p) { return ((int64_t)r << 32) | p; }
 
-ora_source* ora_create(int32_t R, const int64_t* ctx, int32_t B, int32_t T, int32_t page_rows,
+ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B, int32_t T, int32_t page_rows,
                        int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes) {
   if (R <= 0 || B <= 0 || T < 0 || page_rows < 0 || opt_pool_pages < 0 || staging_rows < 0) return NULL;
+  if (max_ctx <= 0 || max_ctx > 0x7fffffff) return NULL;
   if (page_rows == 0 && opt_pool_pages != 0) return NULL;
   ora_source* s = (ora_source*)calloc(1, sizeof(ora_source));
   if (!s) return NULL;
   s->R = R; s->B = B; s->T = T; s->P = page_rows; s->S = staging_rows; s->row_bytes = row_bytes;
   s->opt_pool_pages = opt_pool_pages;
+  s->max_ctx = max_ctx;
   s->ctx = (int64_t*)malloc(sizeof(int64_t) * R);
+  s->n_import = (int64_t*)malloc(sizeof(int64_t) * R);
   s->key = (int32_t*)malloc(sizeof(int32_t) * (size_t)R * B);
   s->rec = (uint32_t*)calloc((size_t)R * B, sizeof(uint32_t));
   s->pt = (int32_t**)calloc(R, sizeof(int32_t*));
   s->opt = (int32_t**)calloc(R, sizeof(int32_t*));
   s->pool_rows = (int64_t)R * B + (int64_t)R * T + opt_pool_pages * page_rows + (int64_t)R * staging_rows;
   s->pool = (int64_t*)malloc(sizeof(int64_t) * (size_t)s->pool_rows);
-  if (!s->ctx || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
+  if (!s->ctx || !s->n_import || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
   for (int64_t i = 0; i < s->pool_rows; ++i) s->pool[i] = -1;
   for (int64_t i = 0; i < (int64_t)R * B; ++i) s->key[i] = -1;
   for (int32_t r = 0; r < R; ++r) {
     s->ctx[r] = ctx[r];
-    if (ctx[r] <= 0 || ctx[r] > 0x7fffffff) { ora_destroy(s); return NULL; }
-    s->pt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)ctx[r]);
+    s->n_import[r] = ctx[r];
+    if (ctx[r] <= 0 || ctx[r] > max_ctx) { ora_destroy(s); return NULL; }
+    s->pt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)max_ctx);
     int64_t np = page_rows ? ctx[r] / page_rows : 0;
     s->opt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1));
     if (!s->pt[r] || !s->opt[r]) { ora_destroy(s); return NULL; }
-    for (int64_t p = 0; p < ctx[r]; ++p) s->pt[r][p] = -1;
+    for (int64_t p = 0; p < max_ctx; ++p) s->pt[r][p] = -1;
     for (int64_t g = 0; g < np; ++g) s->opt[r][g] = -1;
   }
   return s;
@@ -86,7 +92,7 @@ void ora_destroy(ora_source* s) {
   if (!s) return;
   if (s->pt) for (int32_t r = 0; r < s->R; ++r) free(s->pt[r]);
   if (s->opt) for (int32_t r = 0; r < s->R; ++r) free(s->opt[r]);
-  free(s->pt); free(s->opt); free(s->ctx); free(s->key); free(s->rec); free(s->pool); free(s);
+  free(s->pt); free(s->opt); free(s->ctx); free(s->n_import); free(s->key); free(s->rec); free(s->pool); free(s);
 }
 
 int64_t ora_pool_rows(const ora_source* s) { return s->pool_rows; }
@@ -104,7 +110,7 @@ void ora_commit_prefill(ora_source* s) {
  * and publishes its ready location afterwards, reclaim drops the location (-1). */
 int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int64_t n_pages) {
   if (r < 0 || r >= s->R || s->P == 0) return ORA_EINVAL;
-  int64_t complete = s->ctx[r] / s->P;
+  int64_t complete = s->n_import[r] / s->P;
   if (n_pages < 0 || n_pages > complete) return ORA_EINVAL;
   for (int64_t g = 0; g < n_pages; ++g)
     if (page_ids[g] < -1 || page_ids[g] >= s->opt_pool_pages) return ORA_EINVAL;
@@ -113,6 +119,41 @@ int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int
     if (page_ids[g] >= 0)
       for (int64_t i = 0; i < s->P; ++i) s->pool[opt_loc(s, page_ids[g], g * s->P + i)] = pool_tag(r, g * s->P + i);
   }
+  return ORA_OK;
+}
+
+/* [HS] 3.3 step 4 and [AD] 3.2: each request's next `count` rows become positions n_r .. n_r + count - 1,
+ * produced into the tail (the newest rows are always resident); the rows that leave the tail become
+ * history, reachable through the hot cache from their written-through host copies.  Appends are
+ * bounded by the reserved rows, and a row stays in the tail across the next append (2 count <= T), the
+ * window in which its host copy completes. */
+int32_t ora_append(ora_source* s, int32_t count) {
+  if (count < 1 || 2 * (int64_t)count > s->T) return ORA_EINVAL;
+  for (int32_t r = 0; r < s->R; ++r)
+    if (s->ctx[r] + count > s->max_ctx) return ORA_EINVAL;
+  for (int32_t r = 0; r < s->R; ++r) {
+    for (int32_t i = 0; i < count; ++i) {
+      const int64_t p = s->ctx[r] + i;
+      s->pool[tail_loc(s, r, p)] = pool_tag(r, p);
+    }
+    s->ctx[r] += count;
+  }
+  return ORA_OK;
+}
+
+int64_t ora_context_rows(const ora_source* s, int32_t r) { return s->ctx[r]; }
+
+/* [AD] Eq. 8: a source packing m token positions per stored row completes, when a request's tokens grow from
+ * n to n2, the rows s with floor(n/m) <= s < floor(n2/m) (reading: the upper bound is floored as the lower
+ * one, since an incomplete last row stays in the tail until it is complete). */
+int32_t ora_completed_rows(int64_t n, int64_t n2, int32_t m, int64_t* first, int64_t* count) {
+  if (m < 1 || n < 0 || n2 < n) return ORA_EINVAL;
+  int64_t lo = 0, hi = 0;
+  while ((lo + 1) * m <= n) ++lo;      /* floor(n / m), counted out */
+  hi = lo;
+  while ((hi + 1) * m <= n2) ++hi;     /* floor(n2 / m) */
+  *first = lo;
+  *count = hi - lo;
   return ORA_OK;
 }
 
@@ -158,7 +199,8 @@ static void resolve_request(ora_source* s, int32_t r, uint32_t e, const int32_t*
     if (s->T > 0 && p >= n - s->T) {
       klass[f] = ORA_CLS_TAIL;
       locs[f] = (int32_t)tail_loc(s, r, p);
-    } else if (s->P > 0 && p / s->P < n / s->P && s->opt[r][p / s->P] >= 0) {
+    } else if (s->P > 0 && p / s->P < s->n_import[r] / s->P && s->opt[r][p / s->P] >= 0) {
+      /* only complete pages of the imported history are optional ([AD] 3.1); decoded rows are not */
       klass[f] = ORA_CLS_OPT;
       locs[f] = (int32_t)opt_loc(s, s->opt[r][p / s->P], p);
     }
@@ -296,7 +338,7 @@ void ora_snapshot(const ora_source* s, int32_t r, int32_t* key, uint32_t* rec, i
     free(all);
   }
   if (pt) memcpy(pt, s->pt[r], sizeof(int32_t) * (size_t)s->ctx[r]);
-  if (opt && s->P > 0) memcpy(opt, s->opt[r], sizeof(int32_t) * (size_t)(s->ctx[r] / s->P));
+  if (opt && s->P > 0) memcpy(opt, s->opt[r], sizeof(int32_t) * (size_t)(s->n_import[r] / s->P));
 }
 
 void ora_pool_lookup(const ora_source* s, const int32_t* locs, int64_t n, int64_t* out) {

@@ -51,7 +51,7 @@ typedef struct ora_source ora_source;
 /* One payload source: R requests, each with B hot slots, T tail rows, an optional-history page map over
  * its complete pages, and staging_rows staging rows; opt_pool_pages optional pages shared by the source.
  * Pool row layout: [R*B hot][R*T tail][opt_pool_pages*page_rows optional][R*staging_rows staging]. */
-ora_source* ora_create(int32_t R, const int64_t* ctx, int32_t B, int32_t T, int32_t page_rows,
+ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B, int32_t T, int32_t page_rows,
                        int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes);
 void ora_destroy(ora_source* s);
 int64_t ora_pool_rows(const ora_source* s);
@@ -60,6 +60,9 @@ int64_t ora_pool_rows(const ora_source* s);
 void ora_commit_prefill(ora_source* s);
 /* map entries for complete pages [0, n_pages) of request r: page id in the optional pool, or -1 */
 int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int64_t n_pages);
+int32_t ora_append(ora_source* s, int32_t count);
+int64_t ora_context_rows(const ora_source* s, int32_t r);
+int32_t ora_completed_rows(int64_t n, int64_t n2, int32_t m, int64_t* first, int64_t* count);
 
 /* One resolve call over sel[R][Qmax][k] (query j of request r uses its first k entries when j < nq[r]).
  * Outputs (all may be NULL except locs and stats):
