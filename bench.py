@@ -436,6 +436,88 @@ def run_adaptive(hsk, synth, w, steps: int) -> dict:
             "host_fetch_fraction_after_reclaim": float(np.mean(after)), "per_step": per_step, "status": status}
 
 
+def run_decode(hsk, synth, w, steps: int) -> dict:
+    """The 100K batch-64 shape as a decode loop (HiSparse section 3.3 steps 3-4): per layer, each request
+    appends the new token's row (tail ring on the main stream, write-through to host on a backup stream),
+    then its selection (which includes the new row) is resolved and attended.  Reports steps/s and the
+    append and write-through kernel times beside the resolve and attention calls."""
+    import torch
+    R, k, L = w.requests, w.top_k, w.layers
+    st = hsk.KVStore(requests=R, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
+                     tail_rows=w.tail_rows, ctx=w.ctx, max_ctx=w.ctx + steps, max_queries=1, top_k=k)
+    t0 = time.perf_counter()
+    for s_ in range(w.sources):
+        for r in range(R):
+            synth.fill_kv_rows(st.host_ptr(s_, r), w, s_, r, 0, w.ctx)
+    st.commit_prefill()
+    log(f"[decode] host rows filled in {time.perf_counter() - t0:.1f} s")
+    # selections over the growing context: the stream of the fixed-length run, plus the newest row
+    sels = []
+    for l in range(L):
+        sl = synth.selection_stream(w, l, steps=steps)
+        for t in range(steps):
+            sl[t, :, 0, 0] = w.ctx + t          # the row appended at step t
+        sels.append(torch.from_numpy(sl).cuda())
+    rows = [[torch.from_numpy(np.stack([synth.kv_rows(w, l, r, w.ctx + t, 1) for r in range(R)]).view(np.int16))
+             .cuda() for t in range(steps)] for l in range(L)]
+    ad = hsk.mla_desc(requests=R, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k, row_elems=w.row_elems,
+                      scale=w.scale)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    q = [torch.from_numpy(synth.queries(w, l, 0).view(np.int16)).cuda() for l in range(L)]
+    out = torch.empty((R, 1, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    locs = torch.empty((R, 1, k), dtype=torch.int32, device="cuda")
+    stats = hsk.stats_tensor(R)
+    pools = [st.pool_base(l) for l in range(L)]
+    main, backup = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def step(t, evs=None):
+        for l in range(L):
+            if evs is not None:
+                e = [_ev() for _ in range(4)]
+                e[0].record(main)
+            st.append_rows(l, rows[l][t], 1, stream=main, backup_stream=backup)
+            if evs is not None:
+                e[1].record(main)
+            st.resolve_step(l, t + 1, sels[l][t], locs, stats)
+            if evs is not None:
+                e[2].record(main)
+            hsk.sparse_decode_attn(ad, q[l], pools[l], locs, None, out, scratch, nb)
+            if evs is not None:
+                e[3].record(main)
+                evs.append(e)
+
+    # warm-up, a throughput pass with no events between the calls, then a pass with events
+    warm, half = 2, (steps - 2) // 2
+    for t in range(warm):
+        step(t)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for t in range(warm, warm + half):
+        step(t)
+    torch.cuda.synchronize()
+    t_all = time.perf_counter() - t1
+    evs = []
+    for t in range(warm + half, steps):
+        step(t, evs)
+    torch.cuda.synchronize()
+    app_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    res_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    att_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    timed = half
+    status = st.sync_status()
+    tail_ok = all(st.context_rows(l, r) == w.ctx + steps for l in range(L) for r in range(R))
+    st.close()
+    return {"workload": f"decode: {R} requests x 1 query, {L} layers with own payloads, context {w.ctx} growing by "
+                        f"one row per step, B={w.hot_slots}, tail {w.tail_rows}, top-k {k} (the newest row "
+                        f"always selected)", "steps_timed": timed,
+            "rows_per_s": R * k * L * timed / t_all, "steps_per_s": timed / t_all,
+            "append_call_ms": float(np.mean(app_ms)), "resolve_ms": float(np.mean(res_ms)),
+            "attention_ms": float(np.mean(att_ms)), "context_grew": tail_ok, "status": status,
+            "note": "append_call_ms covers the tail write on the main stream (event to event); the write-through "
+                    "runs on a backup stream beside the following calls"}
+
+
 def run_quest(hsk, synth, w, steps: int) -> dict:
     """Page-level GQA: layer 0 resolves the shared page selection; layers 1..7 replay its miss plan on a side
     stream while the previous layer's attention runs (HiSparse section 3.5)."""
@@ -527,7 +609,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the hits-only, misses-only and memcpy runs")
-    ap.add_argument("--workload", default="dsa100k", choices=["dsa100k", "verify", "adaptive", "quest"])
+    ap.add_argument("--workload", default="dsa100k", choices=["dsa100k", "verify", "adaptive", "quest", "decode"])
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
@@ -558,10 +640,10 @@ def main() -> int:
     import hierarchical_sparse_kv_layer_amd as hsk
     import synth
 
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS["dsa100k" if args.workload == "decode" else args.workload]
     if args.workload != "dsa100k":
         torch.cuda.set_device(0)
-        fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest}[args.workload]
+        fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest, "decode": run_decode}[args.workload]
         steps = args.steps if args.steps != 32 else w.steps
         print(json.dumps(fn(hsk, synth, w, steps)), flush=True)
         return 0
