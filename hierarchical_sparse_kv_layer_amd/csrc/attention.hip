@@ -200,7 +200,13 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   const int nrows = max(0, min(a.k, i0 + a.rows_per_split) - i0);
   const int ntiles = (nrows + kTile - 1) / kTile;
   const int hbase = hgrp * (HW * NPAIR) + pair * HW;
-  const int my_dma = (kDmaPerTile - wave + NW - 1) / NW;
+  // Tile loads: NWD waves issue them, dw is this wave's index among them (negative: none).  The fused kernel
+  // with eight waves gives them to waves 4-7 and its pool write-backs to waves 0-1, so the loading waves'
+  // memory counter counts only loads and two tiles can be in flight, as in the plain kernel.
+  constexpr bool kSplitRoles = FUSED && NW == 8;
+  constexpr int NWD = kSplitRoles ? 4 : NW;
+  const int dw = kSplitRoles ? wave - 4 : wave;
+  const int my_dma = dw < 0 ? 0 : (kDmaPerTile - dw + NWD - 1) / NWD;
 
   const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
   for (int x = tid; x < nrows; x += NT) {
@@ -233,14 +239,14 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   int v_base[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) v_base[w] = tile_off(t1, 32 * half + 2 * w + (q4 >> 1)) + (q4 & 1) * 8;
-  // DMA: wave-wide load i (i = wave + NW u) covers tile rows 8 (i & 3) .. + 7 and chunk group i >> 2; a lane
-  // copies 16 bytes of one row: with 4 or more waves every load of a wave uses the same rows (NTOK = 1),
-  // with 2 waves the loads alternate between two rows.
-  constexpr int NTOK = NW >= 4 ? 1 : 2;
+  // DMA: wave-wide load i (i = dw + NWD u) covers tile rows 8 (i & 3) .. + 7 and chunk group i >> 2; a
+  // lane copies 16 bytes of one row: with 4 or more loading waves every load of a wave uses the same rows
+  // (NTOK = 1), with 2 the loads alternate between two rows.
+  constexpr int NTOK = NWD >= 4 ? 1 : 2;
   const uint32_t lds_tile0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
   auto issue = [&](int T, int b) {
     const int tb = T * kTile;
-    const uint32_t lbase = lds_tile0 + b * kTileBytes + wave * 1024;
+    const uint32_t lbase = lds_tile0 + b * kTileBytes + dw * 1024;
     // the row and lane offset are recomputed from the lane id at every issue (a few VALU operations) rather
     // than kept live across the loop, where registers are short
     // (volatile, so that the compiler cannot hoist it and its uses out of the loop again)
@@ -249,8 +255,8 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     const char* rp[NTOK];
 #pragma unroll
     for (int v = 0; v < NTOK; ++v) {
-      const int tok = 8 * ((wave + NW * v) & 3) + (ln >> 3);
-      const int sw = (((ln & 7) ^ tile_swz(tok)) << 4) + (NW >= 4 ? (wave >> 2) * 128 : 0);
+      const int tok = 8 * ((dw + NWD * v) & 3) + (ln >> 3);
+      const int sw = (((ln & 7) ^ tile_swz(tok)) << 4) + (NWD >= 4 ? (dw >> 2) * 128 : 0);
       const int x = tb + tok < nrows ? tb + tok : 0;   // rows past the end re-read row 0 (masked)
       const int32_t loc = s_loc[x];
       if (FUSED && s_fill[x] >= 0) {
@@ -261,13 +267,13 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < (kDmaPerTile + NW - 1) / NW; ++u) {
-      if (wave + NW * u < kDmaPerTile) {
+    for (int u = 0; u < (kDmaPerTile + NWD - 1) / NWD; ++u) {
+      if (dw + NWD * u < kDmaPerTile) {
         // the instruction's immediate offset would also move the LDS destination, so the row offset of
         // the chunk group goes into the address register
-        constexpr int kStep = NW >= 4 ? (NW / 4) * 128 : 0;
-        const uint32_t m0 = lbase + NW * u * 1024;
-        const char* src = NW >= 4 ? rp[0] + kStep * u : rp[u % NTOK] + (u >> 1) * 128;
+        constexpr int kStep = NWD >= 4 ? (NWD / 4) * 128 : 0;
+        const uint32_t m0 = lbase + NWD * u * 1024;
+        const char* src = NWD >= 4 ? rp[0] + kStep * u : rp[u % NTOK] + (u >> 1) * 128;
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
       }
     }
@@ -409,10 +415,21 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     }
   };
 
-  if (ntiles > 0) issue(0, 0);
-  if (!FUSED && ntiles > 1) issue(1, 1);
+  if (dw >= 0) {
+    if (ntiles > 0) issue(0, 0);
+    if ((!FUSED || kSplitRoles) && ntiles > 1) issue(1, 1);
+  }
   for (int T = 0; T < ntiles; ++T) {
-    if (FUSED) {
+    if (kSplitRoles) {
+      // loading waves wait for their loads of tile T (tile T + 1 may stay in flight); the others have only
+      // stores outstanding and need not wait for them
+      if (dw >= 0) {
+        if (T + 1 < ntiles) wait_tile_barrier_n(my_dma); else wait_tile_barrier<0>();
+        if (T + 2 < ntiles) issue(T + 2, (T + 2) % kBufs);
+      } else {
+        lds_barrier();
+      }
+    } else if (FUSED) {
       wait_tile_barrier<0>();
       if (T + 1 < ntiles) issue(T + 1, (T + 1) % kBufs);
     } else {
