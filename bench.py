@@ -295,8 +295,11 @@ def run_verify(hsk, synth, w, steps: int) -> dict:
     and unions beyond the free hot slots go to staging rows (Adaptive DHiSparse section 3.3)."""
     import torch
     R, Q, k, L = w.requests, w.queries, w.top_k, w.layers
+    # the layers run one after another, so one staging arena serves them all (Adaptive DHiSparse section 3.4)
     st = hsk.KVStore(requests=R, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
-                     tail_rows=w.tail_rows, ctx=w.ctx, max_queries=Q, top_k=k, staging_rows=w.staging_rows)
+                     tail_rows=w.tail_rows, ctx=w.ctx, max_queries=Q, top_k=k, staging_rows=w.staging_rows,
+                     staging_arenas=1)
+    staging_gib = R * w.staging_rows * w.row_bytes / 2 ** 30
     t0 = time.perf_counter()
     for s_ in range(w.sources):
         for r in range(R):
@@ -350,7 +353,9 @@ def run_verify(hsk, synth, w, steps: int) -> dict:
             "attention_ms": att, "attention_TFLOPs": flops / (att * 1e-3) / 1e12,
             "attention_frac_mfma_bf16": flops / (att * 1e-3) / 2.5e15,
             "dedup_ratio": agg["miss_sel"] / max(1, agg["miss"]), "fetched_fraction": agg["miss"] / agg["sel"],
-            "staged_rows_per_layer_step": agg["staged"] / (L * (steps - 1)), "status": status}
+            "staged_rows_per_layer_step": agg["staged"] / (L * (steps - 1)),
+            "staging_GiB": {"one_shared_arena": staging_gib, "one_arena_per_layer": staging_gib * w.sources},
+            "status": status}
 
 
 def run_adaptive(hsk, synth, w, steps: int) -> dict:

@@ -36,7 +36,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("num_requests", _i32), ("num_sources", _i32), ("row_bytes", _i32), ("hot_slots", _i32),
                 ("tail_rows", _i32), ("page_rows", _i32), ("opt_pool_pages", _i64), ("max_queries", _i32),
                 ("top_k", _i32), ("staging_rows", _i32), ("host_alias_sources", _i32), ("max_ctx", _i64),
-                ("ctx_len", _vp), ("gather_mode", _i32), ("gather_blocks", _i32)]
+                ("ctx_len", _vp), ("gather_mode", _i32), ("gather_blocks", _i32), ("staging_arenas", _i32)]
 
 
 class AttnDesc(ctypes.Structure):
@@ -244,7 +244,7 @@ class KVStore:
     def __init__(self, *, requests: int, sources: int, row_bytes: int, hot_slots: int, tail_rows: int, ctx,
                  max_ctx: Optional[int] = None, page_rows: int = 0, opt_pool_pages: int = 0, max_queries: int = 1,
                  top_k: int, staging_rows: int = 0, host_alias: bool = False, gather_mode: int = GATHER_ZEROCOPY,
-                 gather_blocks: int = 0, device: str = "cuda", stream=None):
+                 gather_blocks: int = 0, staging_arenas: int = 0, device: str = "cuda", stream=None):
         import torch
         self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, np.int64), (requests,)))
         self.desc = Desc(num_requests=requests, num_sources=sources, row_bytes=row_bytes, hot_slots=hot_slots,
@@ -252,7 +252,8 @@ class KVStore:
                          max_queries=max_queries, top_k=top_k, staging_rows=staging_rows,
                          host_alias_sources=1 if host_alias else 0,
                          max_ctx=int(max_ctx if max_ctx is not None else self.ctx.max()),
-                         ctx_len=self.ctx.ctypes.data, gather_mode=gather_mode, gather_blocks=gather_blocks)
+                         ctx_len=self.ctx.ctypes.data, gather_mode=gather_mode, gather_blocks=gather_blocks,
+                         staging_arenas=staging_arenas)
         ws, pool = workspace_bytes(self.desc)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.pool = torch.empty(pool, dtype=torch.uint8, device=device)
@@ -260,8 +261,9 @@ class KVStore:
         self.R, self.S, self.B, self.T = requests, sources, hot_slots, tail_rows
         self.row_bytes, self.page_rows, self.max_queries, self.top_k = row_bytes, page_rows, max_queries, top_k
         self.staging_rows, self.opt_pool_pages = staging_rows, opt_pool_pages
+        self.staging_arenas = staging_arenas
         self.rows_per_source = requests * hot_slots + requests * tail_rows + opt_pool_pages * page_rows + \
-            requests * staging_rows
+            (0 if staging_arenas else requests * staging_rows)
 
     def host_rows(self, source: int, req: int) -> np.ndarray:
         """The pinned host rows of (source, req) as a writable uint8 array [max_ctx, row_bytes]."""
@@ -299,9 +301,10 @@ class KVStore:
         return pool_base(self.handle, source)
 
     def pool_rows(self, source: int):
-        """torch uint8 view [rows_per_source, row_bytes] of a source's pool region."""
+        """torch uint8 view [rows, row_bytes] from a source's pool base to the end of the pool: the rows its
+        locations index (its own region, and the shared staging arenas after the last region)."""
         off = source * self.rows_per_source * self.row_bytes
-        return self.pool[off: off + self.rows_per_source * self.row_bytes].view(self.rows_per_source, self.row_bytes)
+        return self.pool[off:].view(-1, self.row_bytes)
 
     def snapshot(self, source: int, req: int) -> dict:
         return snapshot(self.handle, source, req, self.B, self.context_rows(source, req), self.page_rows,

@@ -41,6 +41,8 @@ struct WorkspaceLayout {
 
 bool layout_workspace(const hsk_desc& d, WorkspaceLayout* out);
 int64_t rows_per_source(const hsk_desc& d);
+int64_t total_pool_rows(const hsk_desc& d);
+int64_t stg_base_of(const hsk_desc& d, int32_t source);
 
 struct ResolveArgs {
   const int32_t* sel;

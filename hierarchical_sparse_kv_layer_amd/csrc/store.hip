@@ -17,9 +17,23 @@ namespace hsk {
 
 static int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+int64_t total_pool_rows(const hsk_desc& d) {
+  return rows_per_source(d) * d.num_sources +
+         (d.staging_arenas ? (int64_t)d.staging_arenas * d.num_requests * d.staging_rows : 0);
+}
+
+// first staging row of a source, relative to the source's region
+int64_t stg_base_of(const hsk_desc& d, int32_t source) {
+  const int64_t R = d.num_requests;
+  if (!d.staging_arenas) return R * d.hot_slots + R * d.tail_rows + d.opt_pool_pages * d.page_rows;
+  const int64_t P = rows_per_source(d);
+  return P * d.num_sources + (int64_t)(source % d.staging_arenas) * R * d.staging_rows - (int64_t)source * P;
+}
+
+// rows of one source region (staging included only without shared arenas)
 int64_t rows_per_source(const hsk_desc& d) {
   return (int64_t)d.num_requests * d.hot_slots + (int64_t)d.num_requests * d.tail_rows +
-         d.opt_pool_pages * d.page_rows + (int64_t)d.num_requests * d.staging_rows;
+         d.opt_pool_pages * d.page_rows + (d.staging_arenas ? 0 : (int64_t)d.num_requests * d.staging_rows);
 }
 
 static bool valid_desc(const hsk_desc* d) {
@@ -36,7 +50,8 @@ static bool valid_desc(const hsk_desc* d) {
   if (d->gather_blocks < 0 || d->host_alias_sources < 0 || d->host_alias_sources > 1) return false;
   for (int32_t r = 0; r < d->num_requests; ++r)
     if (d->ctx_len[r] < 1 || d->ctx_len[r] > d->max_ctx) return false;
-  if (rows_per_source(*d) > 0x7fffffffLL) return false;  // locations are int32 rows
+  if (d->staging_arenas < 0 || d->staging_arenas > d->num_sources) return false;
+  if (total_pool_rows(*d) > 0x7fffffffLL) return false;  // locations are int32 rows
   return true;
 }
 
@@ -91,7 +106,7 @@ hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, si
   WorkspaceLayout L;
   layout_workspace(*desc, &L);
   *workspace_bytes = (size_t)L.total;
-  *pool_bytes = (size_t)rows_per_source(*desc) * desc->num_sources * desc->row_bytes;
+  *pool_bytes = (size_t)total_pool_rows(*desc) * desc->row_bytes;
   return HSK_OK;
 }
 
@@ -307,7 +322,7 @@ static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, c
   a.err = st->d_err; a.fill = nullptr; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
   const int64_t R = st->d.num_requests;
   a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
-  a.stg_base = a.opt_base + st->d.opt_pool_pages * st->d.page_rows;
+  a.stg_base = stg_base_of(st->d, source);
   a.plan_cap = st->plan_cap;
   a.R = st->d.num_requests; a.B = st->d.hot_slots; a.T = st->d.tail_rows; a.P = st->d.page_rows;
   a.S = st->d.staging_rows; a.Qmax = st->d.max_queries; a.k = st->d.top_k; a.row_bytes = st->d.row_bytes;
@@ -419,6 +434,7 @@ hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_sourc
   if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
       dst_source >= st->d.num_sources)
     return HSK_EINVAL;
+  if (st->d.staging_arenas && st->d.staging_rows) return HSK_EINVAL;
   if (st->d.gather_mode != HSK_GATHER_ZEROCOPY) return HSK_OK;
   void* pool;
   hsk_pool_base(st, dst_source, &pool);

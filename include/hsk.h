@@ -67,11 +67,16 @@ enum { HSK_GATHER_ZEROCOPY = 0, HSK_GATHER_NO_IO = 1 };
  *
  * Per source and request the device pool holds B hot slots, T tail rows and S staging rows; each source
  * also has an optional-history pool of opt_pool_pages pages of page_rows rows.  Pool row layout of one
- * source (row indices are what hsk_resolve_step emits):
+ * source (row indices are what hsk_resolve_step emits, relative to hsk_pool_base of the source):
  *     hot      r*B + slot                                   r < R, slot < B
  *     tail     R*B + r*T + (p mod T)                        positions p >= n_r - T
  *     optional R*B + R*T + g*page_rows + (p mod page_rows)  page id g of a ready complete page
- *     staging  R*B + R*T + opt_pool_pages*page_rows + r*S + c
+ *     staging  R*B + R*T + opt_pool_pages*page_rows + r*S + c            (staging_arenas = 0)
+ * With staging_arenas = A > 0 the sources share A staging arenas (Adaptive DHiSparse section 3.4: one arena
+ * per simultaneously live source, reused by the next layer group once its readers are done): the source
+ * regions hold no staging rows, the A arenas of R*S rows follow the last source region, and source s stages
+ * into arena s mod A, at relative rows  NS*P_s + (s mod A)*R*S + r*S + c - s*P_s  (P_s = rows of one source
+ * region, NS = num_sources).  Sources sharing an arena must be resolved and read in stream order.
  */
 typedef struct hsk_desc {
   int32_t num_requests;        /* R: resolution units (requests, or request x KV head for GQA pages) */
@@ -90,6 +95,7 @@ typedef struct hsk_desc {
                                   1 <= n_r <= max_ctx, n_r < 2^31; hsk_append_rows grows it per source */
   int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
   int32_t gather_blocks;       /* workgroups (of 4 waves) of the gather kernel; 0 = automatic (384) */
+  int32_t staging_arenas;      /* 0: staging inside each source region; A >= 1: A arenas shared by the sources */
 } hsk_desc;
 
 /* Per-request result of one resolve call (device memory, written by hsk_resolve_step). */
@@ -189,7 +195,8 @@ hsk_status hsk_context_rows(hsk_store* store, int32_t source, int32_t req, int64
 hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int64_t* first, int64_t* count);
 
 /* Plan replay (HiSparse section 3.5, plan-then-IO): copy the rows listed in plan_source's last miss plan
- * from dst_source's host rows into dst_source's pool, at the same pool rows.  A layer that shares its
+ * from dst_source's host rows into dst_source's pool, at the same pool rows (EINVAL for a store with shared
+ * staging arenas and staging rows, whose staged rows are not at the same relative rows).  A layer that shares its
  * anchor's selection then reads its own payload at the anchor's locations.  Order it after the anchor's
  * resolve and before the consumer's attention with events when it runs on a side stream. */
 hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_source, hsk_stream_t stream);

@@ -56,7 +56,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is missing: run __graft_entry__.build() first")
         L = ctypes.CDLL(LIB_PATH)
         i32, i64, u32, vp, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double
-        L.ora_create.argtypes = [i32, vp, i64, i32, i32, i32, i64, i32, i32]
+        L.ora_create.argtypes = [i32, vp, i64, i32, i32, i32, i64, i32, i32, i64]
         L.ora_create.restype = vp
         L.ora_destroy.argtypes = [vp]
         L.ora_destroy.restype = None
@@ -104,14 +104,17 @@ class Source:
     """One payload source: R requests' hot caches (B slots), tails (T rows), optional-history page maps
     and staging rows, with a pool model of which host row each pool row holds."""
 
-    def __init__(self, R, ctx, B, T, page_rows=0, opt_pool_pages=0, staging_rows=0, row_bytes=1152, max_ctx=None):
+    def __init__(self, R, ctx, B, T, page_rows=0, opt_pool_pages=0, staging_rows=0, row_bytes=1152, max_ctx=None,
+                 stg_base=-1):
+        """stg_base: first staging row relative to the source's pool rows when staging is an arena shared
+        with other sources (-1: right after the optional pages)."""
         self.R, self.B, self.T = int(R), int(B), int(T)
         self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, dtype=np.int64), (self.R,)))
         self.max_ctx = int(self.ctx.max() if max_ctx is None else max_ctx)
         self.page_rows, self.opt_pool_pages, self.staging_rows = int(page_rows), int(opt_pool_pages), int(staging_rows)
         self.row_bytes = int(row_bytes)
         self._h = lib().ora_create(self.R, _p(self.ctx), self.max_ctx, self.B, self.T, self.page_rows,
-                                   self.opt_pool_pages, self.staging_rows, self.row_bytes)
+                                   self.opt_pool_pages, self.staging_rows, self.row_bytes, int(stg_base))
         if not self._h:
             raise ValueError("ora_create rejected the shape")
 

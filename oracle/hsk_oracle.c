@@ -36,6 +36,7 @@ struct ora_source {
   int32_t** pt;       /* [R] -> [ctx_r] page table: hot slot of a position or -1 */
   int32_t** opt;      /* [R] -> [ctx_r / P] optional page id of a complete page or -1 */
   uint32_t last_epoch;
+  int64_t stg_base;   /* first staging row, relative to the source's pool rows */
   int64_t pool_rows;
   int64_t* pool;      /* [pool_rows] pool model: r * 2^32 + position, or -1 */
 };
@@ -48,13 +49,11 @@ static int64_t tail_loc(const ora_source* s, int32_t r, int64_t p) {
 static int64_t opt_loc(const ora_source* s, int64_t page_id, int64_t p) {
   return (int64_t)s->R * s->B + (int64_t)s->R * s->T + page_id * s->P + (p % s->P);
 }
-static int64_t stg_loc(const ora_source* s, int32_t r, int64_t c) {
-  return (int64_t)s->R * s->B + (int64_t)s->R * s->T + s->opt_pool_pages * s->P + (int64_t)r * s->S + c;
-}
+static int64_t stg_loc(const ora_source* s, int32_t r, int64_t c) { return s->stg_base + (int64_t)r * s->S + c; }
 static int64_t pool_tag(int32_t r, int64_t p) { return ((int64_t)r << 32) | p; }
 
 ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B, int32_t T, int32_t page_rows,
-                       int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes) {
+                       int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes, int64_t stg_base) {
   if (R <= 0 || B <= 0 || T < 0 || page_rows < 0 || opt_pool_pages < 0 || staging_rows < 0) return NULL;
   if (max_ctx <= 0 || max_ctx > 0x7fffffff) return NULL;
   if (page_rows == 0 && opt_pool_pages != 0) return NULL;
@@ -69,7 +68,11 @@ ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B
   s->rec = (uint32_t*)calloc((size_t)R * B, sizeof(uint32_t));
   s->pt = (int32_t**)calloc(R, sizeof(int32_t*));
   s->opt = (int32_t**)calloc(R, sizeof(int32_t*));
-  s->pool_rows = (int64_t)R * B + (int64_t)R * T + opt_pool_pages * page_rows + (int64_t)R * staging_rows;
+  /* staging follows the optional pages, or sits at stg_base (an arena shared by several sources, [AD] 3.4) */
+  const int64_t own = (int64_t)R * B + (int64_t)R * T + opt_pool_pages * page_rows;
+  s->stg_base = stg_base >= 0 ? stg_base : own;
+  s->pool_rows = own + (int64_t)R * staging_rows;
+  if (s->stg_base + (int64_t)R * staging_rows > s->pool_rows) s->pool_rows = s->stg_base + (int64_t)R * staging_rows;
   s->pool = (int64_t*)malloc(sizeof(int64_t) * (size_t)s->pool_rows);
   if (!s->ctx || !s->n_import || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
   for (int64_t i = 0; i < s->pool_rows; ++i) s->pool[i] = -1;

@@ -52,7 +52,7 @@ typedef struct ora_source ora_source;
  * its complete pages, and staging_rows staging rows; opt_pool_pages optional pages shared by the source.
  * Pool row layout: [R*B hot][R*T tail][opt_pool_pages*page_rows optional][R*staging_rows staging]. */
 ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B, int32_t T, int32_t page_rows,
-                       int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes);
+                       int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes, int64_t stg_base);
 void ora_destroy(ora_source* s);
 int64_t ora_pool_rows(const ora_source* s);
 

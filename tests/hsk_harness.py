@@ -27,7 +27,8 @@ def log(msg):
 
 
 class Harness:
-    def __init__(self, w: synth.Workload, steps: int | None = None, gather_blocks: int = 0, check_meta_every: int = 1):
+    def __init__(self, w: synth.Workload, steps: int | None = None, gather_blocks: int = 0, check_meta_every: int = 1,
+                 staging_arenas: int = 0):
         self.w = w
         self.steps = w.steps if steps is None else steps
         self.U = w.units
@@ -50,7 +51,8 @@ class Harness:
         self.store = hsk.KVStore(requests=self.U, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
                                  tail_rows=w.tail_rows, ctx=w.ctx, page_rows=self.page_rows,
                                  opt_pool_pages=opt_pages, max_queries=w.queries, top_k=w.top_k,
-                                 staging_rows=w.staging_rows, host_alias=w.host_alias, gather_blocks=gather_blocks)
+                                 staging_rows=w.staging_rows, host_alias=w.host_alias, gather_blocks=gather_blocks,
+                                 staging_arenas=staging_arenas)
         host_sources = 1 if w.host_alias else w.sources
         for s in range(host_sources):
             for r in range(self.U):
@@ -59,8 +61,14 @@ class Harness:
         # metadata-carrying sources: one per payload source, except that shared-selection layers replay
         # their anchor's plan and carry no state of their own
         self.meta_sources = [0] if w.shared_selection else list(range(w.sources))
+        # with shared staging arenas, source s stages into arena s mod A after the last source region
+        P = self.store.rows_per_source
+
+        def stg_base(s):
+            return w.sources * P + (s % staging_arenas) * self.U * w.staging_rows - s * P if staging_arenas else -1
         self.ora = {s: oracle.Source(R=self.U, ctx=w.ctx, B=w.hot_slots, T=w.tail_rows, page_rows=self.page_rows,
-                                     opt_pool_pages=opt_pages, staging_rows=w.staging_rows, row_bytes=w.row_bytes)
+                                     opt_pool_pages=opt_pages, staging_rows=w.staging_rows, row_bytes=w.row_bytes,
+                                     stg_base=stg_base(s))
                     for s in self.meta_sources}
         for o in self.ora.values():
             o.commit_prefill()
