@@ -65,6 +65,9 @@ _sig = {
     "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "hsk_context_rows": (_i32, [_vp, _i32, _i32, _P(_i64)]),
     "hsk_completed_rows": (_i32, [_i64, _i64, _i32, _P(_i64), _P(_i64)]),
+    "hsk_ring_rows": (_i32, [_i64, _i32, _i32, _P(_i64)]),
+    "hsk_ring_write": (_i32, [_vp, _i64, _i32, _vp, _i32, _i32, _vp, _vp]),
+    "hsk_ring_window_locs": (_i32, [_i64, _i32, _i32, _vp, _vp, _vp]),
     "hsk_pool_base": (_i32, [_vp, _i32, _P(_vp)]),
     "hsk_attn_scratch_bytes": (_i32, [_P(AttnDesc), _P(ctypes.c_size_t)]),
     "hsk_sparse_decode_attn": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -177,6 +180,22 @@ def completed_rows(n_before: int, n_after: int, m: int):
     _check(_lib.hsk_completed_rows(int(n_before), int(n_after), int(m), ctypes.byref(first), ctypes.byref(count)),
            "hsk_completed_rows")
     return first.value, count.value
+
+
+def ring_rows(window: int, page_rows: int, k_max: int) -> int:
+    n = _i64()
+    _check(_lib.hsk_ring_rows(int(window), int(page_rows), int(k_max), ctypes.byref(n)), "hsk_ring_rows")
+    return n.value
+
+
+def ring_write(ring, ring_rows: int, slots: int, rows, count: int, row_bytes: int, t0, stream=None) -> None:
+    _check(_lib.hsk_ring_write(_ptr(ring), int(ring_rows), int(slots), _ptr(rows), int(count), int(row_bytes),
+                               _ptr(t0), _stream(stream)), "hsk_ring_write")
+
+
+def ring_window_locs(ring_rows: int, slots: int, window: int, t_end, locs, stream=None) -> None:
+    _check(_lib.hsk_ring_window_locs(int(ring_rows), int(slots), int(window), _ptr(t_end), _ptr(locs),
+                                     _stream(stream)), "hsk_ring_window_locs")
 
 
 def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> None:

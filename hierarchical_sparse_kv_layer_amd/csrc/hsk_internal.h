@@ -89,6 +89,10 @@ hipError_t launch_copy_runs(const char* host, char* pool, const CopyRun* runs, i
 // decode-loop append: rows -> tail ring, context grows (stream); tail ring -> host rows (backup stream)
 hipError_t launch_append_tail(const char* rows, char* pool, int64_t* ctx, int32_t* wt_pos, int32_t R, int32_t B,
                               int32_t T, int32_t count, int32_t row_bytes, hipStream_t s);
+hipError_t launch_ring_write(char* ring, int64_t ring_rows, int32_t slots, const char* rows, int32_t count,
+                             int32_t row_bytes, const int64_t* t0, hipStream_t s);
+hipError_t launch_ring_locs(int64_t ring_rows, int32_t slots, int32_t window, const int64_t* t_end, int32_t* locs,
+                            hipStream_t s);
 hipError_t launch_write_through(const char* pool, char* host, int64_t host_req_stride, const int32_t* wt_pos,
                                 int32_t R, int32_t B, int32_t T, int32_t count, int32_t row_bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);

@@ -646,6 +646,32 @@ __global__ __launch_bounds__(kGatherThreads) void write_through_kernel(const cha
   }
 }
 
+// Draft ring (Adaptive DHiSparse Eqs. 9-10): one block per slot writes its `count` new rows to i*R_d + (t mod R_d).
+__global__ __launch_bounds__(kGatherThreads) void ring_write_kernel(char* ring, int64_t ring_rows, const char* rows,
+                                                                    int32_t count, int32_t row_bytes,
+                                                                    const int64_t* t0) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int kWaves = kGatherThreads / 64;
+  const int64_t t = t0[i];
+  for (int j = wave; j < count; j += kWaves) {
+    const u32x4* src = (const u32x4*)(rows + ((int64_t)i * count + j) * row_bytes);
+    u32x4* dst = (u32x4*)(ring + ((int64_t)i * ring_rows + (t + j) % ring_rows) * row_bytes);
+    wave_copy_row(src, dst, row_bytes >> 4, lane);
+  }
+}
+
+__global__ void ring_locs_kernel(int64_t ring_rows, int32_t slots, int32_t window, const int64_t* t_end,
+                                 int32_t* locs) {
+  const int64_t n = (int64_t)slots * window;
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = x / window, j = x % window;
+    const int64_t t = t_end[i] - window + j;
+    locs[x] = t < 0 ? -1 : (int32_t)(i * ring_rows + t % ring_rows);
+  }
+}
+
 // Contiguous byte runs host -> pool (optional-history population); one block per run.
 __global__ __launch_bounds__(kGatherThreads) void copy_runs_kernel(const char* host, char* pool, const CopyRun* runs) {
   const CopyRun run = runs[blockIdx.x];
@@ -721,6 +747,20 @@ hipError_t launch_write_through(const char* pool, char* host, int64_t stride, co
                                 int32_t B, int32_t T, int32_t count, int32_t row_bytes, hipStream_t s) {
   hipLaunchKernelGGL(write_through_kernel, dim3(R), dim3(kGatherThreads), 0, s, pool, host, stride, wt_pos, R, B, T,
                      count, row_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_write(char* ring, int64_t ring_rows, int32_t slots, const char* rows, int32_t count,
+                             int32_t row_bytes, const int64_t* t0, hipStream_t s) {
+  hipLaunchKernelGGL(ring_write_kernel, dim3(slots), dim3(kGatherThreads), 0, s, ring, ring_rows, rows, count,
+                     row_bytes, t0);
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_locs(int64_t ring_rows, int32_t slots, int32_t window, const int64_t* t_end, int32_t* locs,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(ring_locs_kernel, dim3(grid_for((int64_t)slots * window, 256)), dim3(256), 0, s, ring_rows,
+                     slots, window, t_end, locs);
   return hipGetLastError();
 }
 

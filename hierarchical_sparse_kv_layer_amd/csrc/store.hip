@@ -423,6 +423,31 @@ hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int6
   return HSK_OK;
 }
 
+hsk_status hsk_ring_rows(int64_t window, int32_t page_rows, int32_t k_max, int64_t* ring_rows) {
+  if (!ring_rows || window < 1 || page_rows < 1 || k_max < 1) return HSK_EINVAL;
+  const int64_t need = window + page_rows - 1 + k_max;     // Eq. 9
+  *ring_rows = (need + page_rows - 1) / page_rows * page_rows;
+  return HSK_OK;
+}
+
+hsk_status hsk_ring_write(void* d_ring, int64_t ring_rows, int32_t slots, const void* d_rows, int32_t count,
+                          int32_t row_bytes, const int64_t* d_t0, hsk_stream_t stream) {
+  if (!d_ring || !d_rows || !d_t0 || slots < 1 || count < 1 || ring_rows < count || row_bytes < 16 ||
+      row_bytes % 16)
+    return HSK_EINVAL;
+  HSK_HIP(launch_ring_write((char*)d_ring, ring_rows, slots, (const char*)d_rows, count, row_bytes, d_t0,
+                            (hipStream_t)stream));
+  return HSK_OK;
+}
+
+hsk_status hsk_ring_window_locs(int64_t ring_rows, int32_t slots, int32_t window, const int64_t* d_t_end,
+                                int32_t* d_locs, hsk_stream_t stream) {
+  if (!d_t_end || !d_locs || slots < 1 || window < 1 || window > ring_rows || (int64_t)slots * ring_rows > 0x7fffffffLL)
+    return HSK_EINVAL;
+  HSK_HIP(launch_ring_locs(ring_rows, slots, window, d_t_end, d_locs, (hipStream_t)stream));
+  return HSK_OK;
+}
+
 hsk_status hsk_context_rows(hsk_store* st, int32_t source, int32_t req, int64_t* n_rows) {
   if (!st || !n_rows || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests)
     return HSK_EINVAL;

@@ -194,6 +194,29 @@ hsk_status hsk_context_rows(hsk_store* store, int32_t source, int32_t req, int64
  * incomplete last row stays in the tail until it is complete. */
 hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int64_t* first, int64_t* count);
 
+/*
+ * Draft KV ring (Adaptive DHiSparse section 3.4, Eqs. 9-10).  A drafter that reads at most `window` prior
+ * positions plus its current block of at most k_max positions keeps, per request slot i, a ring of
+ *     R_d = page_rows * ceil((window + page_rows - 1 + k_max) / page_rows)      rows (Eq. 9),
+ * and draft position t of slot i lives at ring row  phi(i, t) = i * R_d + (t mod R_d)  (Eq. 10): two live
+ * positions of one slot never share a row and slots occupy disjoint ranges.  The ring is caller-owned device
+ * memory of slots * R_d rows; hsk_sparse_decode_attn over hsk_ring_window_locs is the drafter's attention.
+ */
+hsk_status hsk_ring_rows(int64_t window, int32_t page_rows, int32_t k_max, int64_t* ring_rows);
+
+/* Write `count` new draft rows of every slot: d_rows [slots][count][row_bytes] (device) go to ring rows
+ * phi(i, d_t0[i] + j), j < count, of d_ring; d_t0 int64 [slots] (device) is each slot's first new position.
+ * EINVAL for count < 1, a ring smaller than count rows, or row_bytes not a positive multiple of 16. */
+hsk_status hsk_ring_write(void* d_ring, int64_t ring_rows, int32_t slots, const void* d_rows, int32_t count,
+                          int32_t row_bytes, const int64_t* d_t0, hsk_stream_t stream);
+
+/* Locations of the window the drafter reads: d_locs int32 [slots][window] gets phi(i, d_t_end[i] - window + j),
+ * positions d_t_end[i] - window .. d_t_end[i] - 1 in order, and -1 for positions below 0 (a window not yet
+ * full; such entries must not be passed to attention).  EINVAL if window > ring_rows or slots * ring_rows
+ * exceeds the int32 row range. */
+hsk_status hsk_ring_window_locs(int64_t ring_rows, int32_t slots, int32_t window, const int64_t* d_t_end,
+                                int32_t* d_locs, hsk_stream_t stream);
+
 /* Plan replay (HiSparse section 3.5, plan-then-IO): copy the rows listed in plan_source's last miss plan
  * from dst_source's host rows into dst_source's pool, at the same pool rows (EINVAL for a store with shared
  * staging arenas and staging rows, whose staged rows are not at the same relative rows).  A layer that shares its

@@ -55,3 +55,52 @@ def test_replay_rejected_with_shared_staging():
         st.replay_plan(0, 1)
     assert e.value.status == hsk.HSK_EINVAL
     st.close()
+
+
+def test_draft_ring_write_window_and_attention():
+    """Draft rows written round by round (blocks of up to K_max rows) wrap around a ring of R_d rows (Eq. 9);
+    the window locations are Eq. 10's addresses, the ring rows at them hold the window's rows, and attention
+    over the window matches the fp64 oracle."""
+    import oracle
+    rng = np.random.default_rng(31)
+    slots, window, page, k_max, H = 3, 200, 16, 8, 16
+    ring = hsk.ring_rows(window, page, k_max)
+    assert ring == oracle.ring_rows(window, page, k_max)
+    w = synth.WORKLOADS["tiny"].scaled(seed=3200)
+    d_ring = torch.empty(slots * ring * w.row_bytes, dtype=torch.uint8, device="cuda")
+    t = np.array([0, 5, 37], np.int64)          # each slot's next draft position
+    ad = hsk.mla_desc(requests=slots, max_queries=1, heads=H, dk=576, dv=512, top_k=window, row_elems=576,
+                      scale=576 ** -0.5)
+    scratch = torch.empty(hsk.attn_scratch_bytes(ad), dtype=torch.uint8, device="cuda")
+    locs = torch.empty((slots, 1, window), dtype=torch.int32, device="cuda")
+    checked = 0
+    for rnd in range(70):
+        count = int(rng.integers(1, k_max + 1))
+        rows = np.stack([synth.kv_rows(w, 9, i, int(t[i]), count) for i in range(slots)])
+        hsk.ring_write(d_ring, ring, slots, torch.from_numpy(rows.view(np.int16)).cuda(), count, w.row_bytes,
+                       torch.from_numpy(t.copy()).cuda())
+        t += count
+        hsk.ring_window_locs(ring, slots, window, torch.from_numpy(t.copy()).cuda(), locs)
+        lo = locs.cpu().numpy().reshape(slots, window)
+        for i in range(slots):
+            pos = np.arange(t[i] - window, t[i])
+            want = np.array([oracle.ring_addr(i, int(p), ring) if p >= 0 else -1 for p in pos])
+            assert np.array_equal(lo[i], want), f"round {rnd} slot {i}"
+        if np.all(t >= window) and rnd % 10 == 9:
+            view = d_ring.view(slots * ring, w.row_bytes)
+            q = torch.from_numpy(rng.standard_normal((slots, 1, H, 576)).astype(np.float32)).to(torch.bfloat16)
+            out = torch.zeros((slots, 1, H, 512), dtype=torch.int16, device="cuda")
+            hsk.sparse_decode_attn(ad, q.view(torch.int16).cuda(), d_ring, locs, None, out, scratch, scratch.numel())
+            ob = out.cpu().numpy()
+            qb = q.view(torch.int16).numpy().view(np.uint16)
+            for i in range(slots):
+                pos = np.arange(t[i] - window, t[i])
+                got_rows = view.index_select(0, locs[i, 0].long()).cpu().numpy()
+                want_rows = synth.kv_rows_at(w, 9, i, pos).view(np.uint8).reshape(got_rows.shape)
+                assert np.array_equal(got_rows, want_rows)
+                ref = oracle.mla_attention(qb[i, 0], synth.kv_rows_at(w, 9, i, pos), 576, 512, 576 ** -0.5)
+                g = synth.bf16_to_f32(ob[i, 0].view(np.uint16)).astype(np.float64)
+                assert np.all(np.abs(g - ref) <= 1e-2 + 2e-2 * np.abs(ref)), f"round {rnd} slot {i}"
+            checked += 1
+    assert checked >= 2
+    log(f"[ring] R_d={ring}: {checked} attention checks over wrapped windows")

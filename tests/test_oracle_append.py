@@ -123,3 +123,13 @@ def test_append_many_steps_matches_brute_force_tail():
             assert np.array_equal(locs[tail], R * B + r * T + sel[r, 0][tail] % T)
             tags = src.pool_lookup(locs)
             assert np.array_equal(tags, (r << 32) | sel[r, 0].astype(np.int64))
+
+
+def test_ring_rows_library_helper_matches_oracle():
+    """Adaptive DHiSparse Eq. 9 in the C ABI (host function) against the oracle and the worked example."""
+    hsk = pytest.importorskip("hierarchical_sparse_kv_layer_amd")
+    assert hsk.ring_rows(2048, 64, 8) == 2176
+    for window, p, k_max in itertools.product((1, 7, 64, 1000, 2048, 4097), (1, 2, 16, 64), (1, 4, 8, 16)):
+        assert hsk.ring_rows(window, p, k_max) == oracle.ring_rows(window, p, k_max)
+    with pytest.raises(hsk.HskError):
+        hsk.ring_rows(0, 64, 8)
