@@ -20,6 +20,7 @@ brute-force LRU simulator, library softmax attention, invariants and the pages' 
 from __future__ import annotations
 
 import ctypes
+from typing import Optional
 import os
 import subprocess
 
@@ -86,6 +87,8 @@ def lib():
         L.ora_context_rows.restype = i64
         L.ora_completed_rows.argtypes = [i64, i64, i32, vp, vp]
         L.ora_completed_rows.restype = i32
+        L.ora_policy_replay.argtypes = [vp, i32, i32, i64, i64, i32, i32, ctypes.c_uint64, vp]
+        L.ora_policy_replay.restype = i32
         L.ora_ring_rows.argtypes = [i64, i64, i64]
         L.ora_ring_rows.restype = i64
         L.ora_ring_addr.argtypes = [i64, i64, i64]
@@ -225,6 +228,23 @@ def completed_rows(n_before: int, n_after: int, m: int):
     rc = lib().ora_completed_rows(int(n_before), int(n_after), int(m), ctypes.addressof(first),
                                   ctypes.addressof(count))
     return None if rc else (first.value, count.value)
+
+
+POLICIES = {"lru": 0, "fifo": 1, "random": 2, "belady": 3}
+
+
+def policy_replay(sel: np.ndarray, n: int, B: int, policy: str, tail_from: Optional[int] = None,
+                  seed: int = 0) -> np.ndarray:
+    """HiSparse 4.3 / Figure 6: misses per step of one request's stream sel [steps][k] under a replacement
+    policy ("lru", "fifo", "random", "belady") with B slots (B >= k)."""
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    steps, k = sel.shape
+    out = np.zeros(steps, np.int32)
+    rc = lib().ora_policy_replay(_p(sel), steps, k, int(n), int(n if tail_from is None else tail_from), int(B),
+                                 POLICIES[policy], int(seed), _p(out))
+    if rc:
+        raise ValueError(f"ora_policy_replay rejected the input ({rc})")
+    return out
 
 
 def ring_rows(window: int, page_rows: int, k_max: int) -> int:

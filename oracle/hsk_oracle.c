@@ -451,3 +451,105 @@ int64_t ora_ring_addr(int64_t slot, int64_t t, int64_t ring_rows) { return slot 
 double ora_staging_bytes(int64_t live_sources, int64_t slots, int64_t k_max, int64_t k, int64_t row_bytes) {
   return (double)live_sources * (double)slots * (double)k_max * (double)k * (double)row_bytes;
 }
+
+/* ---------------------------------------------------------------------------------------------- */
+/* cache-policy replay: [HS] 4.3 / Figure 6 (LRU, FIFO, random, Belady on one selection stream)    */
+/* ---------------------------------------------------------------------------------------------- */
+/* One request's single-query stream sel[steps][k] over positions [0, n) replayed against B slots (B >= k);
+ * positions >= tail_from resolve directly and are not cached.  misses[t] = selected positions not resident
+ * at step t.  Every policy evicts only slots whose position is not selected in the current step, lowest slot
+ * first among equals:
+ *   ORA_POLICY_LRU    the deterministic LRU of the hot path (rec = 2e+1 after a hit, 2e after a fill, misses
+ *                     take victims in ascending (rec, slot) in first-occurrence order);
+ *   ORA_POLICY_FIFO   the earliest filled slot (hits do not refresh);
+ *   ORA_POLICY_RANDOM a uniformly random slot (SplitMix64 of seed and a counter);
+ *   ORA_POLICY_BELADY the slot whose position is selected again furthest in the future (never: first). */
+static uint64_t ora_splitmix(uint64_t* s) {
+  uint64_t z = (*s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+int32_t ora_policy_replay(const int32_t* sel, int32_t steps, int32_t k, int64_t n, int64_t tail_from, int32_t B,
+                          int32_t policy, uint64_t seed, int32_t* misses) {
+  if (steps < 1 || k < 1 || B < k || n < 1 || policy < 0 || policy > 3) return ORA_EINVAL;
+  int32_t* slot_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);   /* position -> slot or -1 */
+  int32_t* key = (int32_t*)malloc(sizeof(int32_t) * (size_t)B);       /* slot -> position or -1 */
+  int64_t* stamp = (int64_t*)calloc((size_t)B, sizeof(int64_t));      /* LRU rec, FIFO fill order, Belady next use */
+  uint8_t* hit = (uint8_t*)calloc((size_t)B, 1);
+  int32_t* next_use = (int32_t*)malloc(sizeof(int32_t) * (size_t)steps * k);
+  int32_t* last = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
+  int32_t* pend = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  if (!slot_of || !key || !stamp || !hit || !next_use || !last || !pend) {
+    free(slot_of); free(key); free(stamp); free(hit); free(next_use); free(last); free(pend);
+    return ORA_ENOMEM;
+  }
+  for (int64_t p = 0; p < n; ++p) { slot_of[p] = -1; last[p] = 0x7fffffff; }
+  for (int32_t b = 0; b < B; ++b) key[b] = -1;
+  /* next step at which the position of (t, i) is selected again, from a backward pass */
+  for (int32_t t = steps - 1; t >= 0; --t) {
+    for (int32_t i = 0; i < k; ++i) next_use[(int64_t)t * k + i] = last[sel[(int64_t)t * k + i]];
+    for (int32_t i = 0; i < k; ++i) last[sel[(int64_t)t * k + i]] = t;
+  }
+  uint64_t rng = seed;
+  int64_t fills = 0;
+  for (int32_t t = 0; t < steps; ++t) {
+    const int32_t* S = sel + (int64_t)t * k;
+    const uint32_t e = (uint32_t)t + 1;
+    memset(hit, 0, (size_t)B);
+    int32_t m = 0;
+    /* hits and distinct pending positions in first-occurrence order */
+    for (int32_t i = 0; i < k; ++i) {
+      const int32_t p = S[i];
+      if (p < 0 || p >= n) { m = -1; break; }
+      if (p >= tail_from) continue;
+      const int32_t sl = slot_of[p];
+      if (sl >= 0) {
+        hit[sl] = 1;
+        if (policy == 0) stamp[sl] = 2 * (int64_t)e + 1;
+        if (policy == 3) stamp[sl] = next_use[(int64_t)t * k + i];
+      } else {
+        int dup = 0;
+        for (int32_t j = 0; j < m; ++j) dup |= pend[j] == p;
+        if (!dup) pend[m++] = p;
+      }
+    }
+    if (m < 0) { free(slot_of); free(key); free(stamp); free(hit); free(next_use); free(last); free(pend); return ORA_ERANGE; }
+    misses[t] = m;
+    for (int32_t j = 0; j < m; ++j) {
+      /* choose a victim among the slots not hit this step */
+      int32_t v = -1;
+      if (policy == 2) {
+        int32_t cand = 0;
+        for (int32_t b = 0; b < B; ++b) cand += !hit[b];
+        int64_t pick = (int64_t)(ora_splitmix(&rng) % (uint64_t)cand);
+        for (int32_t b = 0; b < B; ++b)
+          if (!hit[b] && pick-- == 0) { v = b; break; }
+      } else {
+        for (int32_t b = 0; b < B; ++b) {
+          if (hit[b]) continue;
+          if (v < 0) { v = b; continue; }
+          if (key[b] < 0 && key[v] >= 0) { v = b; continue; }   /* an empty slot first */
+          if ((key[b] < 0) != (key[v] < 0)) continue;
+          if (policy == 3 ? stamp[b] > stamp[v] : stamp[b] < stamp[v]) v = b;
+        }
+      }
+      if (key[v] >= 0) slot_of[key[v]] = -1;
+      const int32_t p = pend[j];
+      key[v] = p;
+      slot_of[p] = v;
+      hit[v] = 1;   /* a slot filled this step is not a victim again in the same step */
+      if (policy == 0) stamp[v] = 2 * (int64_t)e;
+      if (policy == 1) stamp[v] = ++fills;
+      if (policy == 3) {
+        int32_t nu = 0x7fffffff;
+        for (int32_t i = 0; i < k; ++i)
+          if (S[i] == p) { nu = next_use[(int64_t)t * k + i]; break; }
+        stamp[v] = nu;
+      }
+    }
+  }
+  free(slot_of); free(key); free(stamp); free(hit); free(next_use); free(last); free(pend);
+  return ORA_OK;
+}

@@ -102,6 +102,11 @@ int64_t ora_ring_rows(int64_t window, int64_t page_rows, int64_t k_max);
 int64_t ora_ring_addr(int64_t slot, int64_t t, int64_t ring_rows);
 double ora_staging_bytes(int64_t live_sources, int64_t slots, int64_t k_max, int64_t k, int64_t row_bytes);
 
+/* [HS] 4.3 / Figure 6: replacement policies replayed on one single-query selection stream (test use) */
+enum { ORA_POLICY_LRU = 0, ORA_POLICY_FIFO = 1, ORA_POLICY_RANDOM = 2, ORA_POLICY_BELADY = 3 };
+int32_t ora_policy_replay(const int32_t* sel, int32_t steps, int32_t k, int64_t n, int64_t tail_from, int32_t B,
+                          int32_t policy, uint64_t seed, int32_t* misses);
+
 #ifdef __cplusplus
 }
 #endif
