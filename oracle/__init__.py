@@ -81,6 +81,8 @@ def lib():
         L.ora_bf16_from_f64.restype = None
         L.ora_reclaim_plan.argtypes = [vp, i32, i64]
         L.ora_reclaim_plan.restype = i32
+        L.ora_admit.argtypes = [vp, i32, i64, i64]
+        L.ora_admit.restype = i32
         L.ora_append.argtypes = [vp, i32]
         L.ora_append.restype = i32
         L.ora_context_rows.argtypes = [vp, i32]
@@ -112,7 +114,7 @@ class Source:
         """stg_base: first staging row relative to the source's pool rows when staging is an arena shared
         with other sources (-1: right after the optional pages)."""
         self.R, self.B, self.T = int(R), int(B), int(T)
-        self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, dtype=np.int64), (self.R,)))
+        self.ctx = np.array(np.broadcast_to(np.asarray(ctx, dtype=np.int64), (self.R,)))
         self.max_ctx = int(self.ctx.max() if max_ctx is None else max_ctx)
         self.page_rows, self.opt_pool_pages, self.staging_rows = int(page_rows), int(opt_pool_pages), int(staging_rows)
         self.row_bytes = int(row_bytes)
@@ -144,6 +146,14 @@ class Source:
 
     def context_rows(self, r: int) -> int:
         return int(lib().ora_context_rows(self._h, int(r)))
+
+    def admit(self, r: int, n_rows: int, uid: int) -> int:
+        """A new request (identity uid) takes slot r with n_rows of imported history (Adaptive DHiSparse
+        3.1 admission); later pool rows of the slot are tagged (uid << 32) | position."""
+        rc = int(lib().ora_admit(self._h, int(r), int(n_rows), int(uid)))
+        if rc == OK:
+            self.ctx[r] = int(n_rows)
+        return rc
 
     def resolve(self, epoch: int, sel: np.ndarray, nq=None) -> dict:
         """sel int32 [R][Qmax][k].  Returns locs, cls, stats, plan (per request: positions and pool rows in

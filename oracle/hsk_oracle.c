@@ -29,7 +29,8 @@ struct ora_source {
   int32_t R, B, T, P, S, row_bytes;
   int64_t opt_pool_pages;
   int64_t* ctx;       /* [R] rows of the context, grown by appends */
-  int64_t* n_import;  /* [R] imported history (context at creation) */
+  int64_t* n_import;  /* [R] imported history (context at creation or admission) */
+  int64_t* uid;       /* [R] identity of the request in each slot (the slot index until an admission) */
   int64_t max_ctx;    /* rows reserved per request */
   int32_t* key;       /* [R][B] position held by a hot slot, -1 = empty */
   uint32_t* rec;      /* [R][B] recency stamp, 0 = empty */
@@ -50,7 +51,7 @@ static int64_t opt_loc(const ora_source* s, int64_t page_id, int64_t p) {
   return (int64_t)s->R * s->B + (int64_t)s->R * s->T + page_id * s->P + (p % s->P);
 }
 static int64_t stg_loc(const ora_source* s, int32_t r, int64_t c) { return s->stg_base + (int64_t)r * s->S + c; }
-static int64_t pool_tag(int32_t r, int64_t p) { return ((int64_t)r << 32) | p; }
+static int64_t pool_tag(const ora_source* s, int32_t r, int64_t p) { return (s->uid[r] << 32) | p; }
 
 ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B, int32_t T, int32_t page_rows,
                        int64_t opt_pool_pages, int32_t staging_rows, int32_t row_bytes, int64_t stg_base) {
@@ -64,6 +65,7 @@ ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B
   s->max_ctx = max_ctx;
   s->ctx = (int64_t*)malloc(sizeof(int64_t) * R);
   s->n_import = (int64_t*)malloc(sizeof(int64_t) * R);
+  s->uid = (int64_t*)malloc(sizeof(int64_t) * R);
   s->key = (int32_t*)malloc(sizeof(int32_t) * (size_t)R * B);
   s->rec = (uint32_t*)calloc((size_t)R * B, sizeof(uint32_t));
   s->pt = (int32_t**)calloc(R, sizeof(int32_t*));
@@ -74,12 +76,13 @@ ora_source* ora_create(int32_t R, const int64_t* ctx, int64_t max_ctx, int32_t B
   s->pool_rows = own + (int64_t)R * staging_rows;
   if (s->stg_base + (int64_t)R * staging_rows > s->pool_rows) s->pool_rows = s->stg_base + (int64_t)R * staging_rows;
   s->pool = (int64_t*)malloc(sizeof(int64_t) * (size_t)s->pool_rows);
-  if (!s->ctx || !s->n_import || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
+  if (!s->ctx || !s->n_import || !s->uid || !s->key || !s->rec || !s->pt || !s->opt || !s->pool) { ora_destroy(s); return NULL; }
   for (int64_t i = 0; i < s->pool_rows; ++i) s->pool[i] = -1;
   for (int64_t i = 0; i < (int64_t)R * B; ++i) s->key[i] = -1;
   for (int32_t r = 0; r < R; ++r) {
     s->ctx[r] = ctx[r];
     s->n_import[r] = ctx[r];
+    s->uid[r] = r;
     if (ctx[r] <= 0 || ctx[r] > max_ctx) { ora_destroy(s); return NULL; }
     s->pt[r] = (int32_t*)malloc(sizeof(int32_t) * (size_t)max_ctx);
     int64_t np = page_rows ? ctx[r] / page_rows : 0;
@@ -95,7 +98,7 @@ void ora_destroy(ora_source* s) {
   if (!s) return;
   if (s->pt) for (int32_t r = 0; r < s->R; ++r) free(s->pt[r]);
   if (s->opt) for (int32_t r = 0; r < s->R; ++r) free(s->opt[r]);
-  free(s->pt); free(s->opt); free(s->ctx); free(s->n_import); free(s->key); free(s->rec); free(s->pool); free(s);
+  free(s->pt); free(s->opt); free(s->ctx); free(s->n_import); free(s->uid); free(s->key); free(s->rec); free(s->pool); free(s);
 }
 
 int64_t ora_pool_rows(const ora_source* s) { return s->pool_rows; }
@@ -105,8 +108,33 @@ void ora_commit_prefill(ora_source* s) {
   for (int32_t r = 0; r < s->R; ++r) {
     int64_t lo = s->ctx[r] - s->T;
     if (lo < 0) lo = 0;
-    for (int64_t p = lo; p < s->ctx[r]; ++p) s->pool[tail_loc(s, r, p)] = pool_tag(r, p);
+    for (int64_t p = lo; p < s->ctx[r]; ++p) s->pool[tail_loc(s, r, p)] = pool_tag(s, r, p);
   }
+}
+
+/* [AD] 3.1 admission: a new request (identity uid) takes slot r with n_rows of imported history.  Its hot
+ * cache is reserved empty, it has no optional pages yet, its context is the imported history, and the
+ * newest T rows sit in its tail (tail storage is a required allocation, never lent). */
+int32_t ora_admit(ora_source* s, int32_t r, int64_t n_rows, int64_t uid) {
+  if (r < 0 || r >= s->R || n_rows < 1 || n_rows > s->max_ctx || uid < 0 || uid > 0x7fffffff) return ORA_EINVAL;
+  const int64_t np = s->P ? n_rows / s->P : 0;
+  int32_t* opt = (int32_t*)malloc(sizeof(int32_t) * (size_t)(np > 0 ? np : 1));
+  if (!opt) return ORA_ENOMEM;
+  free(s->opt[r]);
+  s->opt[r] = opt;
+  for (int64_t g = 0; g < np; ++g) s->opt[r][g] = -1;
+  for (int32_t j = 0; j < s->B; ++j) {
+    s->key[(int64_t)r * s->B + j] = -1;
+    s->rec[(int64_t)r * s->B + j] = 0;
+  }
+  for (int64_t p = 0; p < s->max_ctx; ++p) s->pt[r][p] = -1;
+  s->ctx[r] = n_rows;
+  s->n_import[r] = n_rows;
+  s->uid[r] = uid;
+  int64_t lo = n_rows - s->T;
+  if (lo < 0) lo = 0;
+  for (int64_t p = lo; p < n_rows; ++p) s->pool[tail_loc(s, r, p)] = pool_tag(s, r, p);
+  return ORA_OK;
 }
 
 /* [AD] 3.1: optional residency covers complete pages of imported history; population copies the page
@@ -120,7 +148,7 @@ int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int
   for (int64_t g = 0; g < n_pages; ++g) {
     s->opt[r][g] = page_ids[g];
     if (page_ids[g] >= 0)
-      for (int64_t i = 0; i < s->P; ++i) s->pool[opt_loc(s, page_ids[g], g * s->P + i)] = pool_tag(r, g * s->P + i);
+      for (int64_t i = 0; i < s->P; ++i) s->pool[opt_loc(s, page_ids[g], g * s->P + i)] = pool_tag(s, r, g * s->P + i);
   }
   return ORA_OK;
 }
@@ -137,7 +165,7 @@ int32_t ora_append(ora_source* s, int32_t count) {
   for (int32_t r = 0; r < s->R; ++r) {
     for (int32_t i = 0; i < count; ++i) {
       const int64_t p = s->ctx[r] + i;
-      s->pool[tail_loc(s, r, p)] = pool_tag(r, p);
+      s->pool[tail_loc(s, r, p)] = pool_tag(s, r, p);
     }
     s->ctx[r] += count;
   }
@@ -267,7 +295,7 @@ static void resolve_request(ora_source* s, int32_t r, uint32_t e, const int32_t*
       staged_at[miss[i]] = (int32_t)(i - v);
       dst = stg_loc(s, r, i - v);
     }
-    s->pool[dst] = pool_tag(r, miss[i]);
+    s->pool[dst] = pool_tag(s, r, miss[i]);
     if (plan_n && i < plan_cap) {
       plan_pos[(int64_t)r * plan_cap + i] = miss[i];
       plan_loc[(int64_t)r * plan_cap + i] = (int32_t)dst;

@@ -61,6 +61,9 @@ void ora_commit_prefill(ora_source* s);
 /* map entries for complete pages [0, n_pages) of request r: page id in the optional pool, or -1 */
 int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int64_t n_pages);
 int32_t ora_append(ora_source* s, int32_t count);
+/* a new request (identity uid, n_rows of imported history) takes slot r: empty hot cache, no optional pages,
+ * its newest T rows in the tail; pool rows are tagged with uid from then on */
+int32_t ora_admit(ora_source* s, int32_t r, int64_t n_rows, int64_t uid);
 int64_t ora_context_rows(const ora_source* s, int32_t r);
 int32_t ora_completed_rows(int64_t n, int64_t n2, int32_t m, int64_t* first, int64_t* count);
 
