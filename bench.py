@@ -282,7 +282,7 @@ def memcpy_ceiling(nbytes: int = 1 << 28, reps: int = 8) -> dict:
 
 
 # ------------------------------------------------------------------------------------------------------
-# other workloads (python bench.py --workload verify|adaptive|quest): one JSON line each, for the record of
+# other workloads (python bench.py --workload verify|adaptive|quest|decode|loadstep): one JSON line each, for the record of
 # every hot-path step; the default run is the 100K batch-64 decode above
 # ------------------------------------------------------------------------------------------------------
 def _ev():
@@ -523,6 +523,149 @@ def run_decode(hsk, synth, w, steps: int) -> dict:
                     "runs on a backup stream beside the following calls"}
 
 
+def _loadstep_arm(hsk, synth, w, ls, optional: bool) -> dict:
+    """One arm of the load step: requests arrive in a closed loop at the offered concurrency of each phase,
+    are admitted resident-first (their 100K-row history arrives in device memory) when Eq. 3 allows, decode
+    their output length (one resolve + MLA attention per step over the admitted slots) and are released; one
+    bounded round-robin population attempt per step refills optional history on a copy stream."""
+    import collections
+    import torch
+    R, k, P = w.requests, w.top_k, w.page_rows
+    pool_pages = ls.capacity_pages - ls.reserve_pages
+    st = hsk.KVStore(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=w.hot_slots, tail_rows=w.tail_rows,
+                     ctx=1, max_ctx=w.ctx, page_rows=P, opt_pool_pages=pool_pages, max_queries=1, top_k=k)
+    st.residency_init(ls.capacity_pages, ls.reserve_pages, ls.required_pages, ls.pages_per_attempt, optional)
+    hist = torch.from_numpy(synth.kv_rows(w, 0, 0, 0, w.ctx).view(np.int16)).cuda()
+    lmax = ls.out_len[1]
+    tpl = torch.from_numpy(synth.selection_stream(w, 0, steps=lmax, units=slice(0, ls.templates))).cuda()
+    tpl = tpl.reshape(lmax * ls.templates, k)                          # row t * templates + template
+    lengths = synth.output_lengths(ls, 1 << 14)
+    q = torch.from_numpy(synth.queries(w, 0, 0).view(np.int16)).cuda()
+    ad = hsk.mla_desc(requests=R, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k, row_elems=w.row_elems,
+                      scale=w.scale)
+    nb = hsk.attn_scratch_bytes(ad)
+    scratch = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = torch.empty((R, 1, w.heads, w.dv), dtype=torch.int16, device="cuda")
+    locs = torch.empty((R, 1, k), dtype=torch.int32, device="cuda")
+    total = sum(n for _, n in ls.phases)
+    stats = torch.zeros((total, R * hsk.STATS_BYTES), dtype=torch.uint8, device="cuda")
+    pool = st.pool_base(0)
+    main, copy = torch.cuda.current_stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    slot_req = [-1] * R              # request in each slot
+    slot_t = [0] * R                 # steps it has decoded
+    waiting = collections.deque()    # (request, arrival step)
+    arrival, admitted_at, finished_at = {}, {}, {}
+    next_req, in_system = 0, 0
+    ev = [(_ev(), _ev()) for _ in range(total + 1)]
+    series, populated = [], []
+    t = 0
+    for phase, (conc, n_steps) in enumerate(ls.phases):
+        for _ in range(n_steps):
+            while in_system < conc:                                     # closed loop: arrivals
+                waiting.append(next_req)
+                arrival[next_req] = t
+                next_req += 1
+                in_system += 1
+            ev[t][0].record(main)
+            for _a in range(ls.admit_per_step):                          # admissions, FIFO
+                free = [r for r in range(R) if slot_req[r] < 0]
+                if not waiting or not free:
+                    break
+                try:
+                    st.admit(free[0], w.ctx, hist, stream=main)
+                except hsk.HskError as e:
+                    if e.status == hsk.HSK_EWAIT:
+                        break
+                    raise
+                rq = waiting.popleft()
+                slot_req[free[0]], slot_t[free[0]] = rq, 0
+                admitted_at[rq] = t
+            populated.append(st.populate(stream=main, copy_stream=copy) if optional else 0)
+            info = st.residency_info()
+            ev[t][1].record(main)
+            nq = np.array([1 if slot_req[r] >= 0 else 0 for r in range(R)], np.int32)
+            idx = np.array([slot_t[r] * ls.templates + (slot_req[r] % ls.templates) if slot_req[r] >= 0 else 0
+                            for r in range(R)], np.int64)
+            d_nq = torch.from_numpy(nq).cuda()
+            sel = tpl.index_select(0, torch.from_numpy(idx).cuda()).reshape(R, 1, k)
+            st.resolve_step(0, t + 1, sel, locs, stats[t], nq=d_nq, stream=main)
+            hsk.sparse_decode_attn(ad, q, pool, locs, d_nq, out, scratch, nb)
+            for r in range(R):                                           # one output step each; finish
+                rq = slot_req[r]
+                if rq < 0:
+                    continue
+                slot_t[r] += 1
+                if slot_t[r] >= lengths[rq]:
+                    st.release(r, stream=main)
+                    slot_req[r] = -1
+                    finished_at[rq] = t
+                    in_system -= 1
+            series.append({"step": t, "phase": phase, "admitted": info["admitted"], "waiting": len(waiting),
+                           "in_system": in_system,
+                           "coverage": info["ready_pages"] / max(1, info["eligible_pages"]),
+                           "pending_pages": info["pending_pages"], "unbacked_pages": info["unbacked_pages"]})
+            t += 1
+    ev[total][0].record(main)
+    torch.cuda.synchronize()
+    status = st.sync_status()
+    sn = stats.cpu().numpy().view(hsk.STATS_DTYPE).reshape(total, R)
+    st.close()
+    step_ms = [ev[i][0].elapsed_time(ev[i + 1][0]) for i in range(total)]
+    decode_ms = [ev[i][1].elapsed_time(ev[i + 1][0]) for i in range(total)]
+    admit_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(total)]
+    for i, x in enumerate(series):
+        sel_i = int(sn["n_sel"][i].sum())
+        x["host_share"] = int(sn["n_miss_sel"][i].sum()) / max(1, sel_i)
+        x["step_ms"] = step_ms[i]
+    phases, t0 = [], 0
+    for phase, (conc, n_steps) in enumerate(ls.phases):
+        rng_ = range(t0, t0 + n_steps)
+        sel_p = int(sn["n_sel"][t0:t0 + n_steps].sum())
+        miss_p = int(sn["n_miss_sel"][t0:t0 + n_steps].sum())
+        opt_p = int(sn["n_opt"][t0:t0 + n_steps].sum())
+        adm = [rq for rq, a in admitted_at.items() if a in rng_]
+        fin = [rq for rq, f in finished_at.items() if f in rng_]
+        full = next((i - t0 for i in rng_ if series[i]["admitted"] >= R), None)
+        half = next((i - t0 for i in rng_ if series[i]["coverage"] > 0.5), None)
+        # the steps after the in-flight count came back to the offered load (the last row of Table A1)
+        settled = [i for i in rng_ if series[i]["in_system"] <= conc]
+        sel_s = int(sn["n_sel"][settled].sum()) if settled else 0
+        miss_s = int(sn["n_miss_sel"][settled].sum()) if settled else 0
+        phases.append({"offered": conc, "steps": n_steps, "requests_admitted": len(adm), "requests_finished": len(fin),
+                       "host_fetched_pct": 100.0 * miss_p / max(1, sel_p), "optional_pct": 100.0 * opt_p / max(1, sel_p),
+                       "mean_coverage": float(np.mean([series[i]["coverage"] for i in rng_])),
+                       "decode_ms_per_step": float(np.mean([decode_ms[i] for i in rng_])),
+                       "step_ms": float(np.mean([step_ms[i] for i in rng_])),
+                       "admission_ms_per_step": float(np.mean([admit_ms[i] for i in rng_])),
+                       "alloc_wait_steps": float(np.mean([admitted_at[rq] - arrival[rq] for rq in adm])) if adm else None,
+                       "steps_to_fill_slots": full, "steps_to_coverage_50pct": half,
+                       "pages_populated": int(sum(populated[t0:t0 + n_steps])),
+                       "settled_steps": len(settled),
+                       "host_fetched_pct_settled": 100.0 * miss_s / sel_s if sel_s else None,
+                       "step_ms_settled": float(np.mean([step_ms[i] for i in settled])) if settled else None})
+        t0 += n_steps
+    return {"status": status, "phases": phases, "series": series[::5]}
+
+
+def run_loadstep(hsk, synth, w, steps: int) -> dict:
+    """Adaptive DHiSparse 4.3.1 (Figure 6, Table A1 shape): the load step replayed on the kernels, optional
+    residency on and off; coverage, host-fetched share and step time per phase."""
+    ls = synth.LOADSTEP
+    arms = {}
+    for optional in (True, False):
+        t0 = time.perf_counter()
+        arms["residency_on" if optional else "residency_off"] = _loadstep_arm(hsk, synth, w, ls, optional)
+        log(f"[loadstep] arm optional={optional} in {time.perf_counter() - t0:.1f} s")
+    return {"workload": f"load step, one GPU's share: {w.requests} slots, offered concurrency "
+                        f"{' -> '.join(str(c) for c, _ in ls.phases)} for {ls.phases[0][1]} steps each, imported "
+                        f"history {w.ctx} rows in {w.page_rows}-row pages (resident-first admission), output "
+                        f"{ls.out_len[0]}-{ls.out_len[1]} steps, B={w.hot_slots}, T={w.tail_rows}, top-k {w.top_k}, "
+                        f"{w.heads} heads; capacity {ls.capacity_pages} pages, {ls.required_pages} required per "
+                        f"request, reserve {ls.reserve_pages}, {ls.pages_per_attempt} pages per population attempt, "
+                        f"{ls.admit_per_step} admissions per step", **arms}
+
+
 def run_quest(hsk, synth, w, steps: int) -> dict:
     """Page-level GQA: layer 0 resolves the shared page selection; layers 1..7 replay its miss plan on a side
     stream while the previous layer's attention runs (HiSparse section 3.5)."""
@@ -614,7 +757,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the hits-only, misses-only and memcpy runs")
-    ap.add_argument("--workload", default="dsa100k", choices=["dsa100k", "verify", "adaptive", "quest", "decode"])
+    ap.add_argument("--workload", default="dsa100k",
+                    choices=["dsa100k", "verify", "adaptive", "quest", "decode", "loadstep"])
     ap.add_argument("--gather-blocks", type=int, default=0)
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
@@ -648,7 +792,8 @@ def main() -> int:
     w = synth.WORKLOADS["dsa100k" if args.workload == "decode" else args.workload]
     if args.workload != "dsa100k":
         torch.cuda.set_device(0)
-        fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest, "decode": run_decode}[args.workload]
+        fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest, "decode": run_decode,
+              "loadstep": run_loadstep}[args.workload]
         steps = args.steps if args.steps != 32 else w.steps
         print(json.dumps(fn(hsk, synth, w, steps)), flush=True)
         return 0

@@ -3,7 +3,9 @@
 Argument marshalling only: every step of the hot path runs in the HIP kernels of libhsk.so (see
 include/hsk.h).  PyTorch supplies device memory (tensors) and streams; the names below mirror the C ABI:
 
-    kv_store_init / host_rows / commit_prefill / residency_set / reclaim_plan / resolve_step /
+    kv_store_init / host_rows / commit_prefill / residency_set / reclaim_plan / residency_init /
+    request_admit / request_release / residency_reclaim / residency_populate / residency_publish /
+    residency_query / residency_pages / resolve_step /
     replay_plan / pool_base / sparse_decode_attn / attn_scratch_bytes / snapshot / read_plan /
     sync_status / kv_store_destroy
 
@@ -21,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhsk.so")
 
 HSK_OK, HSK_EINVAL, HSK_ENOMEM, HSK_EHIP, HSK_ESTATE, HSK_ERANGE, HSK_ESTAGE, HSK_EEPOCH = 0, -1, -2, -3, -4, -5, -6, -7
+HSK_EWAIT = -8
+PAGE_READY, PAGE_BACKED = 1, 2
 GATHER_ZEROCOPY, GATHER_NO_IO = 0, 1
 ATTN_MLA, ATTN_GQA = 0, 1
 MAX_HOT_SLOTS = 8192
@@ -45,6 +49,17 @@ class AttnDesc(ctypes.Structure):
                 ("page_tokens", _i32), ("split", _i32), ("scale", _f32)]
 
 
+class ResidencyDesc(ctypes.Structure):
+    _fields_ = [("capacity_pages", _i64), ("reserve_pages", _i64), ("required_pages", _i64),
+                ("pages_per_attempt", _i32), ("optional", _i32)]
+
+
+class ResidencyInfo(ctypes.Structure):
+    _fields_ = [("admitted", _i32), ("next_slot", _i32), ("required_pages", _i64), ("optional_pages", _i64),
+                ("ready_pages", _i64), ("pending_pages", _i64), ("unbacked_pages", _i64), ("eligible_pages", _i64),
+                ("free_pages", _i64)]
+
+
 STATS_DTYPE = np.dtype([("n_sel", np.int32), ("n_tail", np.int32), ("n_opt", np.int32), ("n_hit", np.int32),
                         ("n_hit_sel", np.int32), ("n_miss", np.int32), ("n_miss_sel", np.int32),
                         ("n_staged", np.int32), ("status", np.int32), ("reserved", np.int32),
@@ -60,6 +75,14 @@ _sig = {
     "hsk_commit_prefill": (_i32, [_vp, _vp]),
     "hsk_residency_set": (_i32, [_vp, _i32, _i32, _vp, _i64, _vp]),
     "hsk_reclaim_plan": (_i32, [_vp, _i32, _i64, _P(_i32)]),
+    "hsk_residency_init": (_i32, [_vp, _P(ResidencyDesc), _vp]),
+    "hsk_request_admit": (_i32, [_vp, _i32, _i64, _vp, _i64, _vp, _vp, _P(_i32)]),
+    "hsk_request_release": (_i32, [_vp, _i32, _vp]),
+    "hsk_residency_reclaim": (_i32, [_vp, _i64, _vp, _vp, _P(_i32)]),
+    "hsk_residency_populate": (_i32, [_vp, _vp, _vp, _P(_i32)]),
+    "hsk_residency_publish": (_i32, [_vp, _vp, _i32, _P(_i32)]),
+    "hsk_residency_query": (_i32, [_vp, _P(ResidencyInfo)]),
+    "hsk_residency_pages": (_i32, [_vp, _i32, _vp, _vp, _i64, _P(_i64)]),
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
     "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
@@ -158,6 +181,67 @@ def reclaim_plan(pages_held, deficit: int) -> int:
     return q.value
 
 
+def residency_init(store: int, capacity_pages: int, reserve_pages: int, required_pages: int, pages_per_attempt: int,
+                   optional: bool = True, stream=None) -> None:
+    d = ResidencyDesc(capacity_pages=int(capacity_pages), reserve_pages=int(reserve_pages),
+                      required_pages=int(required_pages), pages_per_attempt=int(pages_per_attempt),
+                      optional=1 if optional else 0)
+    _check(_lib.hsk_residency_init(store, ctypes.byref(d), _stream(stream)), "hsk_residency_init")
+
+
+def request_admit(store: int, req: int, n_rows: int, history=None, source_stride: int = 0, stream=None,
+                  num_requests: int = 0) -> list:
+    """Returns the slots reclaimed for the admission; raises HskError(HSK_EWAIT) when it must wait."""
+    out = np.zeros(max(1, num_requests), np.int32)
+    n = _i32()
+    _check(_lib.hsk_request_admit(store, int(req), int(n_rows), _ptr(history), int(source_stride), _stream(stream),
+                                  _ptr(out) if num_requests else None, ctypes.byref(n)), "hsk_request_admit")
+    return out[:n.value].tolist() if num_requests else []
+
+
+def request_release(store: int, req: int, stream=None) -> None:
+    _check(_lib.hsk_request_release(store, int(req), _stream(stream)), "hsk_request_release")
+
+
+def residency_reclaim(store: int, deficit: int, num_requests: int, stream=None) -> list:
+    out = np.zeros(max(1, num_requests), np.int32)
+    n = _i32()
+    _check(_lib.hsk_residency_reclaim(store, int(deficit), _stream(stream), _ptr(out), ctypes.byref(n)),
+           "hsk_residency_reclaim")
+    return out[:n.value].tolist()
+
+
+def residency_populate(store: int, stream=None, copy_stream=None) -> int:
+    n = _i32()
+    _check(_lib.hsk_residency_populate(store, _stream(stream), _stream(copy_stream if copy_stream is not None
+                                                                      else stream), ctypes.byref(n)),
+           "hsk_residency_populate")
+    return n.value
+
+
+def residency_publish(store: int, wait: bool = True, stream=None) -> int:
+    n = _i32()
+    _check(_lib.hsk_residency_publish(store, _stream(stream), 1 if wait else 0, ctypes.byref(n)),
+           "hsk_residency_publish")
+    return n.value
+
+
+def residency_query(store: int) -> dict:
+    i = ResidencyInfo()
+    _check(_lib.hsk_residency_query(store, ctypes.byref(i)), "hsk_residency_query")
+    return {f: getattr(i, f) for f, _ in ResidencyInfo._fields_}
+
+
+def residency_pages(store: int, req: int, cap: int):
+    ids = np.zeros(max(1, cap), np.int32)
+    flags = np.zeros(max(1, cap), np.uint8)
+    n = _i64()
+    _check(_lib.hsk_residency_pages(store, int(req), _ptr(ids), _ptr(flags), int(cap), ctypes.byref(n)),
+           "hsk_residency_pages")
+    m = min(n.value, cap)
+    return ids[:m].copy(), flags[:m].copy()
+
+
 def resolve_step(store: int, source: int, epoch: int, sel, nq, locs, stats, stream=None) -> None:
     _check(_lib.hsk_resolve_step(store, source, int(epoch), _ptr(sel), _ptr(nq), _ptr(locs), _ptr(stats),
                                  _stream(stream)), "hsk_resolve_step")
@@ -231,7 +315,7 @@ def snapshot(store: int, source: int, req: int, B: int, n_rows: int, page_rows: 
     key = np.zeros(B, np.int32)
     rec = np.zeros(B, np.uint32)
     order = np.zeros(B, np.uint16)
-    pt = np.zeros(n_rows, np.int32)
+    pt = np.zeros(max(0, n_rows), np.int32)
     opt = np.zeros(max(1, n_import // page_rows) if page_rows else 1, np.int32)
     _check(_lib.hsk_snapshot(store, source, req, _ptr(key), _ptr(rec), _ptr(order), _ptr(pt), _ptr(opt)),
            "hsk_snapshot")
@@ -265,7 +349,7 @@ class KVStore:
                  top_k: int, staging_rows: int = 0, host_alias: bool = False, gather_mode: int = GATHER_ZEROCOPY,
                  gather_blocks: int = 0, staging_arenas: int = 0, device: str = "cuda", stream=None):
         import torch
-        self.ctx = np.ascontiguousarray(np.broadcast_to(np.asarray(ctx, np.int64), (requests,)))
+        self.ctx = np.array(np.broadcast_to(np.asarray(ctx, np.int64), (requests,)))
         self.desc = Desc(num_requests=requests, num_sources=sources, row_bytes=row_bytes, hot_slots=hot_slots,
                          tail_rows=tail_rows, page_rows=page_rows, opt_pool_pages=opt_pool_pages,
                          max_queries=max_queries, top_k=top_k, staging_rows=staging_rows,
@@ -281,6 +365,7 @@ class KVStore:
         self.row_bytes, self.page_rows, self.max_queries, self.top_k = row_bytes, page_rows, max_queries, top_k
         self.staging_rows, self.opt_pool_pages = staging_rows, opt_pool_pages
         self.staging_arenas = staging_arenas
+        self.max_ctx = int(self.desc.max_ctx)
         self.rows_per_source = requests * hot_slots + requests * tail_rows + opt_pool_pages * page_rows + \
             (0 if staging_arenas else requests * staging_rows)
 
@@ -298,6 +383,37 @@ class KVStore:
 
     def residency_set(self, source: int, req: int, page_ids, stream=None):
         residency_set(self.handle, source, req, page_ids, stream)
+
+    # ---- scheduled residency (Adaptive DHiSparse 3.1) ----
+    def residency_init(self, capacity_pages: int, reserve_pages: int, required_pages: int, pages_per_attempt: int,
+                       optional: bool = True, stream=None):
+        residency_init(self.handle, capacity_pages, reserve_pages, required_pages, pages_per_attempt, optional,
+                       stream)
+        self.ctx[:] = 0
+
+    def admit(self, req: int, n_rows: int, history=None, source_stride: int = 0, stream=None) -> list:
+        out = request_admit(self.handle, req, n_rows, history, source_stride, stream, self.R)
+        self.ctx[req] = int(n_rows)
+        return out
+
+    def release(self, req: int, stream=None):
+        request_release(self.handle, req, stream)
+        self.ctx[req] = 0
+
+    def reclaim(self, deficit: int, stream=None) -> list:
+        return residency_reclaim(self.handle, deficit, self.R, stream)
+
+    def populate(self, stream=None, copy_stream=None) -> int:
+        return residency_populate(self.handle, stream, copy_stream)
+
+    def publish(self, wait: bool = True, stream=None) -> int:
+        return residency_publish(self.handle, wait, stream)
+
+    def residency_info(self) -> dict:
+        return residency_query(self.handle)
+
+    def residency_pages(self, req: int):
+        return residency_pages(self.handle, req, self.max_ctx // self.page_rows if self.page_rows else 0)
 
     def resolve_step(self, source: int, epoch: int, sel, locs, stats=None, nq=None, stream=None):
         resolve_step(self.handle, source, epoch, sel, nq, locs, stats, stream)

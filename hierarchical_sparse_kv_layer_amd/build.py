@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libhsk.so")
-SOURCES = ["store.hip", "resolve.hip", "attention.hip"]
+SOURCES = ["store.hip", "resolve.hip", "attention.hip", "residency.hip"]
 
 
 def hipcc() -> str:

@@ -104,6 +104,9 @@ hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* p
                             const int32_t* fill, const char* host, int64_t host_req_stride, void* out,
                             void* scratch, size_t scratch_bytes, hipStream_t s);
 
+struct ResidencyState;                       // scheduled residency (residency.hip)
+void residency_destroy(hsk_store* st);
+
 }  // namespace hsk
 
 struct hsk_store {
@@ -133,4 +136,5 @@ struct hsk_store {
   size_t h_stage_bytes = 0;
   void* d_stage = nullptr;                  // device copy of run lists
   size_t d_stage_bytes = 0;
+  hsk::ResidencyState* res = nullptr;       // set by hsk_residency_init: the library schedules residency
 };

@@ -616,6 +616,10 @@ __global__ __launch_bounds__(kGatherThreads) void append_tail_kernel(const char*
   const int wave = threadIdx.x >> 6;
   constexpr int kWaves = kGatherThreads / 64;
   const int64_t n = ctx[r];
+  if (n < 0) {  // a free slot (scheduled residency): nothing appended, nothing written through
+    if (threadIdx.x == 0) wt_pos[r] = -1;
+    return;
+  }
   for (int i = wave; i < count; i += kWaves) {
     const u32x4* src = (const u32x4*)(rows + ((int64_t)r * count + i) * row_bytes);
     u32x4* dst = (u32x4*)(pool + ((int64_t)R * B + (int64_t)r * T + ((n + i) % T)) * row_bytes);
@@ -639,6 +643,7 @@ __global__ __launch_bounds__(kGatherThreads) void write_through_kernel(const cha
   const int wave = threadIdx.x >> 6;
   constexpr int kWaves = kGatherThreads / 64;
   const int64_t p0 = wt_pos[r];
+  if (p0 < 0) return;  // free slot
   for (int i = wave; i < count; i += kWaves) {
     const u32x4* src = (const u32x4*)(pool + ((int64_t)R * B + (int64_t)r * T + ((p0 + i) % T)) * row_bytes);
     u32x4* dst = (u32x4*)(host + r * stride + (p0 + i) * row_bytes);

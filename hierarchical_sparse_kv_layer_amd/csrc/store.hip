@@ -97,6 +97,7 @@ const char* hsk_status_str(hsk_status s) {
     case HSK_ERANGE: return "HSK_ERANGE: selected position outside the request's history";
     case HSK_ESTAGE: return "HSK_ESTAGE: missing rows exceed free hot slots plus staging";
     case HSK_EEPOCH: return "HSK_EEPOCH: epoch not greater than the source's last epoch";
+    case HSK_EWAIT: return "HSK_EWAIT: admission waits, optional pages cannot cover its capacity";
     default: return "unknown hsk_status";
   }
 }
@@ -113,6 +114,7 @@ hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, si
 void hsk_kv_store_destroy(hsk_store* st) {
   if (!st) return;
   (void)hipDeviceSynchronize();
+  residency_destroy(st);
   for (hipEvent_t e : st->wt_done)
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : st->tail_done)
@@ -228,6 +230,7 @@ hsk_status hsk_pool_base(hsk_store* st, int32_t source, void** d_pool_source) {
 
 hsk_status hsk_commit_prefill(hsk_store* st, hsk_stream_t stream) {
   if (!st) return HSK_EINVAL;
+  if (st->res) return HSK_ESTATE;  // admissions place the tails
   if (st->d.tail_rows == 0) return HSK_OK;
   const int64_t stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
   for (int32_t k = 0; k < st->d.num_sources; ++k) {
@@ -244,7 +247,7 @@ hsk_status hsk_commit_prefill(hsk_store* st, hsk_stream_t stream) {
 hsk_status hsk_residency_set(hsk_store* st, int32_t source, int32_t req, const int32_t* h_page_ids,
                              int64_t n_pages, hsk_stream_t stream) {
   if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;
-  if (st->d.page_rows == 0) return HSK_ESTATE;
+  if (st->d.page_rows == 0 || st->res) return HSK_ESTATE;  // scheduled residency owns the maps
   // optional residency covers complete pages of the imported history only (Adaptive DHiSparse section 3.1:
   // rows generated during decoding stay under the tail and hot-cache rules)
   const int64_t complete = st->n_import[req] / st->d.page_rows;
@@ -386,8 +389,8 @@ hsk_status hsk_append_rows(hsk_store* st, int32_t source, const void* d_rows, in
     return HSK_EINVAL;
   const int32_t R = st->d.num_requests;
   int64_t* hctx = st->ctx.data() + (size_t)source * R;
-  for (int32_t r = 0; r < R; ++r)
-    if (hctx[r] + count > st->d.max_ctx) return HSK_EINVAL;
+  for (int32_t r = 0; r < R; ++r)  // free slots (context -1) are skipped
+    if (hctx[r] >= 0 && hctx[r] + count > st->d.max_ctx) return HSK_EINVAL;
   hipStream_t s = (hipStream_t)stream, b = (hipStream_t)backup_stream;
   const int par = st->append_parity[source];
   const size_t ev = 2 * (size_t)source + par;
@@ -412,7 +415,8 @@ hsk_status hsk_append_rows(hsk_store* st, int32_t source, const void* d_rows, in
   HSK_HIP(hipEventRecord(st->wt_done[ev], b));
   st->wt_pending[ev] = 1;
   st->append_parity[source] = par ^ 1;
-  for (int32_t r = 0; r < R; ++r) hctx[r] += count;
+  for (int32_t r = 0; r < R; ++r)
+    if (hctx[r] >= 0) hctx[r] += count;
   return HSK_OK;
 }
 
@@ -483,7 +487,7 @@ hsk_status hsk_snapshot(hsk_store* st, int32_t source, int32_t req, int32_t* key
   if (key) HSK_HIP(hipMemcpy(key, m.key + req * B, 4 * B, hipMemcpyDeviceToHost));
   if (rec) HSK_HIP(hipMemcpy(rec, m.rec + req * B, 4 * B, hipMemcpyDeviceToHost));
   if (order) HSK_HIP(hipMemcpy(order, m.order + req * B, 2 * B, hipMemcpyDeviceToHost));
-  const size_t n_r = (size_t)st->ctx[(size_t)source * st->d.num_requests + req];
+  const size_t n_r = (size_t)std::max<int64_t>(0, st->ctx[(size_t)source * st->d.num_requests + req]);
   if (pt) HSK_HIP(hipMemcpy(pt, m.pt + (size_t)req * st->d.max_ctx, 4 * n_r, hipMemcpyDeviceToHost));
   if (opt && st->max_pages) {
     const size_t np = (size_t)(st->n_import[req] / st->d.page_rows);

@@ -47,7 +47,8 @@ enum {
   HSK_ESTATE = -4,  /* call not valid in the store's state */
   HSK_ERANGE = -5,  /* a selected position is outside [0, n_r) */
   HSK_ESTAGE = -6,  /* a request's missing rows exceed its free hot slots plus its staging rows */
-  HSK_EEPOCH = -7   /* epoch not greater than the last epoch resolved on that source */
+  HSK_EEPOCH = -7,  /* epoch not greater than the last epoch resolved on that source */
+  HSK_EWAIT = -8    /* admission waits: the optional pages cannot cover the capacity it needs */
 };
 
 /* A hipStream_t, passed as a plain pointer; NULL is the null stream. */
@@ -151,6 +152,110 @@ hsk_status hsk_residency_set(hsk_store* store, int32_t source, int32_t req, cons
  * h_pages_held[0..n), the smallest q whose first q entries cover `deficit` pages; *q_out = -1 when the
  * optional pages cannot cover it (admission waits), 0 when deficit <= 0. */
 hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t deficit, int32_t* q_out);
+
+/* ---------------------------------------------------------------------------------------------------- */
+/* Load-adaptive residency ("Adaptive DHiSparse", section 3.1, Eqs. 3-4)                                */
+/* ---------------------------------------------------------------------------------------------------- */
+/*
+ * After hsk_residency_init the library schedules the optional-history pages itself and requests come and
+ * go through hsk_request_admit / hsk_request_release.  Capacity is counted in optional pages (page_rows
+ * rows of every source):
+ *   Eq. 3   required_pages x (admitted requests) + (optional pages held) + reserve_pages <= capacity_pages,
+ * where required_pages stands for one request's required allocation (its hot cache and tail, never lent)
+ * and held optional pages are the ready ones plus those whose copies are in flight.  A request's page g
+ * (rows [g*page_rows, (g+1)*page_rows) of its imported history, complete pages only) has the same page id
+ * in every source's optional pool.  Every row of an admitted request's history is at all times either
+ * ready on the device or backed by its host rows, so no resolve ever reads a host row that was not
+ * written.
+ * Ordering: `stream` is the stream the store's resolves and attention run on.  Map changes (publish and
+ * retire) are queued on it, so they take effect after earlier readers on it and before later ones;
+ * readers on other streams must be ordered with it by the caller.
+ */
+typedef struct hsk_residency_desc {
+  int64_t capacity_pages;      /* M of Eq. 3 */
+  int64_t reserve_pages;       /* M_res of Eq. 3: admission reserve, never lent */
+  int64_t required_pages;      /* capacity one admitted request's required allocation takes */
+  int32_t pages_per_attempt;   /* bound of one repopulation attempt (hsk_residency_populate) */
+  int32_t optional;            /* 1: optional residency on; 0: off (no page is ever held) */
+} hsk_residency_desc;
+
+typedef struct hsk_residency_info {
+  int32_t admitted;            /* requests admitted */
+  int32_t next_slot;           /* where the next round-robin attempt starts */
+  int64_t required_pages;      /* required_pages x admitted */
+  int64_t optional_pages;      /* pages held: ready + pending */
+  int64_t ready_pages;         /* published in the optional maps */
+  int64_t pending_pages;       /* reserved, copy in flight or not yet published */
+  int64_t unbacked_pages;      /* ready pages whose rows exist only on the device */
+  int64_t eligible_pages;      /* complete pages of the admitted requests' imported history */
+  int64_t free_pages;          /* capacity optional history may still take under Eq. 3 */
+} hsk_residency_info;
+
+/* Page flags reported by hsk_residency_pages. */
+enum { HSK_PAGE_READY = 1, HSK_PAGE_BACKED = 2 };
+
+/* Switch the store to scheduled residency: every slot becomes free (context -1: resolves must give it no
+ * queries, appends skip it), every optional map is cleared, and hsk_residency_set / hsk_commit_prefill
+ * return HSK_ESTATE from then on.  EINVAL for negative sizes, optional = 1 on a store without optional
+ * pages; ESTATE if called twice.  Allocates a small pinned staging ring for copy and map lists. */
+hsk_status hsk_residency_init(hsk_store* store, const hsk_residency_desc* desc, hsk_stream_t stream);
+
+/*
+ * Admission (section 3.1): a new request takes free slot `req` with n_rows (1..max_ctx) of imported
+ * history.  If Eq. 3 leaves a deficit, whole requests are reclaimed first (hsk_residency_reclaim, in
+ * admission order, oldest first); if all held optional pages cannot cover it the call returns HSK_EWAIT
+ * and changes nothing.  The slot's hot cache is reset empty, its context becomes n_rows in every source and
+ * its newest tail_rows rows are placed in its tail.
+ *   d_history != NULL (resident-first admission): the history is in device memory, source s at
+ *     d_history + hs * source_stride bytes, [n_rows][row_bytes], hs = 0 with host_alias_sources else s
+ *     (source_stride 0 = n_rows * row_bytes).  While Eq. 3 leaves capacity, complete pages 0, 1, ... are
+ *     kept on the device as optional pages (ready at once, host backup deferred); the remaining rows are
+ *     written to the host rows.  d_history must stay valid until `stream` passes the call.
+ *   d_history == NULL: the caller has already written the host rows (hsk_host_rows); nothing is retained and
+ *     pages come later through hsk_residency_populate.  A caller reusing a released slot synchronises
+ *     `stream` before writing its host rows.
+ * reclaimed (nullable, room for num_requests) receives the reclaimed slots, *n_reclaimed their count.
+ * ESTATE if the slot is admitted or residency is not initialised.
+ */
+hsk_status hsk_request_admit(hsk_store* store, int32_t req, int64_t n_rows, const void* d_history,
+                             int64_t source_stride, hsk_stream_t stream, int32_t* reclaimed,
+                             int32_t* n_reclaimed);
+
+/* The request in slot `req` finished: its optional pages are retired without backup (its history is no
+ * longer needed), queued on `stream` after earlier readers and after any in-flight copy into them; the
+ * slot becomes free (context -1).  `stream` is also ordered after the slot's pending write-throughs. */
+hsk_status hsk_request_release(hsk_store* store, int32_t req, hsk_stream_t stream);
+
+/* Eq. 4 reclaim: walking the admitted requests in admission order, take every optional page of the first
+ * q, q the smallest prefix whose pages cover `deficit`.  Pages whose rows exist only on the device are
+ * copied to their host rows first; the map entries are cleared after those copies and after earlier
+ * readers (all on `stream`); the page ids are then free for later work on `stream` and for populations.
+ * The requests stay admitted (their history is then fetched from host until repopulated).  HSK_EWAIT and
+ * no change when all held pages cannot cover the deficit; deficit <= 0 reclaims nothing. */
+hsk_status hsk_residency_reclaim(hsk_store* store, int64_t deficit, hsk_stream_t stream, int32_t* reclaimed,
+                                 int32_t* n_reclaimed);
+
+/* One bounded round-robin repopulation attempt (section 3.1).  First publishes the pending pages whose
+ * copies have completed (hsk_residency_publish with wait = 0).  Then, while Eq. 3 leaves capacity and page
+ * ids are free, visits admitted slots round-robin from where the last attempt stopped, reserving for each
+ * visited request its lowest-numbered page not held (one page per visit, lowest free page id), up to
+ * pages_per_attempt pages.  Their rows are copied from the host rows into the optional pools on
+ * `copy_stream` (which first waits for earlier admissions, releases and reclaims on `stream`); the pages
+ * stay pending (unmapped) until published.  *n_reserved = pages reserved. */
+hsk_status hsk_residency_populate(hsk_store* store, hsk_stream_t stream, hsk_stream_t copy_stream,
+                                  int32_t* n_reserved);
+
+/* Publish ready locations: the pending pages whose copies have completed (wait = 1: wait for all of them)
+ * enter the optional maps, queued on `stream`.  *n_published (nullable) = pages published. */
+hsk_status hsk_residency_publish(hsk_store* store, hsk_stream_t stream, int32_t wait, int32_t* n_published);
+
+/* Host-side view of the scheduler (no device work). */
+hsk_status hsk_residency_query(hsk_store* store, hsk_residency_info* info);
+
+/* Per-page state of the request in slot `req`: ids[g] (page id or -1) and flags[g] (HSK_PAGE_READY |
+ * HSK_PAGE_BACKED) for its complete pages g < *n_pages (at most cap written; either pointer may be NULL). */
+hsk_status hsk_residency_pages(hsk_store* store, int32_t req, int32_t* ids, uint8_t* flags, int64_t cap,
+                               int64_t* n_pages);
 
 /*
  * One resolve call on `source` at LRU clock `epoch` (strictly increasing per source; EEPOCH otherwise).

@@ -17,6 +17,9 @@ seeded synthetic inputs stand in for them with the pages' shapes):
 * ``adaptive``  -- load-adaptive residency, 64 requests, 500,000-token context, 2 layers sharing one
                    source, 64-row optional pages resident at 0/50/100% per request, reclaim of 16
                    requests at step 8.
+* ``loadstep``  -- load step of an MLA deployment (C16 -> C256 -> C16 over four data-parallel decode GPUs),
+                   one GPU's share: 52 request slots, offered concurrency 4 -> 64 -> 4, 100,000-token
+                   imported histories in 64-row pages, output lengths uniform in [60, 180] steps.
 * ``quest``     -- page-level GQA decode, 32 requests x 8 KV heads, 131,072 tokens in 16-token pages,
                    top-256 pages per KV head shared by 8 layers, 512 page slots per KV head.
 
@@ -152,11 +155,42 @@ WORKLOADS = {
                          row_elems=576, hot_slots=4096, tail_rows=128, heads=128, kv_heads=1, dk=576, dv=512,
                          top_k=2048, keep_frac=0.8, fresh="zipf", residency_levels=(0.0, 0.5, 1.0),
                          reclaim_step=8, reclaim_requests=16, seed=4004),
+    "loadstep": Workload(name="loadstep", kind="mla", requests=52, layers=1, sources=1, steps=720, ctx=100_000,
+                         row_elems=576, hot_slots=4096, tail_rows=128, heads=128, kv_heads=1, dk=576, dv=512,
+                         top_k=2048, keep_frac=0.8, fresh="zipf", seed=6006),
     "quest": Workload(name="quest", kind="gqa", requests=32, layers=8, sources=8, steps=16, ctx=8192,
                       row_elems=16 * 256, hot_slots=512, tail_rows=0, heads=32, kv_heads=8, dk=128, dv=128,
                       top_k=256, keep_frac=0.8, fresh="zipf", page_tokens=16, page_rows=0, host_alias=True,
                       shared_selection=True, seed=5005),
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class LoadStep:
+    """Offered-load schedule of the load-step replay: phases of (offered concurrency, steps); a closed loop
+    keeps that many requests in the system (admitted or waiting) and lets it drain when the load falls."""
+    phases: tuple = ((4, 240), (64, 240), (4, 240))
+    out_len: tuple = (60, 180)          # decode steps of a request, uniform, inclusive
+    admit_per_step: int = 2             # admissions per step (the prefill side's rate)
+    required_pages: int = 112           # one request's required allocation, in 64-row pages
+    reserve_pages: int = 112            # admission reserve
+    pages_per_attempt: int = 32         # bound of one repopulation attempt (one per step)
+    templates: int = 64                 # distinct selection streams; request i follows stream i mod templates
+    seed: int = 6006
+
+    @property
+    def capacity_pages(self) -> int:
+        """Capacity that fits 52 admitted requests' required allocations beside the reserve."""
+        return 52 * self.required_pages + self.reserve_pages
+
+
+LOADSTEP = LoadStep()
+
+
+def output_lengths(ls: LoadStep, n: int) -> np.ndarray:
+    """Decode steps of requests 0..n-1 (seeded, uniform in ls.out_len)."""
+    g = np.random.default_rng([ls.seed, 91])
+    return g.integers(ls.out_len[0], ls.out_len[1] + 1, size=n)
 
 
 # ----------------------------------------------------------------------------------------------
