@@ -507,7 +507,7 @@ __device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32
   }
 }
 
-// Host -> device gather of a miss plan (HiSparse section 3.4 phase 4 "GPU-assisted IO", section 3.5
+// Host -> device gather of a miss plan (HiSparse section 3.4 phase 4, the copy done by GPU threads; section 3.5
 // replay): 16-byte zero-copy loads from pinned host memory over PCIe into the pool rows.
 // Rows are numbered globally in request order (rows of earlier requests first) and wave w of the 1-D grid
 // copies the rows whose number is w modulo the number of waves, so every wave gets the same share however

@@ -4,8 +4,8 @@
  * C ABI of libhsk.so.  Plain pointers and sizes only; every call returns an hsk_status and never throws.
  *
  * What the library does, per decode step and layer (the hot path):
- *   1. hsk_resolve_step: the model's top-k selected positions of each request ("logical indices in") are
- *      turned into physical rows of a device pool ("physical slots out"), as the fused Resolve kernel of
+ *   1. hsk_resolve_step: the model's top-k selected positions of each request (logical positions) are
+ *      turned into physical rows of a device pool (pool locations), as the fused Resolve kernel of
  *      "HiSparse: Scaling Sparse-Attention Decoding with Hierarchical KV Cache Management" (section 3.4)
  *      does: tail rows and ready optional-history pages resolve directly ("Adaptive DHiSparse:
  *      Speculative Decoding over a Load-Adaptive KV Hierarchy", section 3.2, Figure 2 callout 1), the
@@ -273,7 +273,7 @@ hsk_status hsk_resolve_step(hsk_store* store, int32_t source, uint32_t epoch, co
                             const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream);
 
 /*
- * Decode-loop append (HiSparse section 3.3, step 4 "write-through of generated KV"; Adaptive DHiSparse
+ * Decode-loop append (HiSparse section 3.3, step 4: newly generated KV written through to host; Adaptive DHiSparse
  * section 3.2, the tail): every request of `source` takes `count` new rows, d_rows [R][count][row_bytes]
  * (device, e.g. the layer's KV of the tokens just generated), as positions n_r .. n_r + count - 1.
  *   On `stream`: the rows are written into the request's tail ring (pool row R*B + r*T + (p mod T)) and
