@@ -896,7 +896,7 @@ def main() -> int:
                    "global_batch": w.requests, "seq_len": w.ctx, "parallelism": "none (1 GPU)",
                    "path": args.path},
         "steps_per_s": K / elapsed,
-        "roofline": {"bound": "hbm", "kernel": "hsk_sparse_decode_attn call (mla_mfma_kernel + combine_kernel)",
+        "roofline": {"bound": "hbm", "kernel": "hsk_sparse_decode_attn call (mla32_kernel + combine_kernel)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": attn_bytes,
                      "avg_launch_ms": att_avg},

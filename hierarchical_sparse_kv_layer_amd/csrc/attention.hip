@@ -24,11 +24,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-__device__ __forceinline__ uint16_t f2bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return 0x7FC0;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+
+// two floats to a bf16 pair (round to nearest even, v_cvt_pk_bf16_f32), x in the low half
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)x, (__bf16)y};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 struct AttnArgs {
@@ -140,6 +141,16 @@ __device__ __forceinline__ void wait_tile_barrier_n(int n) {
     case 5: wait_tile_barrier<5>(); break;
     case 9: wait_tile_barrier<9>(); break;
     case 18: wait_tile_barrier<18>(); break;
+    default: wait_tile_barrier<0>(); break;
+  }
+}
+
+// the 32-head kernel's waits: this wave's loads of 0, 1 or 2 tiles (9 or 18 each) still in flight
+__device__ __forceinline__ void wait_tile_barrier32(int n) {
+  switch (n) {
+    case 9: wait_tile_barrier<9>(); break;
+    case 18: wait_tile_barrier<18>(); break;
+    case 36: wait_tile_barrier<36>(); break;
     default: wait_tile_barrier<0>(); break;
   }
 }
@@ -474,14 +485,409 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
     for (int cb = 0; cb < CB; ++cb) {
       const f32x4 v = oacc[cb][hb] * inv;
       u32x2 w;
-      w.x = (uint32_t)f2bf16(v[0]) | ((uint32_t)f2bf16(v[1]) << 16);
-      w.y = (uint32_t)f2bf16(v[2]) | ((uint32_t)f2bf16(v[3]) << 16);
+      w.x = pack_bf16(v[0], v[1]);
+      w.y = pack_bf16(v[2], v[3]);
       *(u32x2*)(o + 16 * cb) = w;
     }
     if (a.split > 1 && half == 0 && g == 0) {
       a.pm[ps] = m_run[hb] * kLn2;   // natural-log units, as the combine expects
       a.pl[ps] = l;
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------
+// MLA with one wave per SIMD and 32 heads per wave (v_mfma_f32_32x32x16_bf16).
+//
+// Each wave holds the query block of its 32 heads over the whole key width (36 16-dim chunks, 144
+// registers) and accumulates its 32 heads' output over all 512 value columns (256 accumulators), so the
+// waves of a workgroup never exchange scores and a tile needs one workgroup barrier (the one that lets a
+// tile buffer be refilled).  Per tile of 32 selected rows and wave:
+//   S^T (32 rows x 32 heads) = K (32 x 576) . Q^T        36 products, A = K from LDS (16-byte reads:
+//                                                       lane l reads row l % 32, dims 8 (l / 32) .. + 7
+//                                                       of each 16-dim chunk), B = Q in registers
+//   online softmax per head (fp32, exp2 domain)
+//   O^T (512 cols x 32 heads) += V^T . P                 32 products, A = V through transposing reads,
+//                                                       B = P as bf16
+// The scores' accumulator layout (lane l: head l % 32, rows 8 (v / 4) + 4 (l / 32) + v % 4 of element v)
+// is used as-is for the B operand of P.V: a lane's elements 8 ch .. 8 ch + 7 are its k-slots of the 16-row
+// chunk ch, and the transposing reads fetch V in the same row order (rows 16 ch + 8 p + 4 (l / 32) + 0..3
+// for part p), so no data moves between lanes between the two products.
+// Tiles use the chunk swizzle g(a) = ((a & 1) << 2) | (a >> 1), a = (row / 2) mod 8: g is a bijection (the
+// 16 rows of a K read hit 16 distinct 16-byte bank groups) and rows 4m and 4m + 2 get different bit 2 (the
+// 32 lanes of a transposing read, 4 rows x 64 bytes, hit 64 distinct banks).  Four tile buffers keep
+// three tiles in flight.
+// ------------------------------------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kBufs32 = 4;
+
+__device__ __forceinline__ int tile_swz32(int t) {
+  const int a = (t >> 1) & 7;
+  return ((a & 1) << 2) | (a >> 1);
+}
+__device__ __forceinline__ int tile_off32(int t, int c) {
+  return (((c >> 3) << 8) + (t << 3) + ((c & 7) ^ tile_swz32(t))) << 4;
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla32_kernel(MlaArgs a) {
+  constexpr int NT = 64 * NW;
+  constexpr int KC = kMlaDk / 16;              // 36 16-dim chunks of the key
+  constexpr int CB = kMlaDv / 32;              // 16 blocks of 32 value columns
+  constexpr int MY = kDmaPerTile / NW;         // this wave's tile loads
+  static_assert(kDmaPerTile % NW == 0 && (NW == 2 || NW == 4), "four or two waves");
+  __shared__ __attribute__((aligned(1024))) char s_tile[kBufs32][kTileBytes];
+  __shared__ int32_t s_loc[kMaxSplitRows];
+
+  int sp, hgrp, rq;
+  if (!mla_block(a, blockIdx.x, &sp, &hgrp, &rq)) return;
+  if (a.nq) {
+    const int r = rq / a.Qmax, qi = rq % a.Qmax;
+    if (qi >= a.nq[r]) return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, j = lane & 31;
+  const int i0 = sp * a.rows_per_split;
+  const int nrows = max(0, min(a.k, i0 + a.rows_per_split) - i0);
+  const int ntiles = (nrows + kTile - 1) / kTile;
+  const int hbase = hgrp * (32 * NW) + wave * 32;
+
+  const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
+  for (int x = tid; x < nrows; x += NT) s_loc[x] = locs[x];
+  __syncthreads();
+  // The first tiles' loads are issued before the query block is read, so the two latencies overlap.
+  bf16x8 qf[KC];
+
+  // LDS offsets.  K: row j, chunk 2c + h; for c = 4 u + w that is chunk group u (4,096 bytes further per u)
+  // at the position of chunk 2 w + h.  V: part p of chunk ch, column block cb: row 16 ch + 8 p + 4 h + (i >> 2)
+  // and 16-byte chunk 4 cb + 2 ((lane >> 4) & 1) + ((i & 3) >> 1), byte (i & 1) * 8, i = lane & 15; column
+  // blocks 2 u and 2 u + 1 are chunk group u at positions 0-3 and 4-7.
+  int kb[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) kb[w] = tile_off32(j, 2 * w + h);
+  int vb[2][2][2];
+  {
+    const int i = lane & 15, x = 2 * ((lane >> 4) & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int row = 16 * ch + 8 * p + 4 * h + (i >> 2);
+#pragma unroll
+        for (int o = 0; o < 2; ++o) vb[ch][p][o] = tile_off32(row, 4 * o + x) + (i & 1) * 8;
+      }
+  }
+  // DMA: wave-wide load i (i = wave + NW u) covers tile rows 8 (i & 3) .. + 7 of chunk group i >> 2; a lane
+  // copies 16 bytes of one row (four waves: always the same row; two waves: two rows in turn).
+  constexpr int NTOK = NW >= 4 ? 1 : 2;
+  const uint32_t lds_tile0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
+  auto issue = [&](int T, int b) {
+    const int tb = T * kTile;
+    const uint32_t lbase = lds_tile0 + b * kTileBytes + wave * 1024;
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const char* rp[NTOK];
+#pragma unroll
+    for (int v = 0; v < NTOK; ++v) {
+      const int tok = 8 * ((wave + NW * v) & 3) + (ln >> 3);
+      const int sw = ((ln & 7) ^ tile_swz32(tok)) << 4;
+      const int x = tb + tok < nrows ? tb + tok : 0;   // rows past the end re-read row 0 (masked)
+      rp[v] = a.pool + ((int64_t)s_loc[x] * a.row_bytes + sw);
+    }
+#pragma unroll
+    for (int u = 0; u < MY; ++u) {
+      const uint32_t m0 = lbase + NW * u * 1024;
+      const char* src = NW >= 4 ? rp[0] + u * 128 : rp[u % NTOK] + (u >> 1) * 128;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+    }
+  };
+#pragma unroll
+  for (int T = 0; T < kBufs32 - 1; ++T)
+    if (T < ntiles) issue(T, T);
+  {
+    const uint16_t* qb = a.q + ((int64_t)rq * a.H + hbase + j) * kMlaDk + 8 * h;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) qf[c] = *(const bf16x8*)(qb + 16 * c);
+  }
+  // The scores of a wave's head are weighed against one reference maximum m_ref, the maximum of the
+  // partition's first tile, and the output is never rescaled inside the loop (rescaling 256 accumulators
+  // held in the accumulation registers costs more than the loop can afford).  exp2(s - m_ref) stays below
+  // 2^64 as long as no later score exceeds m_ref by more than 64 (log2 units); if one does, the workgroup
+  // redoes the partition: a pass over the tiles for the true maximum, then the full pass against it.
+  f32x16 oacc[CB];
+  float m_ref = 0.f, l_run = 0.f;
+  // S of tile T for this wave's 32 heads.  The K reads are issued from inline assembly two chunks ahead of
+  // their products, with the waits written out (LDS reads of one wave complete in order), from four base
+  // registers per tile and immediate offsets.
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  auto scores = [&](const HSK_LDS char* tile, auto&& side) {
+    const uint32_t t0 = (uint32_t)(uintptr_t)tile;
+    const uint32_t kb0 = t0 + kb[0], kb1 = t0 + kb[1], kb2 = t0 + kb[2], kb3 = t0 + kb[3];
+    u32x4v kf[3];
+    f32x16 sc = f32x16{};
+#define HSK_K_READ(C)                                                                                       \
+  {                                                                                                        \
+    const uint32_t b_ = ((C)&3) == 0 ? kb0 : ((C)&3) == 1 ? kb1 : ((C)&3) == 2 ? kb2 : kb3;               \
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[(C) % 3]) : "v"(b_), "i"(((C) >> 2) * 4096) : "memory"); \
+  }
+#define HSK_K_STEP(C, WAIT)                                                                                 \
+  {                                                                                                        \
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[(C) % 3]) : "i"(WAIT));                                \
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[(C) % 3]), qf[C], sc, 0, 0, 0); \
+  }
+    HSK_K_READ(0) HSK_K_READ(1)
+    HSK_K_READ(2) HSK_K_STEP(0, 2) side(0);
+    HSK_K_READ(3) HSK_K_STEP(1, 2) side(1);
+    HSK_K_READ(4) HSK_K_STEP(2, 2) side(2);
+    HSK_K_READ(5) HSK_K_STEP(3, 2) side(3);
+    HSK_K_READ(6) HSK_K_STEP(4, 2) side(4);
+    HSK_K_READ(7) HSK_K_STEP(5, 2) side(5);
+    HSK_K_READ(8) HSK_K_STEP(6, 2) side(6);
+    HSK_K_READ(9) HSK_K_STEP(7, 2) side(7);
+    HSK_K_READ(10) HSK_K_STEP(8, 2) side(8);
+    HSK_K_READ(11) HSK_K_STEP(9, 2) side(9);
+    HSK_K_READ(12) HSK_K_STEP(10, 2) side(10);
+    HSK_K_READ(13) HSK_K_STEP(11, 2) side(11);
+    HSK_K_READ(14) HSK_K_STEP(12, 2) side(12);
+    HSK_K_READ(15) HSK_K_STEP(13, 2) side(13);
+    HSK_K_READ(16) HSK_K_STEP(14, 2) side(14);
+    HSK_K_READ(17) HSK_K_STEP(15, 2) side(15);
+    HSK_K_READ(18) HSK_K_STEP(16, 2) side(16);
+    HSK_K_READ(19) HSK_K_STEP(17, 2) side(17);
+    HSK_K_READ(20) HSK_K_STEP(18, 2) side(18);
+    HSK_K_READ(21) HSK_K_STEP(19, 2) side(19);
+    HSK_K_READ(22) HSK_K_STEP(20, 2) side(20);
+    HSK_K_READ(23) HSK_K_STEP(21, 2) side(21);
+    HSK_K_READ(24) HSK_K_STEP(22, 2) side(22);
+    HSK_K_READ(25) HSK_K_STEP(23, 2) side(23);
+    HSK_K_READ(26) HSK_K_STEP(24, 2) side(24);
+    HSK_K_READ(27) HSK_K_STEP(25, 2) side(25);
+    HSK_K_READ(28) HSK_K_STEP(26, 2) side(26);
+    HSK_K_READ(29) HSK_K_STEP(27, 2) side(27);
+    HSK_K_READ(30) HSK_K_STEP(28, 2) side(28);
+    HSK_K_READ(31) HSK_K_STEP(29, 2) side(29);
+    HSK_K_READ(32) HSK_K_STEP(30, 2) side(30);
+    HSK_K_READ(33) HSK_K_STEP(31, 2) side(31);
+    HSK_K_READ(34) HSK_K_STEP(32, 2) side(32);
+    HSK_K_READ(35) HSK_K_STEP(33, 2) side(33);
+    HSK_K_STEP(34, 1) side(34);
+    HSK_K_STEP(35, 0) side(35);
+#undef HSK_K_READ
+#undef HSK_K_STEP
+    static_assert(KC == 36, "the unrolled score sequence covers 36 chunks");
+    return sc;
+  };
+  // maximum over the valid rows of a tile, in log2 units, the same in lanes l and l ^ 32 (rows past the
+  // partition's end are set to -inf without a branch)
+  auto tile_max = [&](f32x16& sc, int T) {
+    const int rem = nrows - T * kTile;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sc[v] = 8 * (v >> 2) + 4 * h + (v & 3) < rem ? sc[v] : -INFINITY;
+    float tmax = sc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) tmax = fmaxf(tmax, sc[v]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+  };
+  // softmax weights of tile T against m_ref (set from tile 0 when set_ref), as the bf16 B operands of P.V
+  bool over = false;
+  auto softmax = [&](f32x16 sc, int T, bool set_ref, bf16x8 (&pf)[2]) {
+    const float tmax = tile_max(sc, T);
+    m_ref = set_ref && T == 0 ? tmax : m_ref;
+    over |= tmax > m_ref + 64.f;
+    const float mneg = -m_ref;
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(sc[v], a.scale_log2, mneg));
+      psum += pv;
+      pf[v >> 3][v & 7] = (__bf16)pv;
+    }
+    l_run += psum;
+  };
+  // O^T += V^T P over one tile: step 2 cb + ch (column block cb, chunk ch) multiplies two transposing reads
+  // (parts 0 and 1: 8 rows of V) by P; the reads run two steps ahead, from eight base registers per tile
+  auto pv = [&](const HSK_LDS char* tile, const bf16x8 (&pf)[2]) {
+    const uint32_t t0 = (uint32_t)(uintptr_t)tile;
+    const uint32_t v000 = t0 + vb[0][0][0], v001 = t0 + vb[0][0][1], v010 = t0 + vb[0][1][0],
+                   v011 = t0 + vb[0][1][1], v100 = t0 + vb[1][0][0], v101 = t0 + vb[1][0][1],
+                   v110 = t0 + vb[1][1][0], v111 = t0 + vb[1][1][1];
+    i16x4 vlo[3], vhi[3];
+#define HSK_V_READ(S)                                                                                      \
+  {                                                                                                       \
+    constexpr int cb_ = (S) >> 1, ch_ = (S)&1;                                                            \
+    const uint32_t b0_ = ch_ ? ((cb_ & 1) ? v101 : v100) : ((cb_ & 1) ? v001 : v000);                     \
+    const uint32_t b1_ = ch_ ? ((cb_ & 1) ? v111 : v110) : ((cb_ & 1) ? v011 : v010);                     \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vlo[(S) % 3]) : "v"(b0_), "i"((cb_ >> 1) * 4096) : "memory"); \
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(vhi[(S) % 3]) : "v"(b1_), "i"((cb_ >> 1) * 4096) : "memory"); \
+  }
+#define HSK_V_STEP(S, WAIT)                                                                                \
+  {                                                                                                       \
+    asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(vlo[(S) % 3]), "+v"(vhi[(S) % 3]) : "i"(WAIT));           \
+    const bf16x8 vf_ = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[(S) % 3], vhi[(S) % 3], 0, 1, 2, 3, 4, 5, 6, 7)); \
+    oacc[(S) >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf_, pf[(S)&1], oacc[(S) >> 1], 0, 0, 0);  \
+  }
+    HSK_V_READ(0) HSK_V_READ(1)
+    HSK_V_READ(2) HSK_V_STEP(0, 4)
+    HSK_V_READ(3) HSK_V_STEP(1, 4)
+    HSK_V_READ(4) HSK_V_STEP(2, 4)
+    HSK_V_READ(5) HSK_V_STEP(3, 4)
+    HSK_V_READ(6) HSK_V_STEP(4, 4)
+    HSK_V_READ(7) HSK_V_STEP(5, 4)
+    HSK_V_READ(8) HSK_V_STEP(6, 4)
+    HSK_V_READ(9) HSK_V_STEP(7, 4)
+    HSK_V_READ(10) HSK_V_STEP(8, 4)
+    HSK_V_READ(11) HSK_V_STEP(9, 4)
+    HSK_V_READ(12) HSK_V_STEP(10, 4)
+    HSK_V_READ(13) HSK_V_STEP(11, 4)
+    HSK_V_READ(14) HSK_V_STEP(12, 4)
+    HSK_V_READ(15) HSK_V_STEP(13, 4)
+    HSK_V_READ(16) HSK_V_STEP(14, 4)
+    HSK_V_READ(17) HSK_V_STEP(15, 4)
+    HSK_V_READ(18) HSK_V_STEP(16, 4)
+    HSK_V_READ(19) HSK_V_STEP(17, 4)
+    HSK_V_READ(20) HSK_V_STEP(18, 4)
+    HSK_V_READ(21) HSK_V_STEP(19, 4)
+    HSK_V_READ(22) HSK_V_STEP(20, 4)
+    HSK_V_READ(23) HSK_V_STEP(21, 4)
+    HSK_V_READ(24) HSK_V_STEP(22, 4)
+    HSK_V_READ(25) HSK_V_STEP(23, 4)
+    HSK_V_READ(26) HSK_V_STEP(24, 4)
+    HSK_V_READ(27) HSK_V_STEP(25, 4)
+    HSK_V_READ(28) HSK_V_STEP(26, 4)
+    HSK_V_READ(29) HSK_V_STEP(27, 4)
+    HSK_V_READ(30) HSK_V_STEP(28, 4)
+    HSK_V_READ(31) HSK_V_STEP(29, 4)
+    HSK_V_STEP(30, 2)
+    HSK_V_STEP(31, 0)
+#undef HSK_V_READ
+#undef HSK_V_STEP
+    static_assert(CB == 16, "the unrolled P.V sequence covers 32 steps");
+  };
+  // The full pass is software-pipelined by one tile: iteration T computes S of tile T + 1 and, in the same
+  // straight-line block, the softmax and P.V of tile T, so the matrix cores are fed while the softmax of
+  // the previous tile runs.  Tile T + 3 is loaded into the buffer of tile T - 1, which every wave has
+  // finished with at the barrier that also makes tile T + 1 visible.
+  auto no_side = [](int) {};
+  auto full_pass = [&](bool set_ref, bool issued) {
+    if (!issued) {
+#pragma unroll
+      for (int T = 0; T < kBufs32 - 1; ++T)
+        if (T < ntiles) issue(T, T);
+    }
+    // (loads complete in order: when the query block was read after the first tiles, this wait also
+    // covers those tiles, and the products wait for the query block themselves)
+    wait_tile_barrier32(MY * min(ntiles - 1, kBufs32 - 2));
+    f32x16 sc = scores((const HSK_LDS char*)&s_tile[0][0], no_side);
+    bf16x8 pf[2];
+    for (int T = 0; T + 1 < ntiles; ++T) {
+      wait_tile_barrier32(MY * min(ntiles - 2 - T, 1));
+      if (T + kBufs32 - 1 < ntiles) issue(T + kBufs32 - 1, (T + kBufs32 - 1) % kBufs32);
+      // the softmax of tile T in six pieces between the products of S(T + 1): masks and maxima, the
+      // cross-lane maximum and reference, then the exponentials four at a time and the bf16 packing
+      const int rem = nrows - T * kTile;
+      float tmx = -INFINITY, mneg = 0.f, psum = 0.f, pw[16];
+      auto side = [&](int step) {
+        if ((step & 3) != 3 || step > 23) return;
+        const int piece = step >> 2;
+        if (piece <= 1) {
+#pragma unroll
+          for (int v = 8 * piece; v < 8 * piece + 8; ++v) {
+            sc[v] = 8 * (v >> 2) + 4 * h + (v & 3) < rem ? sc[v] : -INFINITY;
+            tmx = fmaxf(tmx, sc[v]);
+          }
+          if (piece == 1) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx), __float_as_uint(tmx), false, false);
+            const float tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+            m_ref = set_ref && T == 0 ? tmax : m_ref;
+            over |= tmax > m_ref + 64.f;
+            mneg = -m_ref;
+          }
+        } else {
+#pragma unroll
+          for (int v = 4 * (piece - 2); v < 4 * (piece - 2) + 4; ++v) {
+            pw[v] = __builtin_amdgcn_exp2f(fmaf(sc[v], a.scale_log2, mneg));
+            psum += pw[v];
+          }
+          if (piece == 5) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) pf[v >> 3][v & 7] = (__bf16)pw[v];
+            l_run += psum;
+          }
+        }
+      };
+      const f32x16 sn = scores((const HSK_LDS char*)&s_tile[(T + 1) % kBufs32][0], side);
+      pv((const HSK_LDS char*)&s_tile[T % kBufs32][0], pf);
+      sc = sn;
+    }
+    softmax(sc, ntiles - 1, set_ref, pf);
+    pv((const HSK_LDS char*)&s_tile[(ntiles - 1) % kBufs32][0], pf);
+  };
+  // the slow path's first pass: the true maximum over the partition's tiles
+  auto max_pass = [&]() {
+#pragma unroll
+    for (int T = 0; T < kBufs32 - 1; ++T)
+      if (T < ntiles) issue(T, T);
+    for (int T = 0; T < ntiles; ++T) {
+      wait_tile_barrier32(MY * min(ntiles - 1 - T, kBufs32 - 2));
+      if (T + kBufs32 - 1 < ntiles) issue(T + kBufs32 - 1, (T + kBufs32 - 1) % kBufs32);
+      f32x16 sc = scores((const HSK_LDS char*)&s_tile[T % kBufs32][0], no_side);
+      const float tmax = tile_max(sc, T);
+      m_ref = T == 0 ? tmax : fmaxf(m_ref, tmax);
+    }
+  };
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+  if (ntiles > 0) full_pass(true, true);  // every partition the planner makes has rows
+  // every wave's loads are done (the last wait is for all of them) and every LDS read of the tiles is done;
+  // any wave over the bound makes the workgroup redo the partition
+  __syncthreads();
+  if (__syncthreads_or(over)) {
+    max_pass();
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
+    l_run = 0.f;
+    over = false;
+    full_pass(false, false);
+  }
+  const float m_run = m_ref;
+
+  // epilogue: lane holds head hbase + j, columns 32 cb + 8 (v / 4) + 4 h + v % 4.  The bf16 rows of the
+  // wave's 32 heads are staged in the (now idle) tile buffers, 1,040 bytes apart so that the 32 heads of a
+  // column step fall in different banks, then written out as whole 1,024-byte rows, 16 bytes per lane.
+  const float l = l_run + __shfl_xor(l_run, 32, 64);
+  const int head = hbase + j;
+  const float inv = 1.f / l;
+  const int64_t ps = ((int64_t)rq * a.split + sp) * a.H + head;
+  constexpr int kRowStage = 1040;
+  __syncthreads();  // every wave is done with the tile buffers
+  HSK_LDS char* stage = (HSK_LDS char*)&s_tile[0][0] + wave * 32 * kRowStage;
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2 w;
+      w.x = pack_bf16(oacc[cb][4 * g4] * inv, oacc[cb][4 * g4 + 1] * inv);
+      w.y = pack_bf16(oacc[cb][4 * g4 + 2] * inv, oacc[cb][4 * g4 + 3] * inv);
+      *(HSK_LDS u32x2*)(stage + j * kRowStage + (32 * cb + 8 * g4 + 4 * h) * 2) = w;
+    }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's staged rows are written
+  __builtin_amdgcn_wave_barrier();
+  {
+    // the wave's 32 output rows are contiguous: [head][512] bf16 from head hbase
+    const int64_t row0 = a.split == 1 ? (int64_t)rq * a.H + hbase : ((int64_t)rq * a.split + sp) * a.H + hbase;
+    char* dst = (char*)(a.split == 1 ? a.out : a.po) + row0 * kMlaDv * 2;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const u32x4 v = *(const HSK_LDS u32x4*)(stage + i * kRowStage + lane * 16);
+      *(u32x4*)(dst + (int64_t)i * kMlaDv * 2 + lane * 16) = v;
+    }
+  }
+  if (a.split > 1 && h == 0) {
+    a.pm[ps] = m_run * kLn2;
+    a.pl[ps] = l;
   }
 }
 
@@ -607,7 +1013,7 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
   const float inv = 1.f / l;
-  const uint32_t w = (uint32_t)f2bf16(o0 * inv) | ((uint32_t)f2bf16(o1 * inv) << 16);
+  const uint32_t w = pack_bf16(o0 * inv, o1 * inv);
   if (a.split == 1) {
     *(uint32_t*)(a.out + ((int64_t)r * a.H + head) * 128 + 2 * lane) = w;
     return;
@@ -679,10 +1085,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
   }
   if (mine) {
     u32x4 o;
-    o.x = (uint32_t)f2bf16(acc[0]) | ((uint32_t)f2bf16(acc[1]) << 16);
-    o.y = (uint32_t)f2bf16(acc[2]) | ((uint32_t)f2bf16(acc[3]) << 16);
-    o.z = (uint32_t)f2bf16(acc[4]) | ((uint32_t)f2bf16(acc[5]) << 16);
-    o.w = (uint32_t)f2bf16(acc[6]) | ((uint32_t)f2bf16(acc[7]) << 16);
+    o.x = pack_bf16(acc[0], acc[1]);
+    o.y = pack_bf16(acc[2], acc[3]);
+    o.z = pack_bf16(acc[4], acc[5]);
+    o.w = pack_bf16(acc[6], acc[7]);
     *(u32x4*)(a.out + ((int64_t)rq * a.H + h) * dv + 8 * lane) = o;
   }
 }
@@ -691,6 +1097,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
 struct AttnPlan {
   int split, rows_per_split;
   int nhb, npair, hgroups;  // MLA: 16-head blocks per wave pair, pairs per workgroup, head groups
+  int nw32;                 // MLA with heads % 64 == 0: waves (32 heads each) of mla32_kernel, same head groups
   int64_t po_bytes, pm_bytes, scratch;
 };
 
@@ -707,6 +1114,8 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
     const int units = d->heads / (16 * p->nhb);
     p->npair = units % 4 == 0 ? 4 : units % 2 == 0 ? 2 : 1;
     p->hgroups = units / p->npair;
+    // 32 heads per wave: 4 waves when the heads come in 128s, else 2 (64s); the head groups are the same
+    p->nw32 = d->heads % 128 == 0 ? 4 : d->heads % 64 == 0 ? 2 : 0;
     const int min_split = (k + max_rows - 1) / max_rows;
     if (d->split > 0) {
       p->split = d->split;
@@ -752,6 +1161,16 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
   p->scratch = p->po_bytes + 2 * p->pm_bytes;
   if (p->scratch < 256) p->scratch = 256;
   return true;
+}
+
+template <int NW>
+static void launch_mla32(MlaArgs m, const AttnPlan& p, int64_t RQ, hipStream_t s) {
+  const int64_t G = (int64_t)p.split * p.hgroups;
+  m.hgroups = p.hgroups;
+  m.RQ = (int32_t)RQ;
+  m.xcd_groups = (G > 1 && RQ >= 8) ? (int32_t)G : 0;
+  const int64_t blocks = m.xcd_groups ? 8 * G * ((RQ + 7) / 8) : G * RQ;
+  hipLaunchKernelGGL((mla32_kernel<NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, s, m);
 }
 
 // Fills the launch fields of m (head groups, queries, XCD grouping) and launches the MLA kernel.
@@ -811,7 +1230,9 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
     m.split = p.split; m.rows_per_split = p.rows_per_split;
     m.scale_log2 = d->scale * kLog2e;
     m.fill = nullptr; m.host = nullptr; m.host_req_stride = 0;
-    if (p.nhb == 2 && p.npair == 4) launch_mla<2, 4>(m, p, RQ, s);
+    if (p.nw32 == 4) launch_mla32<4>(m, p, RQ, s);
+    else if (p.nw32 == 2) launch_mla32<2>(m, p, RQ, s);
+    else if (p.nhb == 2 && p.npair == 4) launch_mla<2, 4>(m, p, RQ, s);
     else if (p.nhb == 2 && p.npair == 2) launch_mla<2, 2>(m, p, RQ, s);
     else if (p.nhb == 2) launch_mla<2, 1>(m, p, RQ, s);
     else launch_mla<1, 1>(m, p, RQ, s);

@@ -376,9 +376,11 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* desc, const void* d_q, co
  * call fetches straight from the pinned host rows and writes each of them once into its pool row, so the
  * host reads overlap the attention over resident rows instead of preceding it (the overlap of IO with
  * computation of HiSparse section 3.5, within one layer).  Locations, statistics, pool contents and the
- * miss plan are those of hsk_resolve_step; d_out is that of hsk_sparse_decode_attn at the same locations
- * (bit-identical when both plan the same partitions, which they do whenever hsk_sparse_decode_attn's
- * partitions hold at most 1,024 rows).
+ * miss plan are those of hsk_resolve_step; d_out is attention over the same rows as hsk_sparse_decode_attn
+ * with the same partitions (whenever hsk_sparse_decode_attn's partitions hold at most 1,024 rows), equal to
+ * it bit for bit when the heads are not a multiple of 64 (both then run the same kernel) and within bf16
+ * rounding otherwise (hsk_sparse_decode_attn then runs its 32-heads-per-wave kernel, which sums in another
+ * order).
  *   d_sel, d_locs, d_stats: as hsk_resolve_step with Qmax = 1 (no query counts).
  *   desc: an HSK_ATTN_MLA descriptor with num_requests, top_k and row_elems * 2 equal to the store's
  *         requests, top_k and row_bytes, row_elems = dk, max_queries = 1; its partitions hold at most

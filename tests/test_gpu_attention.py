@@ -22,11 +22,13 @@ def _bf16(x: np.ndarray) -> np.ndarray:
         .view(np.uint16)
 
 
-def _run_mla(R, Q, H, k, n_rows, split=0, nq=None, seed=0, row_elems=576, q_scale=1.0):
+def _run_mla(R, Q, H, k, n_rows, split=0, nq=None, seed=0, row_elems=576, q_scale=1.0, make=None):
     rng = np.random.default_rng(seed)
     rows = _bf16(rng.standard_normal((n_rows, row_elems)))
     q = _bf16(q_scale * rng.standard_normal((R, Q, H, 576)))
     locs = rng.integers(0, n_rows, size=(R, Q, k)).astype(np.int32)
+    if make is not None:
+        rows, q, locs = make(rng, rows, q, locs)
     ad = hsk.mla_desc(requests=R, max_queries=Q, heads=H, dk=576, dv=512, top_k=k, row_elems=row_elems,
                       scale=576 ** -0.5, split=split)
     nb = hsk.attn_scratch_bytes(ad)
@@ -66,6 +68,30 @@ def test_mla_split_and_ragged_k(k, split):
     """Ragged last tiles, one row, one partition (direct bf16 output), uneven forced splits, partitions
     that end inside a tile, and k larger than one partition may hold (forced to several)."""
     _run_mla(R=2, Q=2, H=32, k=k, n_rows=5000, split=split, seed=k + split)
+
+
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("k,split", [(1, 0), (31, 0), (33, 1), (100, 3), (257, 5), (2048, 1), (2048, 0)])
+def test_mla_32_head_waves_split_and_ragged_k(H, k, split):
+    """The 32-heads-per-wave kernel (heads in 64s or 128s): ragged last tiles, one row, one partition,
+    uneven forced splits, the full 2,048-row list."""
+    _run_mla(R=2, Q=1, H=H, k=k, n_rows=5000, split=split, seed=7 * k + split + H)
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_mla_score_jump_after_the_first_tile(H):
+    """Scores that rise by far more than 2^64 above the first tile's maximum (one row of a late tile aligned
+    with every head's query): the workgroup redoes its partition against the true maximum, and the result
+    (dominated by that row) still matches the fp64 oracle; a partition without the jump is unaffected."""
+    def make(rng, rows, q, locs):
+        rows = _bf16(0.05 * rng.standard_normal((rows.shape[0], rows.shape[1])))
+        qf = synth.bf16_to_f32(q).astype(np.float32)
+        big = 3.0 * np.sign(qf[0, 0, 0])                   # aligned with head 0's query, large for all heads
+        rows[17] = _bf16(np.concatenate([big, np.zeros(rows.shape[1] - 576)]))
+        locs = locs.copy()
+        locs[0, 0, 200] = 17                               # a late tile of the first partition of request 0
+        return rows, _bf16(np.abs(qf) * np.sign(qf[0, 0, 0])), locs
+    _run_mla(R=2, Q=1, H=H, k=300, n_rows=1000, split=2, seed=H, make=make)
 
 
 def test_mla_partial_queries_and_wide_rows():

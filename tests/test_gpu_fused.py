@@ -2,8 +2,10 @@
 
 Two identical stores run the same selections, one through hsk_resolve_step + hsk_sparse_decode_attn and
 one through hsk_resolve_attend: locations, statistics, miss plans, metadata and pool bytes must be
-identical, and the attention outputs bit-identical (same partitions, same bytes, same arithmetic).  Both
-are also checked against the CPU oracle (indexing bit-exact, attention within 1e-2 + 2e-2 |ref|).
+identical; both attention outputs are checked against the CPU oracle (indexing bit-exact, attention
+within 1e-2 + 2e-2 |ref|).  The outputs agree bit for bit where both calls run the same kernel (heads not
+in multiples of 64); with heads in 64s the separate call runs the 32-heads-per-wave kernel, whose sums are
+accumulated in another order.
 """
 import numpy as np
 import pytest
@@ -37,7 +39,7 @@ FUSED_CASES = {
 
 
 @pytest.mark.parametrize("case", list(FUSED_CASES))
-def test_fused_matches_unfused_bit_for_bit(case):
+def test_fused_matches_unfused(case):
     w = synth.WORKLOADS["tiny"].scaled(**FUSED_CASES[case], seed=6100 + len(case))
     hu, hf = _pair(w, steps=5)
     for t in range(hu.steps):
@@ -50,7 +52,9 @@ def test_fused_matches_unfused_bit_for_bit(case):
             if f != "pad":
                 assert np.array_equal(ru["stats"][f], rf["stats"][f]), f
         hf.check_bytes(rf)
-        assert torch.equal(out_u, rf["out"]), "fused output differs from resolve + attention"
+        if w.heads % 64:
+            assert torch.equal(out_u, rf["out"]), "fused output differs from resolve + attention"
+        hu.check_attention(0, t, ru, out_u)
         err = hf.check_attention(0, t, rf, rf["out"])
         log(f"[fused {case}] step {t}: misses={int(rf['stats']['n_miss'].sum())} attn err {err[0]:.2e}")
     hu.close()
