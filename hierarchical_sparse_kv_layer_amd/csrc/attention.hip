@@ -919,8 +919,11 @@ struct GqaArgs {
   float scale_log2;
 };
 
+constexpr int kGqaMaxPages = 1024;             // pages of one partition (their locations are kept in LDS)
+
 __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_tile[2][kGqaTileBytes];
+  __shared__ int32_t s_loc[kGqaMaxPages];
   const int sp = blockIdx.x, unit = blockIdx.y;
   const int r = unit / a.Hkv, grp = unit % a.Hkv;
   const int hg = a.H / a.Hkv;
@@ -943,6 +946,11 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) qv[i] = __builtin_bit_cast(bf16x2, qh[i]);
   }
+  // the partition's page locations go to LDS first: a tile's loads then wait for an LDS read, not for a
+  // global one (whose in-order counter would also make them wait for the loads already in flight)
+  for (int x = threadIdx.x; x < npages; x += 256) s_loc[x] = locs[x];
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
   // DMA: wave-wide load j covers tile tokens 2j, 2j+1; lane l copies 16-byte slot l & 31 of token 2j + l / 32:
   // slots 0..15 are the key chunks, stored at position chunk ^ (token & 15), slots 16..31 the value chunks
@@ -955,7 +963,7 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
       int tok = T * kGqaTok + t;
       tok = tok < ntok ? tok : 0;  // past the end: re-read token 0 (masked)
       const int chunk_off = pos < 16 ? ((pos ^ (t & 15)) << 4) : 256 + ((pos - 16) << 4);
-      const char* src = a.pool + (int64_t)locs[tok / pt] * a.row_bytes + (tok % pt) * kGqaTokBytes + chunk_off;
+      const char* src = a.pool + (int64_t)s_loc[tok / pt] * a.row_bytes + (tok % pt) * kGqaTokBytes + chunk_off;
       const uint32_t m0 = lds0 + b * kGqaTileBytes + j * 1024;
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
     }
@@ -1144,13 +1152,15 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
     if (d->split > 0) {
       p->split = d->split;
     } else {
-      // about four workgroups per CU (a workgroup holds 64 KB of LDS)
+      // about four workgroups per CU at a time (a workgroup holds 68 KB of LDS: two fit)
       const int64_t base = (int64_t)d->num_requests * d->kv_heads;
       int64_t s = (1024 + base - 1) / base;
       s = s < 1 ? 1 : s;
+      s = s < (k + kGqaMaxPages - 1) / kGqaMaxPages ? (k + kGqaMaxPages - 1) / kGqaMaxPages : s;
       p->split = (int)(s > k ? k : s);
     }
     p->rows_per_split = (k + p->split - 1) / p->split;
+    if (p->rows_per_split > kGqaMaxPages) return false;
   } else {
     return false;
   }
