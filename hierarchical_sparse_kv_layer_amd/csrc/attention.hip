@@ -556,7 +556,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
   for (int x = tid; x < nrows; x += NT) s_loc[x] = locs[x];
   __syncthreads();
-  // The first tiles' loads are issued before the query block is read, so the two latencies overlap.
+  // The query block is requested first, then the first tiles: loads of a wave complete in order, so the
+  // first score products (which wait for the query chunks as the compiler counts them, i.e. for
+  // everything issued before each chunk) wait for the query block and only as much of the tiles as
+  // precedes each chunk's turn, instead of for all three tiles.
   bf16x8 qf[KC];
 
   // LDS offsets.  K: row j, chunk 2c + h; for c = 4 u + w that is chunk group u (4,096 bytes further per u)
@@ -602,14 +605,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
     }
   };
-#pragma unroll
-  for (int T = 0; T < kBufs32 - 1; ++T)
-    if (T < ntiles) issue(T, T);
   {
     const uint16_t* qb = a.q + ((int64_t)rq * a.H + hbase + j) * kMlaDk + 8 * h;
 #pragma unroll
     for (int c = 0; c < KC; ++c) qf[c] = *(const bf16x8*)(qb + 16 * c);
   }
+#pragma unroll
+  for (int T = 0; T < kBufs32 - 1; ++T)
+    if (T < ntiles) issue(T, T);
   // The scores of a wave's head are weighed against one reference maximum m_ref, the maximum of the
   // partition's first tile, and the output is never rescaled inside the loop (rescaling 256 accumulators
   // held in the accumulation registers costs more than the loop can afford).  exp2(s - m_ref) stays below
@@ -776,8 +779,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
       for (int T = 0; T < kBufs32 - 1; ++T)
         if (T < ntiles) issue(T, T);
     }
-    // (loads complete in order: when the query block was read after the first tiles, this wait also
-    // covers those tiles, and the products wait for the query block themselves)
+    // (loads complete in order: this wait for tile 0 also covers the query block read before it, when
+    // the first tiles were issued with it)
     wait_tile_barrier32(MY * min(ntiles - 1, kBufs32 - 2));
     f32x16 sc = scores((const HSK_LDS char*)&s_tile[0][0], no_side);
     bf16x8 pf[2];
@@ -1037,22 +1040,77 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
 // ------------------------------------------------------------------------------------------------------
 // combine: one wave per (query, head), 4 waves per block.  Partition s holds its output normalised by its
 // own sum l_s, in bf16, with its maximum m_s: out = sum_s w_s o_s with w_s = l_s e^(m_s - M) / L and
-// L = sum_s l_s e^(m_s - M).  The weights come from a lane-parallel max and sum over the partitions; lane
-// x owns the 16-byte chunk x (8 values) of the dv outputs (dv <= 512), read four partitions at a time.
+// L = sum_s l_s e^(m_s - M).  Lane x owns the 16-byte chunk x (8 values) of the dv outputs (dv <= 512).
+// Up to four partitions (the usual case) take one round trip: the rows, maxima and sums of all four are
+// requested before any is used.  More partitions take a lane-parallel max and sum, then four rows at a time.
+// With xcd set, block b serves query 8 ((b / 8) / (H / 4)) + b mod 8: blocks are dealt to the 8 XCDs by
+// id mod 8, so a query's combine runs on the XCD whose MLA workgroups wrote its partials (same grouping as
+// mla_block), and reads them from that XCD's L2 where they are still held.
 // ------------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xcd) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t RQ = (int64_t)a.R * a.Qmax;
-  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-  if (item >= RQ * a.H) return;
-  const int rq = (int)(item / a.H), h = (int)(item % a.H);
+  int64_t rq;
+  int h;
+  if (xcd) {
+    const int hb = a.H >> 2;
+    const int64_t j = blockIdx.x >> 3;
+    rq = (j / hb) * 8 + (blockIdx.x & 7);
+    h = 4 * (int)(j % hb) + wave;
+    if (rq >= RQ) return;
+  } else {
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= RQ * a.H) return;
+    rq = item / a.H;
+    h = (int)(item % a.H);
+  }
   if (a.nq) {
-    const int r = rq / a.Qmax, j = rq % a.Qmax;
+    const int r = (int)(rq / a.Qmax), j = (int)(rq % a.Qmax);
     if (j >= a.nq[r]) return;
   }
   const int S = a.split;
-  const int64_t p0 = (int64_t)rq * S * a.H + h;  // partition s of (rq, h) is p0 + s * H
+  const int64_t p0 = rq * S * a.H + h;  // partition s of (rq, h) is p0 + s * H
+  const bool mine = lane < (dv >> 3);
+  if (S <= 4) {
+    float mu[4], lu[4];
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t ps = p0 + (int64_t)(u < S ? u : 0) * a.H;
+      mu[u] = u < S ? a.pm[ps] : -INFINITY;
+      lu[u] = u < S ? a.pl[ps] : 0.f;
+      v[u] = (u < S && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float M = fmaxf(fmaxf(mu[0], mu[1]), fmaxf(mu[2], mu[3]));
+    float w[4], L = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      w[u] = mu[u] == -INFINITY ? 0.f : __expf(mu[u] - M) * lu[u];
+      L += w[u];
+    }
+    const float invL = 1.f / L;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wu = w[u] * invL;
+      const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(x[e] << 16) * wu;
+        acc[2 * e + 1] += __uint_as_float(x[e] & 0xffff0000u) * wu;
+      }
+    }
+    if (mine) {
+      u32x4 o;
+      o.x = pack_bf16(acc[0], acc[1]);
+      o.y = pack_bf16(acc[2], acc[3]);
+      o.z = pack_bf16(acc[4], acc[5]);
+      o.w = pack_bf16(acc[6], acc[7]);
+      *(u32x4*)(a.out + (rq * a.H + h) * dv + 8 * lane) = o;
+    }
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += 64)
     if (s0 + lane < S) M = fmaxf(M, a.pm[p0 + (int64_t)(s0 + lane) * a.H]);
@@ -1068,7 +1126,6 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
   const float invL = 1.f / L;
-  const bool mine = lane < (dv >> 3);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += 4) {
     float w[4];
@@ -1097,8 +1154,15 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv) {
     o.y = pack_bf16(acc[2], acc[3]);
     o.z = pack_bf16(acc[4], acc[5]);
     o.w = pack_bf16(acc[6], acc[7]);
-    *(u32x4*)(a.out + ((int64_t)rq * a.H + h) * dv + 8 * lane) = o;
+    *(u32x4*)(a.out + (rq * a.H + h) * dv + 8 * lane) = o;
   }
+}
+
+// Grid of combine_kernel: blocks of four (query, head) waves, XCD-grouped when the heads come in fours.
+static void launch_combine(const AttnArgs& a, int64_t RQ, hipStream_t s) {
+  const int xcd = (a.H % 4 == 0 && RQ >= 8) ? 1 : 0;
+  const int64_t blocks = xcd ? 8 * (int64_t)(a.H / 4) * ((RQ + 7) / 8) : (RQ * a.H + 3) / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, a.dv, xcd);
 }
 
 // Launch plan of one attention call: split-k partitions and, for MLA, the wave-pair shape.
@@ -1258,7 +1322,7 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
     HSK_HIP(hipGetLastError());
     if (p.split == 1) return HSK_OK;
   }
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((RQ * d->heads + 3) / 4)), dim3(256), 0, s, a, d->dv);
+  launch_combine(a, RQ, s);
   HSK_HIP(hipGetLastError());
   return HSK_OK;
 }
@@ -1304,7 +1368,7 @@ hsk_status launch_mla_fused(const hsk_attn_desc* d, const void* q, const char* p
   a.dk = d->dk; a.dv = d->dv; a.k = d->top_k; a.row_elems = d->row_elems; a.page_tokens = 1;
   a.split = p.split; a.rows_per_split = p.rows_per_split; a.scale = d->scale;
   a.po = m.po; a.pm = m.pm; a.pl = m.pl;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((RQ * d->heads + 3) / 4)), dim3(256), 0, s, a, d->dv);
+  launch_combine(a, RQ, s);
   HSK_HIP(hipGetLastError());
   return HSK_OK;
 }
