@@ -41,16 +41,27 @@ __device__ __forceinline__ void claim_min(int32_t* p, int32_t v) {
   __hip_atomic_fetch_min(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele within each row of 16 lanes by DPP row
+// shifts (lanes without a source add 0), then each row adds the totals of the rows before it, read with
+// readlane from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 // Exclusive prefix sum of small non-negative ints over the workgroup in thread order (LDS-only barriers:
-// global stores of the caller stay in flight).  Must be called by every thread of the block.
+// global stores of the caller stay in flight).  Must be called by every thread of the block.  The wave
+// totals go to s_wsum, which has no barrier after its reads: two scans in a row use different buffers (a
+// scan's first barrier is passed only once every thread has read the buffer of the scan before).
 __device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_wsum[wave] = x;
   lds_barrier();
   int base = 0, tot = 0;
@@ -60,7 +71,6 @@ __device__ __forceinline__ int block_sum_scan(int v, int* total, int* s_wsum) {
     base += (w < wave) ? c : 0;
     tot += c;
   }
-  lds_barrier();
   *total = tot;
   return base + x - v;
 }
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   __shared__ uint16_t s_victim[HSK_MAX_HOT_SLOTS];
   __shared__ uint16_t s_neworder[HSK_MAX_HOT_SLOTS];
   __shared__ int32_t s_key[HSK_MAX_HOT_SLOTS];
-  __shared__ int s_wsum[kResolveWaves];
+  __shared__ int s_wsum[2][kResolveWaves];
   __shared__ int s_cnt[4];
 
   const int r = blockIdx.x;
@@ -267,8 +277,9 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     bool first[kPer];
     int nfirst = 0;
     int32_t cv[kPer];
+    // only missing selections hold a claim to read back (all issued together; hits and direct rows skip)
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) cv[e] = rmw_read(&pt[pv[e]]);  // branch-free: all issued together
+    for (int e = 0; e < kPer; ++e) cv[e] = (fb + e < nsel && code[e] == kCodeMiss) ? rmw_read(&pt[pv[e]]) : 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       first[e] = false;
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
           fill[fb + e] = (code[e] == kCodeMiss || is_claim(code[e])) ? 2 * pv[e] + (first[e] ? 1 : 0) : -1;
     }
     int cnt;
-    int idx = m + block_sum_scan(nfirst, &cnt, s_wsum);
+    int idx = m + block_sum_scan(nfirst, &cnt, s_wsum[rd & 1]);
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
       if (first[e]) {
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   int nhit = 0;
   {
     const int hw = tid < nwords ? __popc(s_hit[tid]) : 0;
-    const int pre = block_sum_scan(hw, &nhit, s_wsum);
+    const int pre = block_sum_scan(hw, &nhit, s_wsum[0]);
     if (tid < nwords) s_hit_pre[tid] = pre;
   }
   const int free_slots = B - nhit;
@@ -369,7 +380,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       }
     }
     int tot;
-    int rank = block_sum_scan(cnt_nh, &tot, s_wsum);
+    int rank = block_sum_scan(cnt_nh, &tot, s_wsum[1]);
 #pragma unroll
     for (int e = 0; e < kSlotsPerThread; ++e) {
       if (sl[e] == 0xFFFF) continue;
@@ -387,7 +398,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   {
     const int vw = tid < nwords ? __popc(s_vic[tid]) : 0;
     int vtot;
-    const int pre = block_sum_scan(vw, &vtot, s_wsum);
+    const int pre = block_sum_scan(vw, &vtot, s_wsum[0]);
     if (tid < nwords) s_vic_pre[tid] = pre;
   }
   __syncthreads();
