@@ -903,7 +903,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 //            registers (v_dot2_f32_bf16 on bf16 pairs); the 16 key chunks of a token are XOR-swizzled by
 //            the token so that 16 lanes reading chunk i hit 16 different bank groups;
 //   softmax: online, fp32, exp2 domain, reference maximum moved only when exceeded by 2^8;
-//   P.V:     lane l owns value dims 2l, 2l+1 and walks the 64 tokens, each weight broadcast from its lane.
+//   P.V:     lane l owns value dims 2l, 2l+1 and walks the 64 tokens in pairs: the pair's weights (bf16)
+//            broadcast from one lane, the two tokens' values of a dim paired by a byte permute, v_dot2.
 // ------------------------------------------------------------------------------------------------------
 constexpr int kGqaTok = 64;                    // tokens per tile
 constexpr int kGqaTokBytes = 512;              // one token: K 128 bf16 | V 128 bf16
@@ -923,6 +924,19 @@ struct GqaArgs {
 };
 
 constexpr int kGqaMaxPages = 1024;             // pages of one partition (their locations are kept in LDS)
+
+// maximum over the 64 lanes: within each row of 16 lanes by DPP row shifts (a lane without a source keeps
+// its own value), then the four rows' last lanes by readlane
+__device__ __forceinline__ float wave_max(float x) {
+  int v = __float_as_int(x);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false))));
+  const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 15)), __int_as_float(__builtin_amdgcn_readlane(v, 31)));
+  const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(v, 47)), __int_as_float(__builtin_amdgcn_readlane(v, 63)));
+  return fmaxf(a, b);
+}
 
 __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
   __shared__ __attribute__((aligned(1024))) char s_tile[2][kGqaTileBytes];
@@ -996,9 +1010,7 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), qv[4 * i + 3], acc, false);
       }
       const float sc = T * kGqaTok + lane < ntok ? acc * a.scale_log2 : -INFINITY;
-      float tmax = sc;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o, 64));
+      const float tmax = wave_max(sc);
       if (tmax > m_run + 8.f) {  // wave-uniform: the reference maximum moves (always on the first tile)
         const float alpha = __builtin_amdgcn_exp2f(m_run - tmax);
         l_lane *= alpha;
@@ -1008,14 +1020,21 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
       }
       const float p = __builtin_amdgcn_exp2f(sc - m_run);
       l_lane += p;
-      // P.V: lane = value dims 2 lane, 2 lane + 1
+      // P.V: lane = value dims 2 lane, 2 lane + 1, tokens in pairs: lane t (t even) holds the weights of
+      // tokens t and t + 1 as one bf16 pair, broadcast by one readlane; the two tokens' values of each dim
+      // are paired with a byte permute and multiplied by v_dot2 (fp32 accumulation)
+      const float pn = __shfl_down(p, 1, 64);
+      const uint32_t pp = pack_bf16(p, pn);
       const HSK_LDS char* vt = tile + 256 + 4 * lane;
 #pragma unroll
-      for (int t = 0; t < kGqaTok; ++t) {
-        const float pt_ = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), t));
-        const uint32_t vw = *(const HSK_LDS uint32_t*)(vt + t * kGqaTokBytes);
-        o0 = fmaf(pt_, bf16lo(vw), o0);
-        o1 = fmaf(pt_, bf16hi(vw), o1);
+      for (int t = 0; t < kGqaTok; t += 2) {
+        const bf16x2 w = __builtin_bit_cast(bf16x2, (uint32_t)__builtin_amdgcn_readlane((int)pp, t));
+        const uint32_t v0 = *(const HSK_LDS uint32_t*)(vt + t * kGqaTokBytes);
+        const uint32_t v1 = *(const HSK_LDS uint32_t*)(vt + (t + 1) * kGqaTokBytes);
+        const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x05040100u);  // dim 2 lane of tokens t, t + 1
+        const uint32_t hi = __builtin_amdgcn_perm(v1, v0, 0x07060302u);  // dim 2 lane + 1
+        o0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lo), w, o0, false);
+        o1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hi), w, o1, false);
       }
     }
   }
