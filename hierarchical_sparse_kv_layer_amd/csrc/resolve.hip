@@ -183,6 +183,19 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       bad |= (pv[e] < 0) || ((int64_t)pv[e] >= n);
     }
   }
+  // With one round, the page-table words (and optional-page map entries) of this thread's selections are
+  // requested now, before the validation barrier, so the probe's latency overlaps it; positions are
+  // clamped into the request's rows for the address only (an invalid request returns at the barrier).
+  int32_t ptv[kPer], ovv[kPer];
+  if (one_round) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int32_t pc = (pv[e] < 0 || n <= 0) ? 0 : ((int64_t)pv[e] >= n ? (int32_t)(n - 1) : pv[e]);
+      ptv[e] = pt[pc];
+      const int64_t page = opt ? min((int64_t)(pc / a.P), a.max_pages - 1) : 0;
+      ovv[e] = opt ? opt[page] : -1;
+    }
+  }
   int32_t* fill = a.fill ? a.fill + (int64_t)r * total : nullptr;
   if (__syncthreads_or(bad)) {
     for (int f = tid; f < total; f += NT) {
@@ -213,15 +226,16 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       for (int e = 0; e < kPer; ++e) pv[e] = fb + e < nsel ? sel[fb + e] : 0;
     }
     // branch-free loads, all issued before any is used: the page-table word (and the optional-page map
-    // entry) of every selection, direct or not
-    int32_t ptv[kPer], ovv[kPer];
+    // entry) of every selection, direct or not (with one round they were requested before the barrier)
     bool pend[kPer];
+    if (!one_round) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) ptv[e] = pt[pv[e]];
+      for (int e = 0; e < kPer; ++e) ptv[e] = pt[pv[e]];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int64_t page = opt ? min((int64_t)(pv[e] / a.P), a.max_pages - 1) : 0;
-      ovv[e] = opt ? opt[page] : -1;
+      for (int e = 0; e < kPer; ++e) {
+        const int64_t page = opt ? min((int64_t)(pv[e] / a.P), a.max_pages - 1) : 0;
+        ovv[e] = opt ? opt[page] : -1;
+      }
     }
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -459,21 +473,18 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   }
   lds_barrier();
   for (int q = tid; q < B; q += NT) order[q] = s_neworder[q];
-  // class counts: wave sums first (1,024 same-address LDS atomics would serialise for microseconds)
+  // class counts: wave sums first (1,024 same-address LDS atomics would serialise for microseconds), two
+  // counts per word in 16-bit fields (a wave handles at most 64 x 4 x 16 = 4,096 selections), summed by
+  // the DPP scan and read from lane 63
   {
-    int c0 = my_tail, c1 = my_opt, c2 = my_hit_sel, c3 = my_miss_sel;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      c0 += __shfl_xor(c0, o, 64);
-      c1 += __shfl_xor(c1, o, 64);
-      c2 += __shfl_xor(c2, o, 64);
-      c3 += __shfl_xor(c3, o, 64);
-    }
+    const int c01 = wave_incl_scan(my_tail | (my_opt << 16));
+    const int c23 = wave_incl_scan(my_hit_sel | (my_miss_sel << 16));
+    const int w01 = __builtin_amdgcn_readlane(c01, 63), w23 = __builtin_amdgcn_readlane(c23, 63);
     if ((tid & 63) == 0) {
-      atomicAdd(&s_cnt[0], c0);
-      atomicAdd(&s_cnt[1], c1);
-      atomicAdd(&s_cnt[2], c2);
-      atomicAdd(&s_cnt[3], c3);
+      atomicAdd(&s_cnt[0], w01 & 0xFFFF);
+      atomicAdd(&s_cnt[1], w01 >> 16);
+      atomicAdd(&s_cnt[2], w23 & 0xFFFF);
+      atomicAdd(&s_cnt[3], w23 >> 16);
     }
   }
   lds_barrier();
