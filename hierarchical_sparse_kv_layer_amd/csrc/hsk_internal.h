@@ -57,6 +57,9 @@ struct ResolveArgs {
   int64_t opt_base;   // first optional row: R*B + R*T
   int64_t stg_base;   // first staging row: R*B + R*T + opt_pool_pages*page_rows
   int32_t* fill;       // nullable: per-selection host source for a fused resolve + attend (see resolve.hip)
+  const char* host;    // nullable: host rows of (host source, request 0); set, the kernel copies the misses
+  char* pool;          // row 0 of the source's pool (the copies' destination)
+  int64_t host_req_stride;  // bytes between requests in the host rows
   int32_t plan_cap;
   int32_t R, B, T, P, S, Qmax, k, row_bytes;
   uint32_t epoch;

@@ -18,8 +18,9 @@
 //     that list, skipping hit slots, yields the oldest unselected slots in order -- no sort, no atomics;
 //   * the new order is written as [unselected non-victims in old order][fills by slot][hits by slot],
 //     which is exactly the ascending (rec, slot) order once fills get 2e and hits 2e+1 (epochs increase).
-// The host-to-device copies of the missing rows run in gather_kernel, a second launch that spreads the rows
-// of all requests evenly over its waves so that enough 16-byte host reads are in flight to fill the PCIe link.
+// The host-to-device copies of the missing rows run at the end of the same kernel (each workgroup copies its
+// request's rows); gather_kernel, which spreads a plan's rows evenly over all its waves, replays a recorded
+// plan into another source's pool.
 #include <climits>
 
 #include "hsk_internal.h"
@@ -105,6 +106,7 @@ __device__ __forceinline__ int classify(const ResolveArgs& a, int r, int64_t n, 
 //   kCodeMiss         a missing position, before its claim is read back
 //   INT_MIN + f0      a repeated miss whose first occurrence is selection f0
 //   -2 - i            the first occurrence of distinct miss i (also stored at locs[f0] for repeats to read)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int32_t kCodeMiss = -1;
 constexpr int kPer = 4;                                   // contiguous selections per thread per round
 constexpr int kSlotsPerThread = HSK_MAX_HOT_SLOTS / kResolveThreads;
@@ -506,9 +508,52 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       a.stats[r] = st;
     }
   }
+
+  // ---- phase 6: this call's distinct missing rows, host -> pool ------------------------------------------
+  // The copy done by GPU threads (HiSparse section 3.4, phase 4), here by the resolving workgroup itself, so
+  // a resolve is one launch: zero-copy 16-byte loads of the pinned host rows over PCIe.  Wave w copies miss
+  // rows 4 w .. 4 w + 3, then the four rows kResolveWaves * 4 further on, and so on; a batch's positions are
+  // read first (written by phase 2 before this workgroup's barriers), then every chunk of the batch is loaded
+  // before any is stored.  64 workgroups x 16 waves keep megabytes of host reads in flight.
+  if (a.host != nullptr && m > 0) {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
+    const char* hreq = a.host + (int64_t)r * a.host_req_stride;
+    for (int i0 = 4 * wv; i0 < m; i0 += 4 * kResolveWaves) {
+      const u32x4* src[4];
+      u32x4* dst[4];
+      int nrow = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u;
+        const bool ok = i < m;
+        const int32_t p = ok ? ppos[i] : 0;
+        const int64_t d = !ok ? 0 : (i < v ? hot0 + s_victim[i] : stg0 + (i - v));
+        src[u] = (const u32x4*)(hreq + (int64_t)p * a.row_bytes);
+        dst[u] = (u32x4*)(a.pool + d * a.row_bytes);
+        nrow += ok;
+      }
+      for (int c0 = 0; c0 < cpr; c0 += 128) {
+        u32x4 buf[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = c0 + 64 * h + lane;
+            if (u < nrow && c < cpr) buf[u][h] = __builtin_nontemporal_load(src[u] + c);
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = c0 + 64 * h + lane;
+            if (u < nrow && c < cpr) dst[u][c] = buf[u][h];
+          }
+      }
+    }
+  }
 }
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Copy one row of `chunks` 16-byte chunks with the 64 lanes of a wave: all loads first, then stores.
 __device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int chunks,

@@ -323,6 +323,7 @@ static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, c
   a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats;
   a.ctx = st->d_ctx + (size_t)source * st->d.num_requests; a.m = st->meta[source];
   a.err = st->d_err; a.fill = nullptr; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
+  a.host = nullptr; a.pool = nullptr; a.host_req_stride = 0;
   const int64_t R = st->d.num_requests;
   a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
   a.stg_base = stg_base_of(st->d, source);
@@ -338,20 +339,18 @@ hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const
   if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs) return HSK_EINVAL;
   if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
   hipStream_t s = (hipStream_t)stream;
-  const ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
-  HSK_HIP(launch_resolve(a, s));
-  st->last_epoch[source] = epoch;
+  ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
   if (st->d.gather_mode == HSK_GATHER_ZEROCOPY) {
+    // the resolving workgroups copy their requests' missing rows themselves (zero-copy host reads)
     void* pool;
     hsk_pool_base(st, source, &pool);
-    GatherArgs g;
     const int32_t hs = st->d.host_alias_sources ? 0 : source;
-    g.host = st->host[hs]; g.pool = (char*)pool;
-    g.plan_n = a.m.plan_n; g.plan_pos = a.m.plan_pos; g.plan_dst = a.m.plan_dst;
-    g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
-    g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
-    HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
+    a.host = st->host[hs];
+    a.pool = (char*)pool;
+    a.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
   }
+  HSK_HIP(launch_resolve(a, s));
+  st->last_epoch[source] = epoch;
   return HSK_OK;
 }
 

@@ -95,7 +95,7 @@ typedef struct hsk_desc {
   const int64_t* ctx_len;      /* host array [R]: n_r at creation (the imported history, every source),
                                   1 <= n_r <= max_ctx, n_r < 2^31; hsk_append_rows grows it per source */
   int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
-  int32_t gather_blocks;       /* workgroups (of 4 waves) of the gather kernel; 0 = automatic (384) */
+  int32_t gather_blocks;       /* workgroups (of 4 waves) of the plan-replay copy kernel; 0 = automatic (384) */
   int32_t staging_arenas;      /* 0: staging inside each source region; A >= 1: A arenas shared by the sources */
 } hsk_desc;
 
@@ -264,9 +264,9 @@ hsk_status hsk_residency_pages(hsk_store* store, int32_t req, int32_t* ids, uint
  *   d_locs  int32 [R][Qmax][k] device out: pool row of every selection, in selection order (-1 for
  *           queries j >= nq[r] and for rejected requests)
  *   d_stats hsk_stats [R] device out, or NULL
- * Queued on `stream`: one resolve kernel (one workgroup per request) then one gather kernel that copies
- * the distinct missing rows from pinned host memory into their slots with 16-byte loads.  Locations are
- * final when the stream reaches the end of the call.  The distinct missing rows and their destination
+ * Queued on `stream`: one resolve kernel, one workgroup per request, which ends by copying its request's
+ * distinct missing rows from pinned host memory into their slots with 16-byte zero-copy loads (none with
+ * HSK_GATHER_NO_IO).  Locations and pool rows are final when the stream reaches the end of the call.  The distinct missing rows and their destination
  * rows are kept as the source's miss plan (HiSparse section 3.5) until its next resolve call.
  */
 hsk_status hsk_resolve_step(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
