@@ -970,8 +970,36 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
   __syncthreads();
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];
   // DMA: wave-wide load j covers tile tokens 2j, 2j+1; lane l copies 16-byte slot l & 31 of token 2j + l / 32:
-  // slots 0..15 are the key chunks, stored at position chunk ^ (token & 15), slots 16..31 the value chunks
-  auto issue = [&](int T, int b) {
+  // slots 0..15 are the key chunks, stored at position chunk ^ (token & 15), slots 16..31 the value chunks.
+  // Pages of a power-of-two size up to a tile: a tile holds whole pages, so a lane's page within the tile and
+  // its byte offset in the page row are the same for every tile; a load then costs one page index, one
+  // location read and one 32 x 32 -> 64-bit multiply-add.  Other page sizes take the general form.
+  constexpr int kGqaSlots = kGqaDma / 4;
+  const bool whole_pages = (pt & (pt - 1)) == 0 && pt <= kGqaTok;
+  const int ppt = whole_pages ? kGqaTok / pt : 0;  // pages per tile
+  int pg_u[kGqaSlots];
+  const char* base_u[kGqaSlots];
+  if (whole_pages) {
+#pragma unroll
+    for (int u = 0; u < kGqaSlots; ++u) {
+      const int t = 2 * (wave + 4 * u) + (lane >> 5);
+      const int pos = lane & 31;
+      const int chunk_off = pos < 16 ? ((pos ^ (t & 15)) << 4) : 256 + ((pos - 16) << 4);
+      pg_u[u] = t / pt;
+      base_u[u] = a.pool + (t % pt) * kGqaTokBytes + chunk_off;
+    }
+  }
+  auto issue_pages = [&](int T, int b) {
+#pragma unroll
+    for (int u = 0; u < kGqaSlots; ++u) {
+      int page = T * ppt + pg_u[u];
+      page = page < npages ? page : 0;  // past the end: re-read page 0 (masked)
+      const char* src = base_u[u] + (uint64_t)(uint32_t)s_loc[page] * (uint32_t)a.row_bytes;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + b * kGqaTileBytes + (wave + 4 * u) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+    }
+  };
+  auto issue_any = [&](int T, int b) {
 #pragma unroll
     for (int u = 0; u < kGqaDma / 4; ++u) {
       const int j = wave + 4 * u;
@@ -981,9 +1009,13 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
       tok = tok < ntok ? tok : 0;  // past the end: re-read token 0 (masked)
       const int chunk_off = pos < 16 ? ((pos ^ (t & 15)) << 4) : 256 + ((pos - 16) << 4);
       const char* src = a.pool + (int64_t)s_loc[tok / pt] * a.row_bytes + (tok % pt) * kGqaTokBytes + chunk_off;
-      const uint32_t m0 = lds0 + b * kGqaTileBytes + j * 1024;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + b * kGqaTileBytes + j * 1024);  // wave-uniform
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
     }
+  };
+
+  auto issue = [&](int T, int b) {
+    if (whole_pages) issue_pages(T, b); else issue_any(T, b);
   };
 
   float m_run = -INFINITY, l_lane = 0.f, o0 = 0.f, o1 = 0.f;

@@ -163,7 +163,9 @@ def test_gqa_pages_split_and_ragged(k, split):
     _run_gqa(R=3, H=32, Hkv=8, k=k, n_pages=600, split=split, seed=k * 10 + split)
 
 
-@pytest.mark.parametrize("H,Hkv,pt", [(8, 8, 16), (16, 8, 16), (32, 8, 8), (32, 8, 32)])
+@pytest.mark.parametrize("H,Hkv,pt", [(8, 8, 16), (16, 8, 16), (32, 8, 8), (32, 8, 32), (32, 8, 1), (32, 8, 64),
+                                      (32, 8, 12), (32, 8, 128)])
 def test_gqa_group_sizes_and_page_sizes(H, Hkv, pt):
-    """1, 2 and 4 query heads per KV head; pages of 8 and 32 tokens; a large score range."""
+    """1, 2 and 4 query heads per KV head; a large score range; pages of 1 to 64 tokens (power-of-two sizes
+    up to a 64-token tile: whole pages per tile), and of 12 and 128 tokens (a page split across tiles)."""
     _run_gqa(R=2, H=H, Hkv=Hkv, k=40, n_pages=300, page_tokens=pt, seed=H + pt, q_scale=3.0)
