@@ -2,7 +2,7 @@
 """Benchmark: resolve + sparse decode attention, 100K-context batch-64 MLA decode (4 layers) on one GPU.
 
 One step = for each of the 4 layers: hsk_resolve_step (direct pass, hot-cache probe, LRU victims,
-metadata update, host->device gather of the distinct misses) then hsk_sparse_decode_attn (exact MLA
+metadata update, host->device copies of the distinct misses, all in one kernel) then hsk_sparse_decode_attn (exact MLA
 attention of 128 heads over the 2,048 resolved rows) -- the whole hot path, every launch through the
 C ABI.  Inputs (host KV rows, selections, queries) are seeded and synthetic (see synth/) and resident
 before the timed region; selections are the indexer stand-in (80% kept step to step, Zipf(1.1) fresh
@@ -170,7 +170,7 @@ def misses_only(hsk, synth, w, gather_blocks: int, calls: int = 12) -> dict:
     gbs = fetched / (ms * 1e-3) / 1e9
     return {"bytes_per_call": fetched, "ms_per_call": ms, "achieved_GBps": gbs, "host_link_peak_GBps": PCIE_PEAK_GBS,
             "frac_host_link": gbs / PCIE_PEAK_GBS, "status": status,
-            "note": "resolve kernel + zero-copy gather per call; bytes = distinct misses x 1152"}
+            "note": "resolve kernel with its zero-copy miss copies per call; bytes = distinct misses x 1152"}
 
 
 def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) -> dict:
@@ -759,7 +759,9 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip the hits-only, misses-only and memcpy runs")
     ap.add_argument("--workload", default="dsa100k",
                     choices=["dsa100k", "verify", "adaptive", "quest", "decode", "loadstep"])
-    ap.add_argument("--gather-blocks", type=int, default=0)
+    ap.add_argument("--gather-blocks", type=int, default=0,
+                    help="workgroups of the plan-replay copy kernel (0 = automatic); resolve calls copy their "
+                         "misses inside the resolve kernel")
     ap.add_argument("--split", type=int, default=0)
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
                     help="separate: hsk_resolve_step then hsk_sparse_decode_attn per layer; fused: "
