@@ -94,6 +94,14 @@ def test_mla_score_jump_after_the_first_tile(H):
     _run_mla(R=2, Q=1, H=H, k=300, n_rows=1000, split=2, seed=H, make=make)
 
 
+@pytest.mark.parametrize("R,Q,H,split", [(11, 1, 128, 0), (5, 3, 128, 3), (9, 1, 64, 2), (13, 2, 16, 0)])
+def test_mla_xcd_grouped_launches_with_partial_groups(R, Q, H, split):
+    """Eight or more queries: the MLA workgroups and the split-k combine are grouped by XCD (query q with the
+    XCD q mod 8); query counts that leave the last group of eight partial, for the 32-head-wave kernel (128
+    and 64 heads) and the 16-head-block kernel."""
+    _run_mla(R=R, Q=Q, H=H, k=300, n_rows=2000, split=split, seed=R * 7 + Q)
+
+
 def test_mla_partial_queries_and_wide_rows():
     """Per-request query counts (outputs of skipped queries untouched), pool rows wider than the 576 key
     values (only row[0:576] is read), large score range (q scaled up)."""
@@ -161,6 +169,11 @@ def test_gqa_pages_split_and_ragged(k, split):
     """GQA page attention: one page, ragged last tiles (k*16 not a multiple of 64 tokens), forced and
     automatic splits, partitions holding no page."""
     _run_gqa(R=3, H=32, Hkv=8, k=k, n_pages=600, split=split, seed=k * 10 + split)
+
+
+def test_gqa_xcd_grouped_combine_partial_group():
+    """Nine requests: the split-k combine of the GQA partitions grouped by XCD with a partial last group."""
+    _run_gqa(R=9, H=32, Hkv=8, k=100, n_pages=500, split=3, seed=99)
 
 
 @pytest.mark.parametrize("H,Hkv,pt", [(8, 8, 16), (16, 8, 16), (32, 8, 8), (32, 8, 32), (32, 8, 1), (32, 8, 64),
