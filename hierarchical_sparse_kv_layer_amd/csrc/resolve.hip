@@ -514,7 +514,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   // a resolve is one launch: zero-copy 16-byte loads of the pinned host rows over PCIe.  Wave w copies miss
   // rows 4 w .. 4 w + 3, then the four rows kResolveWaves * 4 further on, and so on; a batch's positions are
   // read first (written by phase 2 before this workgroup's barriers), then every chunk of the batch is loaded
-  // before any is stored.  64 workgroups x 16 waves keep megabytes of host reads in flight.
+  // before any is stored.  Each of a workgroup's 16 waves keeps up to four rows' reads in flight (64 requests
+  // of 1,152-byte rows: ~4.7 MB), far more than the link needs to stream.
   if (a.host != nullptr && m > 0) {
     const int lane = tid & 63, wv = tid >> 6;
     const int cpr = a.row_bytes >> 4;  // 16-byte chunks per row
