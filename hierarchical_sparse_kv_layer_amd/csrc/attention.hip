@@ -842,7 +842,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   };
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) oacc[cb] = f32x16{};
-  if (ntiles > 0) full_pass(true, true);  // every partition the planner makes has rows
+  if (ntiles > 0) full_pass(true, true);  // plan_attn makes no empty partition (and the combine skips a partition whose sum is 0)
   // every wave's loads are done (the last wait is for all of them) and every LDS read of the tiles is done;
   // any wave over the bound makes the workgroup redo the partition
   __syncthreads();
@@ -1131,13 +1131,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xc
       const int64_t ps = p0 + (int64_t)(u < S ? u : 0) * a.H;
       mu[u] = u < S ? a.pm[ps] : -INFINITY;
       lu[u] = u < S ? a.pl[ps] : 0.f;
-      v[u] = (u < S && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = (u < S && mine && lu[u] > 0.f) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
     }
     const float M = fmaxf(fmaxf(mu[0], mu[1]), fmaxf(mu[2], mu[3]));
     float w[4], L = 0.f;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      w[u] = mu[u] == -INFINITY ? 0.f : __expf(mu[u] - M) * lu[u];
+      w[u] = (mu[u] == -INFINITY || !(lu[u] > 0.f)) ? 0.f : __expf(mu[u] - M) * lu[u];
       L += w[u];
     }
     const float invL = 1.f / L;
@@ -1171,7 +1171,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xc
   for (int s0 = 0; s0 < S; s0 += 64) {
     if (s0 + lane < S) {
       const float m = a.pm[p0 + (int64_t)(s0 + lane) * a.H];
-      if (m != -INFINITY) L += __expf(m - M) * a.pl[p0 + (int64_t)(s0 + lane) * a.H];
+      const float lp = a.pl[p0 + (int64_t)(s0 + lane) * a.H];
+      if (m != -INFINITY && lp > 0.f) L += __expf(m - M) * lp;
     }
   }
 #pragma unroll
@@ -1186,8 +1187,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xc
       const int sidx = s0 + u;
       const int64_t ps = p0 + (int64_t)(sidx < S ? sidx : 0) * a.H;
       const float m = sidx < S ? a.pm[ps] : -INFINITY;
-      w[u] = m == -INFINITY ? 0.f : __expf(m - M) * a.pl[ps] * invL;
-      v[u] = (sidx < S && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+      const float lp = sidx < S ? a.pl[ps] : 0.f;
+      w[u] = (m == -INFINITY || !(lp > 0.f)) ? 0.f : __expf(m - M) * lp * invL;
+      v[u] = (w[u] != 0.f && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1227,6 +1229,9 @@ struct AttnPlan {
 // max_rows bounds the rows of one partition (the fused kernel keeps two location arrays in LDS).
 static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSplitRows) {
   if (!d || d->num_requests < 1 || d->max_queries < 1 || d->heads < 1 || d->top_k < 1 || d->split < 0) return false;
+  // the kernels take the maximum of the raw scores and scale it afterwards, which is the maximum of the
+  // scaled scores only for a positive scale
+  if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return false;
   const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
   const int k = d->top_k;
   if (d->kind == HSK_ATTN_MLA) {
@@ -1241,9 +1246,11 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
     p->nw32 = d->heads % 128 == 0 ? 4 : d->heads % 64 == 0 ? 2 : 0;
     const int min_split = (k + max_rows - 1) / max_rows;
     if (d->split > 0) {
-      p->split = d->split;
-      p->rows_per_split = (k + p->split - 1) / p->split;
+      // a forced split is an upper bound: rows_per_split = ceil(k / split), and the partitions are the
+      // ceil(k / rows_per_split) non-empty runs of that many rows (k = 2,048 with split = 100 gives 98)
+      p->rows_per_split = (k + d->split - 1) / d->split;
       if (p->rows_per_split > max_rows) return false;
+      p->split = (k + p->rows_per_split - 1) / p->rows_per_split;
     } else {
       // about one workgroup per compute unit (a workgroup fills a CU's LDS), tiles of whole 32-row blocks
       const int64_t base = RQ * p->hgroups;
@@ -1274,8 +1281,11 @@ static bool plan_attn(const hsk_attn_desc* d, AttnPlan* p, int max_rows = kMaxSp
       s = s < (k + kGqaMaxPages - 1) / kGqaMaxPages ? (k + kGqaMaxPages - 1) / kGqaMaxPages : s;
       p->split = (int)(s > k ? k : s);
     }
+    // every partition holds at least one page: with rows_per_split = ceil(k / split) pages each, only
+    // ceil(k / rows_per_split) partitions are non-empty (R = 3, Hkv = 8, k = 100 asks for 43 and gets 34)
     p->rows_per_split = (k + p->split - 1) / p->split;
     if (p->rows_per_split > kGqaMaxPages) return false;
+    p->split = (k + p->rows_per_split - 1) / p->rows_per_split;
   } else {
     return false;
   }

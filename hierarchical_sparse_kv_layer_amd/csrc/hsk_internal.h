@@ -134,6 +134,7 @@ struct hsk_store {
   std::vector<hsk::SourceMeta> meta;
   std::vector<char*> host;                  // pinned host rows per host source
   std::vector<uint32_t> last_epoch;         // per source
+  std::vector<uint8_t> replay_dst;           // per source: 1 once it received a replayed plan (no own resolves)
   std::vector<std::vector<int32_t>> opt_mirror;  // [source * R + r] host copy of the optional map
   void* h_stage = nullptr;                  // pinned staging for map and run-list uploads
   size_t h_stage_bytes = 0;

@@ -174,6 +174,7 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
     st->meta.push_back(m);
   }
   st->last_epoch.assign(desc->num_sources, 0u);
+  st->replay_dst.assign(desc->num_sources, 0);
   st->opt_mirror.assign((size_t)desc->num_sources * R, std::vector<int32_t>());
   for (auto& v : st->opt_mirror) v.assign((size_t)st->max_pages, -1);
   // pinned, device-mapped host rows
@@ -337,6 +338,7 @@ static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, c
 hsk_status hsk_resolve_step(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel, const int32_t* d_nq,
                             int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream) {
   if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs) return HSK_EINVAL;
+  if (st->replay_dst[source]) return HSK_ESTATE;  // its pool rows follow another source's slot table
   if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
   hipStream_t s = (hipStream_t)stream;
   ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
@@ -366,6 +368,7 @@ hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, con
       desc->kind != HSK_ATTN_MLA || desc->num_requests != st->d.num_requests || desc->max_queries != 1 ||
       desc->top_k != st->d.top_k || (int64_t)desc->row_elems * 2 != st->d.row_bytes || desc->row_elems != desc->dk)
     return HSK_EINVAL;
+  if (st->replay_dst[source]) return HSK_ESTATE;
   if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
   hipStream_t s = (hipStream_t)stream;
   ResolveArgs a = resolve_args(st, source, epoch, d_sel, nullptr, d_locs, d_stats);
@@ -460,9 +463,13 @@ hsk_status hsk_context_rows(hsk_store* st, int32_t source, int32_t req, int64_t*
 
 hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
   if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
-      dst_source >= st->d.num_sources)
+      dst_source >= st->d.num_sources || plan_source == dst_source)
     return HSK_EINVAL;
   if (st->d.staging_arenas && st->d.staging_rows) return HSK_EINVAL;
+  // A destination's pool rows follow the plan source's slot table, not its own metadata: it never resolves
+  // again (HSK_ESTATE), and it cannot serve as a plan source, having no plan of its own.
+  if (st->replay_dst[plan_source] || st->last_epoch[dst_source] != 0) return HSK_ESTATE;
+  st->replay_dst[dst_source] = 1;
   if (st->d.gather_mode != HSK_GATHER_ZEROCOPY) return HSK_OK;
   void* pool;
   hsk_pool_base(st, dst_source, &pool);

@@ -117,11 +117,13 @@ typedef struct hsk_stats {
 typedef struct hsk_store hsk_store;
 
 /* Device memory the caller must provide for a store described by *desc: the metadata workspace and the
- * row pool of all sources.  Both must be 256-byte aligned. */
+ * row pool of all sources.  Both must be 256-byte aligned.  HiSparse section 3.3 (admission): the
+ * per-layer GPU caches of a request (hot slots, tail, staging) are reserved up front, the full history
+ * lives in host memory; this call sizes those reservations for all R requests and sources at once. */
 hsk_status hsk_workspace_bytes(const hsk_desc* desc, size_t* workspace_bytes, size_t* pool_bytes);
 
-/* Create a store over caller-owned device memory (sizes from hsk_workspace_bytes) and allocate its pinned
- * host rows (num_sources, or 1 with host_alias_sources, x R x max_ctx x row_bytes).  Metadata is set empty
+/* HiSparse section 3.3 (admission and prefill): create a store over caller-owned device memory (sizes from
+ * hsk_workspace_bytes) and allocate its pinned host rows (num_sources, or 1 with host_alias_sources, x R x max_ctx x row_bytes).  Metadata is set empty
  * on `stream`: keys -1, recency 0, page tables -1, optional maps -1, slot order 0..B-1.  The host rows are
  * uninitialised: the caller writes them (hsk_host_rows) before hsk_commit_prefill.
  * Returns HSK_ENOMEM if the pinned allocation fails. */
@@ -129,7 +131,7 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
                              hsk_store** out);
 
 /* Host pointer to the pinned rows [0, max_ctx) of (source, request); the caller may write them (the
- * prefill stand-in).  With host_alias_sources every source returns source 0's rows. */
+ * prefill stand-in: HiSparse section 3.3 step 1 has prefill write every layer's KV to host memory).  With host_alias_sources every source returns source 0's rows. */
 hsk_status hsk_host_rows(hsk_store* store, int32_t source, int32_t req, void** h_rows, int64_t* n_rows);
 
 /* Copy every request's tail rows (positions [n_r - T, n_r)) of every source from host to pool.  HiSparse
@@ -295,16 +297,16 @@ hsk_status hsk_context_rows(hsk_store* store, int32_t source, int32_t req, int64
 
 /* Adaptive DHiSparse Eq. 8 (pure host function): for a source that packs m consecutive token positions into
  * each stored row, the rows completed when a request's tokens grow from n_before to n_after are
- * [first, first + count) with first = floor(n_before / m) and first + count = floor(n_after / m); an
- * incomplete last row stays in the tail until it is complete. */
+ * [first, first + count) with first = floor(n_before / m) and first + count = floor(n_after / m); a
+ * partly filled last row is not counted and remains a tail row. */
 hsk_status hsk_completed_rows(int64_t n_before, int64_t n_after, int32_t m, int64_t* first, int64_t* count);
 
 /*
  * Draft KV ring (Adaptive DHiSparse section 3.4, Eqs. 9-10).  A drafter that reads at most `window` prior
  * positions plus its current block of at most k_max positions keeps, per request slot i, a ring of
  *     R_d = page_rows * ceil((window + page_rows - 1 + k_max) / page_rows)      rows (Eq. 9),
- * and draft position t of slot i lives at ring row  phi(i, t) = i * R_d + (t mod R_d)  (Eq. 10): two live
- * positions of one slot never share a row and slots occupy disjoint ranges.  The ring is caller-owned device
+ * and draft position t of slot i lives at ring row  phi(i, t) = i * R_d + (t mod R_d)  (Eq. 10): within a
+ * slot, positions that are live together map to distinct rows, and each slot owns its own R_d rows.  The ring is caller-owned device
  * memory of slots * R_d rows; hsk_sparse_decode_attn over hsk_ring_window_locs is the drafter's attention.
  */
 hsk_status hsk_ring_rows(int64_t window, int32_t page_rows, int32_t k_max, int64_t* ring_rows);
@@ -324,9 +326,14 @@ hsk_status hsk_ring_window_locs(int64_t ring_rows, int32_t slots, int32_t window
 
 /* Plan replay (HiSparse section 3.5, plan-then-IO): copy the rows listed in plan_source's last miss plan
  * from dst_source's host rows into dst_source's pool, at the same pool rows (EINVAL for a store with shared
- * staging arenas and staging rows, whose staged rows are not at the same relative rows).  A layer that shares its
- * anchor's selection then reads its own payload at the anchor's locations.  Order it after the anchor's
- * resolve and before the consumer's attention with events when it runs on a side stream. */
+ * staging arenas and staging rows, whose staged rows are not at the same relative rows, and for
+ * plan_source == dst_source).  A layer that shares its anchor's selection then reads its own payload at the
+ * anchor's locations.  Order it after the anchor's resolve and before the consumer's attention with events
+ * when it runs on a side stream.
+ * A replay destination is replay-only: its pool rows follow plan_source's slot table while its own metadata
+ * stays empty, so once a source has received a replay, hsk_resolve_step and hsk_resolve_attend on it return
+ * HSK_ESTATE, and so does a replay into a source that has resolved before or from a source that is itself a
+ * replay destination. */
 hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_source, hsk_stream_t stream);
 
 /* Device address of a source's pool region (row 0 of the layout above). */
@@ -348,8 +355,10 @@ typedef struct hsk_attn_desc {
   int32_t top_k;         /* selected rows (MLA) or pages (GQA) per query */
   int32_t row_elems;     /* bf16 values per pool row (MLA >= dk; GQA page_tokens * 2 * dk) */
   int32_t page_tokens;   /* GQA: tokens per page row, each [K dk | V dk].  MLA: 1 */
-  int32_t split;         /* partitions of the k rows per query (split-k); 0 = automatic */
-  float scale;           /* softmax scale, e.g. 1/sqrt(dk) */
+  int32_t split;         /* partitions of the k rows per query (split-k); 0 = automatic.  A forced split is
+                            an upper bound: partitions hold ceil(k / split) rows each and only the non-empty
+                            ones, ceil(k / ceil(k / split)) of them, are made */
+  float scale;           /* softmax scale, e.g. 1/sqrt(dk); must be positive and finite (else HSK_EINVAL) */
 } hsk_attn_desc;
 
 /* Device scratch (bytes) that hsk_sparse_decode_attn and hsk_resolve_attend need for split-k partial

@@ -176,7 +176,7 @@ int64_t ora_context_rows(const ora_source* s, int32_t r) { return s->ctx[r]; }
 
 /* [AD] Eq. 8: a source packing m token positions per stored row completes, when a request's tokens grow from
  * n to n2, the rows s with floor(n/m) <= s < floor(n2/m) (reading: the upper bound is floored as the lower
- * one, since an incomplete last row stays in the tail until it is complete). */
+ * one, since a row with some of its m positions still missing is not yet complete and remains in the tail). */
 int32_t ora_completed_rows(int64_t n, int64_t n2, int32_t m, int64_t* first, int64_t* count) {
   if (m < 1 || n < 0 || n2 < n) return ORA_EINVAL;
   int64_t lo = 0, hi = 0;

@@ -4,12 +4,13 @@ Follows "Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierar
 
 * Eq. 3: required allocations (hot cache and tail of every admitted request), optional history and the
   admission reserve share the capacity M; required allocations and the reserve come first.
-* Optional residency covers complete pages of a request's imported history.
+* Only whole pages of the history a request arrived with can be optional; a partly filled page and rows
+  produced while decoding never are.
 * Eq. 4: an admission that leaves a deficit of D pages reclaims whole requests, walking the admitted ones
   in reclaim order and taking the pages of the first q, q the smallest prefix whose pages cover D; if all
   optional pages together cannot cover D the admission waits and nothing changes.
-* When pages are free again a bounded round-robin scheduler repopulates history, a limited number of pages
-  per attempt; ready locations are tracked apart from allocated pages, so a page whose copy is still in
+* Freed capacity is refilled by a round-robin pass over the requests that takes at most a fixed number of
+  pages in one attempt; ready locations are tracked apart from allocated pages, so a page whose copy is still in
   flight stays out of the optional map (pending) until it is published.
 * Reclaim only after host backing: pages whose rows exist only on the device are backed up first, then
   retired.  Population reserves pages, copies or retains their bytes, then publishes ready locations.

@@ -90,3 +90,15 @@ def test_attention_scratch_sizes(hsk):
         hsk.attn_scratch_bytes(bad)
     g = hsk.gqa_desc(requests=32, heads=32, kv_heads=8, dh=128, top_k=256, page_tokens=16, scale=0.088)
     assert hsk.attn_scratch_bytes(g) >= 32 * 32 * 128 * 4
+
+
+def test_attention_rejects_non_positive_or_non_finite_scale(hsk):
+    """The kernels take the maximum of the raw scores and scale it afterwards, which needs scale > 0."""
+    for sc in (0.0, -0.04, float("nan"), float("inf")):
+        d = hsk.mla_desc(requests=2, max_queries=1, heads=128, dk=576, dv=512, top_k=64, row_elems=576, scale=sc)
+        with pytest.raises(hsk.HskError) as e:
+            hsk.attn_scratch_bytes(d)
+        assert e.value.status == hsk.HSK_EINVAL
+        g = hsk.gqa_desc(requests=2, heads=32, kv_heads=8, dh=128, top_k=16, page_tokens=16, scale=sc)
+        with pytest.raises(hsk.HskError):
+            hsk.attn_scratch_bytes(g)

@@ -78,6 +78,15 @@ def test_mla_32_head_waves_split_and_ragged_k(H, k, split):
     _run_mla(R=2, Q=1, H=H, k=k, n_rows=5000, split=split, seed=7 * k + split + H)
 
 
+@pytest.mark.parametrize("H,k,split", [(128, 2048, 100), (64, 2048, 100), (32, 1000, 300), (128, 70, 64)])
+def test_mla_forced_split_with_would_be_empty_partitions(H, k, split):
+    """Forced splits whose ceil(k / split)-row partitions would leave the last ones empty (k = 2,048 in 100
+    partitions of 21 rows: 98 hold rows; k = 70 in 64 partitions of 2 rows: 35 do): the planner makes only
+    the non-empty partitions, so no partition contributes a 0/0 to the combine, for the 32-heads-per-wave
+    kernel (128, 64 heads) and the 16-head-block kernel (32 heads)."""
+    _run_mla(R=2, Q=1, H=H, k=k, n_rows=4000, split=split, seed=k + split + H)
+
+
 @pytest.mark.parametrize("H", [64, 128])
 def test_mla_score_jump_after_the_first_tile(H):
     """Scores that rise by far more than 2^64 above the first tile's maximum (one row of a late tile aligned
@@ -132,7 +141,8 @@ def test_mla_identical_rows_and_duplicates():
 
 
 def test_mla_rejects_unsupported_shapes():
-    for kw in ({"dk": 512}, {"dv": 256}, {"heads": 24}, {"row_elems": 500}, {"top_k": 4096, "split": 1}):
+    for kw in ({"dk": 512}, {"dv": 256}, {"heads": 24}, {"row_elems": 500}, {"top_k": 4096, "split": 1},
+               {"scale": 0.0}, {"scale": -0.1}, {"scale": float("nan")}, {"scale": float("inf")}):
         args = dict(requests=1, max_queries=1, heads=16, dk=576, dv=512, top_k=8, row_elems=576, scale=0.1)
         args.update(kw)
         with pytest.raises(hsk.HskError):
@@ -164,10 +174,13 @@ def _run_gqa(R, H, Hkv, k, n_pages, page_tokens=16, split=0, seed=0, q_scale=1.0
         assert np.all(err <= ATOL + RTOL * np.abs(ref)), f"unit {u}: max abs err {err.max():.3e}"
 
 
-@pytest.mark.parametrize("k,split", [(1, 0), (7, 1), (7, 3), (256, 0), (256, 1), (100, 6)])
+@pytest.mark.parametrize("k,split", [(1, 0), (7, 1), (7, 3), (256, 0), (256, 1), (100, 6), (100, 0), (200, 0),
+                                     (10, 8)])
 def test_gqa_pages_split_and_ragged(k, split):
     """GQA page attention: one page, ragged last tiles (k*16 not a multiple of 64 tokens), forced and
-    automatic splits, partitions holding no page."""
+    automatic splits.  Automatic splits at R = 3, Hkv = 8 ask for 43 partitions: k = 100 (ceil 3 pages each,
+    so only 34 hold pages) and k = 200 (5 pages each, 40 hold pages); the forced k = 10 in 8 (2 pages each,
+    5 hold pages).  The planner makes only the non-empty partitions."""
     _run_gqa(R=3, H=32, Hkv=8, k=k, n_pages=600, split=split, seed=k * 10 + split)
 
 

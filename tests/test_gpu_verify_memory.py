@@ -57,6 +57,35 @@ def test_replay_rejected_with_shared_staging():
     st.close()
 
 
+def test_replay_destination_is_replay_only():
+    """A replay destination's pool rows follow the plan source's slot table, so the library refuses to
+    resolve it afterwards, to replay into a source that has resolved, to use a destination as a plan
+    source, and to replay a source into itself."""
+    st = hsk.KVStore(requests=2, sources=3, row_bytes=1152, hot_slots=8, tail_rows=4, ctx=64, max_queries=1,
+                     top_k=8)
+    sel = torch.zeros((2, 1, 8), dtype=torch.int32, device="cuda")
+    sel[:, 0, :] = torch.arange(8, dtype=torch.int32)
+    locs = torch.empty_like(sel)
+    st.resolve_step(0, 1, sel, locs)
+    with pytest.raises(hsk.HskError) as e:
+        st.replay_plan(0, 0)
+    assert e.value.status == hsk.HSK_EINVAL
+    st.resolve_step(2, 1, sel, locs)
+    with pytest.raises(hsk.HskError) as e:          # source 2 has its own metadata
+        st.replay_plan(0, 2)
+    assert e.value.status == hsk.HSK_ESTATE
+    st.replay_plan(0, 1)
+    with pytest.raises(hsk.HskError) as e:
+        st.resolve_step(1, 2, sel, locs)
+    assert e.value.status == hsk.HSK_ESTATE
+    with pytest.raises(hsk.HskError) as e:
+        st.replay_plan(1, 2)
+    assert e.value.status == hsk.HSK_ESTATE
+    st.replay_plan(0, 1)                             # replaying again into the same destination is fine
+    assert st.sync_status() == 0
+    st.close()
+
+
 def test_draft_ring_write_window_and_attention():
     """Draft rows written round by round (blocks of up to K_max rows) wrap around a ring of R_d rows (Eq. 9);
     the window locations are Eq. 10's addresses, the ring rows at them hold the window's rows, and attention
