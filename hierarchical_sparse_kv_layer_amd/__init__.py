@@ -6,7 +6,8 @@ include/hsk.h).  PyTorch supplies device memory (tensors) and streams; the names
     kv_store_init / host_rows / commit_prefill / residency_set / reclaim_plan / residency_init /
     request_admit / request_release / residency_reclaim / residency_populate / residency_publish /
     residency_query / residency_pages / resolve_step /
-    replay_plan / pool_base / sparse_decode_attn / attn_scratch_bytes / snapshot / read_plan /
+    replay_plan / pool_base / sparse_decode_attn / sparse_decode_attn_noalloc / attn_scratch_bytes /
+    snapshot / read_plan /
     sync_status / kv_store_destroy
 
 The library must be built (``__graft_entry__.build()``); importing this package without it raises.
@@ -24,6 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libhsk.so")
 
 HSK_OK, HSK_EINVAL, HSK_ENOMEM, HSK_EHIP, HSK_ESTATE, HSK_ERANGE, HSK_ESTAGE, HSK_EEPOCH = 0, -1, -2, -3, -4, -5, -6, -7
 HSK_EWAIT = -8
+HSK_ESCRATCH = -9
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PAGE_READY, PAGE_BACKED = 1, 2
 GATHER_ZEROCOPY, GATHER_NO_IO = 0, 1
 ATTN_MLA, ATTN_GQA = 0, 1
@@ -94,6 +97,7 @@ _sig = {
     "hsk_pool_base": (_i32, [_vp, _i32, _P(_vp)]),
     "hsk_attn_scratch_bytes": (_i32, [_P(AttnDesc), _P(ctypes.c_size_t)]),
     "hsk_sparse_decode_attn": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "hsk_sparse_decode_attn_noalloc": (_i32, [_P(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp]),
     "hsk_resolve_attend": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _P(AttnDesc), _vp, _vp, _vp, ctypes.c_size_t,
                                   _vp]),
     "hsk_snapshot": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -301,6 +305,11 @@ def attn_scratch_bytes(adesc: AttnDesc) -> int:
 def sparse_decode_attn(adesc: AttnDesc, q, pool, locs, nq, out, scratch, scratch_bytes: int, stream=None) -> None:
     _check(_lib.hsk_sparse_decode_attn(ctypes.byref(adesc), _ptr(q), _ptr(pool), _ptr(locs), _ptr(nq), _ptr(out),
                                        _ptr(scratch), int(scratch_bytes), _stream(stream)), "hsk_sparse_decode_attn")
+
+
+def sparse_decode_attn_noalloc(adesc: AttnDesc, q, pool, locs, nq, out, stream=None) -> None:
+    _check(_lib.hsk_sparse_decode_attn_noalloc(ctypes.byref(adesc), _ptr(q), _ptr(pool), _ptr(locs), _ptr(nq),
+                                               _ptr(out), _stream(stream)), "hsk_sparse_decode_attn_noalloc")
 
 
 def resolve_attend(store: int, source: int, epoch: int, sel, locs, stats, adesc: AttnDesc, q, out, scratch,

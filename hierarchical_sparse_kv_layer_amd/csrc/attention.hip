@@ -13,6 +13,7 @@
 // combine kernel merges the partitions (o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s) and rounds to
 // bf16 (round to nearest even).
 #include <cmath>
+#include <mutex>
 
 #include "hsk_internal.h"
 
@@ -1319,6 +1320,37 @@ static void launch_mla(MlaArgs m, const AttnPlan& p, int64_t RQ, hipStream_t s) 
   hipLaunchKernelGGL((mla_mfma_kernel<NHB, NPAIR, FUSED>), dim3((unsigned)blocks), dim3(128 * NPAIR), 0, s, m);
 }
 
+static hsk_status launch_attn(const hsk_attn_desc* d, const AttnPlan& p, const void* d_q, const void* d_pool,
+                              const int32_t* d_locs, const int32_t* d_nq, void* d_out, void* d_scratch,
+                              hipStream_t s);
+
+// Split-k scratch of hsk_sparse_decode_attn_noalloc, for callers that cannot allocate.  In host code the
+// name `scratch` is only a host-side handle of the array: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device current and kept in
+// g_scratch_dev (each GPU holds its own copy of the array, at its own address).
+constexpr size_t kNoAllocScratchBytes = HSK_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices];
+
+static hsk_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HSK_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return HSK_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return HSK_EHIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return HSK_OK;
+}
+
 }  // namespace hsk
 
 using namespace hsk;
@@ -1341,7 +1373,30 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
   AttnPlan p;
   if (!plan_attn(d, &p) || !d_q || !d_pool || !d_locs || !d_out || !d_scratch) return HSK_EINVAL;
   if (scratch_bytes < (size_t)p.scratch || ((uintptr_t)d_scratch % 256)) return HSK_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
+  return launch_attn(d, p, d_q, d_pool, d_locs, d_nq, d_out, d_scratch, (hipStream_t)stream);
+}
+
+hsk_status hsk_sparse_decode_attn_noalloc(const hsk_attn_desc* d, const void* d_q, const void* d_pool,
+                                          const int32_t* d_locs, const int32_t* d_nq, void* d_out,
+                                          hsk_stream_t stream) {
+  AttnPlan p;
+  if (!plan_attn(d, &p) || !d_q || !d_pool || !d_locs || !d_out) return HSK_EINVAL;
+  if ((uint64_t)p.scratch > (uint64_t)kNoAllocScratchBytes) return HSK_ESCRATCH;
+  void* buf = nullptr;
+  const hsk_status st = noalloc_scratch(&buf);
+  if (st != HSK_OK) return st;
+  return launch_attn(d, p, d_q, d_pool, d_locs, d_nq, d_out, buf, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace hsk {
+
+// One attention call on stream s: the MLA or GQA kernel, then the split-k combine when there are several
+// partitions.  The plan p and the scratch (>= p.scratch bytes, 256-byte aligned) are checked by the caller.
+static hsk_status launch_attn(const hsk_attn_desc* d, const AttnPlan& p, const void* d_q, const void* d_pool,
+                              const int32_t* d_locs, const int32_t* d_nq, void* d_out, void* d_scratch,
+                              hipStream_t s) {
   const int64_t RQ = (int64_t)d->num_requests * d->max_queries;
   AttnArgs a;
   a.q = (const uint16_t*)d_q;
@@ -1387,10 +1442,6 @@ hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* d, const void* d_q, const
   HSK_HIP(hipGetLastError());
   return HSK_OK;
 }
-
-}  // extern "C"
-
-namespace hsk {
 
 hsk_status check_mla_fused(const hsk_attn_desc* d, const void* scratch, size_t scratch_bytes) {
   AttnPlan p;

@@ -98,6 +98,7 @@ const char* hsk_status_str(hsk_status s) {
     case HSK_ESTAGE: return "HSK_ESTAGE: missing rows exceed free hot slots plus staging";
     case HSK_EEPOCH: return "HSK_EEPOCH: epoch not greater than the source's last epoch";
     case HSK_EWAIT: return "HSK_EWAIT: admission waits, optional pages cannot cover its capacity";
+    case HSK_ESCRATCH: return "HSK_ESCRATCH: the call needs more scratch than the static buffer holds";
     default: return "unknown hsk_status";
   }
 }

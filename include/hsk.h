@@ -48,7 +48,8 @@ enum {
   HSK_ERANGE = -5,  /* a selected position is outside [0, n_r) */
   HSK_ESTAGE = -6,  /* a request's missing rows exceed its free hot slots plus its staging rows */
   HSK_EEPOCH = -7,  /* epoch not greater than the last epoch resolved on that source */
-  HSK_EWAIT = -8    /* admission waits: the optional pages cannot cover the capacity it needs */
+  HSK_EWAIT = -8,   /* admission waits: the optional pages cannot cover the capacity it needs */
+  HSK_ESCRATCH = -9 /* the call needs more scratch than the library's static buffer holds */
 };
 
 /* A hipStream_t, passed as a plain pointer; NULL is the null stream. */
@@ -378,6 +379,25 @@ hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* desc, size_t* scratch_byt
 hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* desc, const void* d_q, const void* d_pool,
                                   const int32_t* d_locs, const int32_t* d_nq, void* d_out, void* d_scratch,
                                   size_t scratch_bytes, hsk_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): hsk_sparse_decode_attn with its split-k scratch taken from a static
+ * device buffer inside the library instead of a caller buffer.  Same kernels, partitions and results as
+ * hsk_sparse_decode_attn with the same descriptor.  The buffer holds HSK_NOALLOC_SCRATCH_BYTES bytes on
+ * every GPU the library runs on and lives until the process ends; its device address is looked up once
+ * per device on the first call there (with that device current).  The call allocates nothing.
+ *   The device is the one current at the call; `stream` must belong to it.
+ *   Every call on one GPU shares that GPU's buffer, which keeps the last call's contents: calls that can
+ *   overlap on one GPU (different streams without ordering between them) race and give wrong results;
+ *   order them on one stream or with events.
+ * HSK_ESCRATCH (nothing queued) if hsk_attn_scratch_bytes(desc) exceeds HSK_NOALLOC_SCRATCH_BYTES; other
+ * errors as hsk_sparse_decode_attn.
+ */
+#define HSK_NOALLOC_SCRATCH_BYTES (64u << 20)
+hsk_status hsk_sparse_decode_attn_noalloc(const hsk_attn_desc* desc, const void* d_q, const void* d_pool,
+                                          const int32_t* d_locs, const int32_t* d_nq, void* d_out,
+                                          hsk_stream_t stream);
 
 /*
  * Resolve (HiSparse section 3.4) and MLA sparse decode attention (Adaptive DHiSparse Eq. 1) in one call,

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(hsk):
 
 
 def test_status_strings(hsk):
-    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, -9):
         assert hsk.status_str(s).startswith("HSK_")
     assert hsk.status_str(-99) == "unknown hsk_status"
 
