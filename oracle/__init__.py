@@ -69,6 +69,8 @@ def lib():
         L.ora_residency_set.restype = i32
         L.ora_resolve.argtypes = [vp, u32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.ora_resolve.restype = i32
+        L.ora_promote.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
+        L.ora_promote.restype = i32
         L.ora_snapshot.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.ora_snapshot.restype = None
         L.ora_pool_lookup.argtypes = [vp, vp, i64, vp]
@@ -177,6 +179,20 @@ class Source:
         out = {"rc": int(rc), "locs": locs, "cls": cls, "stats": stats,
                "plan": [(plan_pos[r, :plan_n[r]].copy(), plan_loc[r, :plan_n[r]].copy()) for r in range(R)],
                "evictions": [(ev_slot[r, :ev_n[r]].copy(), ev_key[r, :ev_n[r]].copy()) for r in range(R)]}
+        return out
+
+    def promote(self, sel: np.ndarray, locs: np.ndarray, accepted, nq=None) -> np.ndarray:
+        """Promotion copy-back after the last resolve (Adaptive DHiSparse 3.4): queries 0..accepted[r] are
+        committed.  Returns the number of rows promoted per request."""
+        sel = np.ascontiguousarray(sel, dtype=np.int32)
+        locs = np.ascontiguousarray(locs, dtype=np.int32)
+        R, Q, k = sel.shape
+        acc = np.ascontiguousarray(np.broadcast_to(np.asarray(accepted, np.int32), (R,)))
+        nqa = None if nq is None else np.ascontiguousarray(np.asarray(nq, dtype=np.int32))
+        out = np.zeros(R, np.int32)
+        rc = lib().ora_promote(self._h, _p(sel), Q, k, _p(nqa), _p(locs), _p(acc), _p(out))
+        if rc != OK:
+            raise ValueError(f"ora_promote: {rc}")
         return out
 
     def snapshot(self, r: int) -> dict:

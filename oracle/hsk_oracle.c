@@ -15,8 +15,10 @@
  *     the optional map and the hot cache at once, [AD] 3.1);
  *   - directly resolved rows leave the hot-cache metadata untouched ([AD] 3.2: they never reach
  *     replacement);
- *   - misses beyond the free hot slots of a call go to staging in miss order and are not promoted
- *     ([AD] 3.3 overflow to staging);
+ *   - misses beyond the free hot slots of a call go to staging in miss order ([AD] 3.3 overflow to
+ *     staging); the resolve itself never promotes them: ora_promote, called after the round's acceptance,
+ *     copies staged rows of committed queries into slots that only rejected drafts used ([AD] 3.4, Figure 3
+ *     callout 3; the reading is stated at ora_promote);
  *   - out-of-range positions and staging overflow reject the whole request before any state changes.
  */
 #include "hsk_oracle.h"
@@ -353,6 +355,80 @@ int32_t ora_resolve(ora_source* s, uint32_t epoch, const int32_t* sel, int32_t Q
                     stats + r, plan_pos, plan_loc, plan_n, plan_cap, ev_slot, ev_key, ev_n);
   }
   s->last_epoch = epoch;
+  return ORA_OK;
+}
+
+/*
+ * Promotion copy-back ([AD] 3.4 and Figure 3 callout 3: rows that overflowed into a staging arena; the
+ * promoted ones are copied back to stable hot-cache addresses before the arena is released).  The pages do
+ * not say which staged rows are promoted; the reading taken here ties promotion to the round's acceptance:
+ * queries 0..A_r of request r are committed (the anchor and its A_r accepted drafts, Eq. 7), the others are
+ * rejected.  After the resolve at epoch e (the source's last epoch) and the round's attention:
+ *   1. P = the distinct staged positions that a committed query selected, in staging order, and that are
+ *      not in the hot cache;
+ *   2. D = the hot slots touched at epoch e (rec >= 2e) whose position no committed query selected, in
+ *      ascending (rec, slot) order: the rows only rejected drafts asked for, fills before hits;
+ *   3. for i < min(|P|, |D|): the position held by slot D_i leaves the hot cache, P_i takes the slot with
+ *      rec = 2e (a fill of this epoch), and its row is copied from its staging row into the slot's pool row.
+ * A second call after the same resolve changes nothing (promoted rows are hot and committed).  locs are the
+ * locations that resolve emitted for sel (same layout); accepted[r] is clamped to [0, nq[r] - 1].
+ */
+int32_t ora_promote(ora_source* s, const int32_t* sel, int32_t Qmax, int32_t k, const int32_t* nq,
+                    const int32_t* locs, const int32_t* accepted, int32_t* promoted) {
+  if (s->last_epoch == 0 || Qmax <= 0 || k <= 0) return ORA_EINVAL;
+  const uint32_t e = s->last_epoch;
+  const int32_t B = s->B;
+  for (int32_t r = 0; r < s->R; ++r) {
+    promoted[r] = 0;
+    const int32_t q = nq ? nq[r] : Qmax;
+    if (q <= 0) continue;
+    int32_t A = accepted[r];
+    if (A < 0) A = 0;
+    if (A > q - 1) A = q - 1;
+    const int32_t* sr = sel + (int64_t)r * Qmax * k;
+    const int32_t* lr = locs + (int64_t)r * Qmax * k;
+    int32_t* key = s->key + (int64_t)r * B;
+    uint32_t* rec = s->rec + (int64_t)r * B;
+    int32_t* pt = s->pt[r];
+    const int64_t n = s->ctx[r];
+    /* committed positions */
+    uint8_t* committed = (uint8_t*)calloc((size_t)n, 1);
+    for (int32_t j = 0; j <= A; ++j)
+      for (int32_t i = 0; i < k; ++i) committed[sr[(int64_t)j * k + i]] = 1;
+    /* 1. staged positions selected by a committed query, by staging index, not hot */
+    int32_t* pos_at = (int32_t*)malloc(sizeof(int32_t) * (size_t)(s->S > 0 ? s->S : 1));
+    for (int32_t c = 0; c < s->S; ++c) pos_at[c] = -1;
+    for (int32_t j = 0; j <= A; ++j)
+      for (int32_t i = 0; i < k; ++i) {
+        const int64_t c = (int64_t)lr[(int64_t)j * k + i] - stg_loc(s, r, 0);
+        if (c >= 0 && c < s->S) pos_at[c] = sr[(int64_t)j * k + i];
+      }
+    int32_t* P = (int32_t*)malloc(sizeof(int32_t) * (size_t)(s->S > 0 ? s->S : 1));
+    int32_t* Pc = (int32_t*)malloc(sizeof(int32_t) * (size_t)(s->S > 0 ? s->S : 1));
+    int32_t np = 0;
+    for (int32_t c = 0; c < s->S; ++c)
+      if (pos_at[c] >= 0 && pt[pos_at[c]] < 0) { P[np] = pos_at[c]; Pc[np] = c; ++np; }
+    /* 2. slots of this epoch holding positions no committed query selected, ascending (rec, slot) */
+    rs_pair* D = (rs_pair*)malloc(sizeof(rs_pair) * (size_t)B);
+    int32_t nd = 0;
+    for (int32_t slot = 0; slot < B; ++slot)
+      if (key[slot] >= 0 && rec[slot] >= 2u * e && !committed[key[slot]]) {
+        D[nd].rec = rec[slot]; D[nd].slot = slot; ++nd;
+      }
+    qsort(D, (size_t)nd, sizeof(rs_pair), cmp_rs);
+    /* 3. pair and copy back */
+    const int32_t m = np < nd ? np : nd;
+    for (int32_t i = 0; i < m; ++i) {
+      const int32_t slot = D[i].slot;
+      pt[key[slot]] = -1;
+      key[slot] = P[i];
+      pt[P[i]] = slot;
+      rec[slot] = 2u * e;
+      s->pool[hot_loc(s, r, slot)] = s->pool[stg_loc(s, r, Pc[i])];
+    }
+    promoted[r] = m;
+    free(committed); free(pos_at); free(P); free(Pc); free(D);
+  }
   return ORA_OK;
 }
 

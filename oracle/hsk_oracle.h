@@ -17,6 +17,7 @@
  *   - ora_reclaim_plan: the whole-request reclaim rule, Adaptive DHiSparse Eq. 4.
  *   - a pool model (which host row each pool row holds) so that Eq. 12 of Adaptive DHiSparse,
  *     KV[loc] = c_{r,s}, can be checked for every emitted location.
+ *   - ora_promote: promotion copy-back of staged rows after the round's acceptance (section 3.4).
  *   - sizing closed forms: the draft ring (Eq. 9), ring address (Eq. 10), staging reservation (Eq. 11).
  */
 #ifndef HSK_ORACLE_H
@@ -80,6 +81,13 @@ int32_t ora_resolve(ora_source* s, uint32_t epoch, const int32_t* sel, int32_t Q
                     const int32_t* nq, int32_t* locs, uint8_t* cls, ora_stats* stats,
                     int32_t* plan_pos, int32_t* plan_loc, int32_t* plan_n, int32_t plan_cap,
                     int32_t* ev_slot, int32_t* ev_key, int32_t* ev_n);
+
+/* Promotion copy-back after the last resolve ([AD] 3.4, Figure 3 callout 3), read as: queries 0..accepted[r]
+ * of request r are committed; staged rows that a committed query selected take, in staging order, the hot
+ * slots of this epoch whose rows only rejected queries selected, in ascending (rec, slot) order, and are copied
+ * there from staging.  sel and locs: the last resolve's selections and emitted locations.  promoted[R] out. */
+int32_t ora_promote(ora_source* s, const int32_t* sel, int32_t Qmax, int32_t k, const int32_t* nq,
+                    const int32_t* locs, const int32_t* accepted, int32_t* promoted);
 
 /* state of request r: key[B], rec[B], order[B] (slots ascending by (rec, slot)), pt[ctx_r], opt[pages_r] */
 void ora_snapshot(const ora_source* s, int32_t r, int32_t* key, uint32_t* rec, int32_t* order, int32_t* pt,

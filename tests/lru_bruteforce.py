@@ -79,6 +79,7 @@ class BruteRequest:
         fill_slots = sorted(victims)
         moved = set(fill_slots) | hit_set
         self.recency = [s for s in self.recency if s not in moved] + fill_slots + hit_slots
+        self.last_fill, self.last_hit, self.last_staged = list(fill_slots), list(hit_slots), list(staged)
         where = {pos: s for s, pos in enumerate(self.holds) if pos is not None}
         out_cls = []
         for p, c in zip(flat, classes):
@@ -93,3 +94,28 @@ class BruteRequest:
         return {"error": None, "classes": out_cls, "hit_slots": hit_slots, "misses": misses,
                 "victims": victims, "staged": staged, "evictions": evictions,
                 "slot_of": dict(where)}
+
+    def promote(self, lists, accepted: int):
+        """Promotion after the round's acceptance (Adaptive DHiSparse 3.4, Figure 3 callout 3), as read
+        here: lists 0..accepted are committed.  Staged rows of the last step that a committed list selected
+        (in staging order, skipping rows already held) replace the rows of the last step's touched slots
+        that no committed list selected, least recently used first; the slots that received a row rank as
+        that step's fills.  Returns the (slot, new position, old position) triples."""
+        if not lists:
+            return []
+        a = min(max(accepted, 0), len(lists) - 1)
+        committed = {p for lst in lists[:a + 1] for p in lst}
+        held = {pos for pos in self.holds if pos is not None}
+        promotable = [p for p in self.last_staged if p in committed and p not in held]
+        touched = set(self.last_fill) | set(self.last_hit)
+        demotable = [s for s in self.recency if s in touched and self.holds[s] not in committed]
+        pairs = []
+        for p, s in zip(promotable, demotable):
+            pairs.append((s, p, self.holds[s]))
+            self.holds[s] = p
+        moved = {s for s, _, _ in pairs}
+        fills = sorted(set(self.last_fill) | moved)
+        hits = sorted(set(self.last_hit) - moved)
+        self.recency = [s for s in self.recency if s not in touched] + fills + hits
+        self.last_fill, self.last_hit = fills, hits
+        return pairs

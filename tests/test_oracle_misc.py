@@ -226,3 +226,21 @@ def test_location_layout_hand_worked():
     np.testing.assert_array_equal(out["locs"][1], [[4, 7, 5, 26, 20, 11], [6, 6, 6, 6, 6, 6]])
     ev_slot, ev_key = out["evictions"][1]
     assert ev_slot.tolist() == [1] and ev_key.tolist() == [0]
+
+
+def test_table1_speculative_increment_is_ring_plus_staging_per_session():
+    """Table 1: Adaptive DHiSparse needs 0.060 GiB more per session than Adaptive HiSparse at both 32K and
+    100K context.  That is the draft ring (Eq. 9: 2,176 rows x 12,288 B per slot) plus the shared staging
+    reservation (Eq. 11: four live arenas x 35 slots x 8 x 2,048 rows x 576 B), per GPU, over 35 sessions."""
+    g = _golden("table1_session_memory.json")
+    s = _golden("sizing_worked_examples.json")
+    ring = oracle.ring_rows(s["ring"]["window"], s["ring"]["page_rows"], s["ring"]["k_max"])
+    n = g["sessions_per_gpu"]
+    ring_gib = n * ring * s["ring_memory"]["bytes_per_row"] / 2 ** 30
+    sh = s["staging_shape"]
+    stage_gib = oracle.staging_bytes(s["staging"]["live_sources"], n, sh["k_max"], sh["k"], sh["row_bytes"]) / 2 ** 30
+    per_session = (ring_gib + stage_gib) / n
+    for ctx in ("32K", "100K"):
+        diff = g["adaptive_dhisparse_gib"][ctx] - g["adaptive_hisparse_gib"][ctx]
+        assert abs(diff - g["increment_gib"]) < 5e-4
+        assert abs(per_session - diff) < 1e-3, (per_session, diff)
