@@ -6,7 +6,7 @@ include/hsk.h).  PyTorch supplies device memory (tensors) and streams; the names
     kv_store_init / host_rows / commit_prefill / residency_set / reclaim_plan / residency_init /
     request_admit / request_release / residency_reclaim / residency_populate / residency_publish /
     residency_query / residency_pages / resolve_step /
-    replay_plan / pool_base / sparse_decode_attn / sparse_decode_attn_noalloc / attn_scratch_bytes /
+    replay_plan / promote_staged / pool_base / sparse_decode_attn / sparse_decode_attn_noalloc / attn_scratch_bytes /
     snapshot / read_plan /
     sync_status / kv_store_destroy
 
@@ -88,6 +88,7 @@ _sig = {
     "hsk_residency_pages": (_i32, [_vp, _i32, _vp, _vp, _i64, _P(_i64)]),
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
+    "hsk_promote_staged": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "hsk_context_rows": (_i32, [_vp, _i32, _i32, _P(_i64)]),
     "hsk_completed_rows": (_i32, [_i64, _i64, _i32, _P(_i64), _P(_i64)]),
@@ -290,6 +291,11 @@ def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> N
     _check(_lib.hsk_replay_plan(store, plan_source, dst_source, _stream(stream)), "hsk_replay_plan")
 
 
+def promote_staged(store: int, source: int, locs, nq, accepted, promoted=None, stream=None) -> None:
+    _check(_lib.hsk_promote_staged(store, source, _ptr(locs), _ptr(nq), _ptr(accepted), _ptr(promoted),
+                                   _stream(stream)), "hsk_promote_staged")
+
+
 def pool_base(store: int, source: int) -> int:
     p = _vp()
     _check(_lib.hsk_pool_base(store, source, ctypes.byref(p)), "hsk_pool_base")
@@ -426,6 +432,9 @@ class KVStore:
 
     def resolve_step(self, source: int, epoch: int, sel, locs, stats=None, nq=None, stream=None):
         resolve_step(self.handle, source, epoch, sel, nq, locs, stats, stream)
+
+    def promote_staged(self, source: int, locs, accepted, promoted=None, nq=None, stream=None):
+        promote_staged(self.handle, source, locs, nq, accepted, promoted, stream)
 
     def resolve_attend(self, source: int, epoch: int, sel, locs, adesc: AttnDesc, q, out, scratch, stats=None,
                        stream=None):

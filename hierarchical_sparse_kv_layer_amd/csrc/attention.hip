@@ -146,11 +146,12 @@ __device__ __forceinline__ void wait_tile_barrier_n(int n) {
   }
 }
 
-// the 32-head kernel's waits: this wave's loads of 0, 1 or 2 tiles (9 or 18 each) still in flight
+// the 32-head kernels' waits: this wave's loads of 0 to 3 tiles (9 or 18 each) still in flight
 __device__ __forceinline__ void wait_tile_barrier32(int n) {
   switch (n) {
     case 9: wait_tile_barrier<9>(); break;
     case 18: wait_tile_barrier<18>(); break;
+    case 27: wait_tile_barrier<27>(); break;
     case 36: wait_tile_barrier<36>(); break;
     default: wait_tile_barrier<0>(); break;
   }

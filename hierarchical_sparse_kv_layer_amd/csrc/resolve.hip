@@ -585,6 +585,170 @@ __device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32
 constexpr int kGatherWaves = kGatherThreads / 64;
 constexpr int kGatherList = 64;
 
+// Promotion copy-back ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", section 3.4
+// and Figure 3 callout 3: promoted staged rows are copied back to stable hot-cache addresses before the staging
+// arena is reused).  Reading: queries 0..A of a request (the anchor and its A accepted drafts) are committed;
+// the staged rows of the last resolve that a committed query selected (in staging order, skipping rows already
+// hot) take the hot slots touched at that epoch whose rows no committed query selected, in ascending
+// (rec, slot) order -- the slot order list -- and become fills of the epoch (rec = 2e).  One 1024-thread
+// workgroup per request:
+//   1. committed selections mark their hot slots and staging rows in two LDS bitmaps (from the locations the
+//      resolve emitted);
+//   2. the marked staging rows not yet hot are compacted in staging order (block prefix sum); a marked row
+//      that is already hot (promoted by an earlier call after the same resolve) marks its slot instead;
+//   3. the unmarked slots of this epoch are compacted in slot-order-list order;
+//   4. pair i takes slot D_i for staged row P_i: page table, key and recency updated;
+//   5. the slot order is rewritten: its prefix of older slots is unchanged, then this epoch's fills, then its
+//      hits, each by ascending slot (the promoted slots count as fills);
+//   6. the rows are copied from their staging rows into the slots' pool rows.
+struct PromoteArgs {
+  const int32_t* locs;
+  const int32_t* nq;
+  const int32_t* accepted;
+  int32_t* promoted;
+  SourceMeta m;
+  char* pool;
+  int64_t max_ctx;
+  int64_t stg_base;
+  int32_t R, B, S, Qmax, k, row_bytes;
+  uint32_t epoch;
+};
+
+__global__ __launch_bounds__(kResolveThreads) void promote_kernel(PromoteArgs a) {
+  __shared__ uint32_t s_hot[HSK_MAX_HOT_SLOTS / 32];                 // committed hot slots
+  __shared__ uint32_t s_dem[HSK_MAX_HOT_SLOTS / 32];                 // slots that receive a promoted row
+  __shared__ uint32_t s_stg[HSK_MAX_SELECTIONS_PER_REQUEST / 32];    // staging rows a committed query selected
+  __shared__ uint16_t s_P[HSK_MAX_HOT_SLOTS];                        // promotable staging rows, in order
+  __shared__ uint16_t s_D[HSK_MAX_HOT_SLOTS];                        // demotable slots, in order
+  __shared__ int s_wsum[2][kResolveWaves];
+  __shared__ int s_v;
+  const int r = blockIdx.x, tid = threadIdx.x, NT = kResolveThreads;
+  const int B = a.B, S = a.S;
+  const int nq = a.nq ? a.nq[r] : a.Qmax;
+  if (nq <= 0 || nq > a.Qmax) {
+    if (a.promoted && tid == 0) a.promoted[r] = 0;
+    return;
+  }
+  const int A = min(max(a.accepted[r], 0), nq - 1);
+  const int32_t* locs = a.locs + (int64_t)r * a.Qmax * a.k;
+  int32_t* key = a.m.key + (int64_t)r * B;
+  uint32_t* rec = a.m.rec + (int64_t)r * B;
+  uint16_t* order = a.m.order + (int64_t)r * B;
+  int32_t* pt = a.m.pt + (int64_t)r * a.max_ctx;
+  const int32_t* ppos = a.m.plan_pos + (int64_t)r * a.Qmax * a.k;
+  const int32_t* pdst = a.m.plan_dst + (int64_t)r * a.Qmax * a.k;
+  const int plan_n = a.m.plan_n[r];
+  const int64_t hot0 = (int64_t)r * B, stg0 = a.stg_base + (int64_t)r * S;
+  const uint32_t e2 = 2u * a.epoch;
+  const int bw = (B + 31) >> 5, sw = (S + 31) >> 5;
+  for (int w = tid; w < bw; w += NT) { s_hot[w] = 0u; s_dem[w] = 0u; }
+  for (int w = tid; w < sw; w += NT) s_stg[w] = 0u;
+  if (tid == 0) s_v = plan_n;
+  __syncthreads();
+  // 1. marks from the committed queries' locations; v = the first staged entry of the plan (fills come first)
+  const int ncommit = (A + 1) * a.k;
+  for (int f = tid; f < ncommit; f += NT) {
+    const int64_t loc = locs[f];
+    if (loc >= hot0 && loc < hot0 + B) atomicOr(&s_hot[(loc - hot0) >> 5], 1u << ((loc - hot0) & 31));
+    else if (loc >= stg0 && loc < stg0 + S) atomicOr(&s_stg[(loc - stg0) >> 5], 1u << ((loc - stg0) & 31));
+  }
+  for (int i = tid; i < plan_n; i += NT)
+    if (pdst[i] >= stg0 && pdst[i] < stg0 + S) atomicMin(&s_v, i);
+  __syncthreads();
+  const int v = s_v;
+  // 2. promotable staging rows in staging order; thread t owns rows [t * per, (t + 1) * per)
+  const int per = (S + NT - 1) / NT;
+  int cnt = 0;
+  // (a staging row is taken only if the plan lists it, so locations that do not come from the source's last
+  // resolve cannot index past the plan or the page table)
+  auto staged_pos = [&](int c) -> int32_t {
+    if (!((s_stg[c >> 5] >> (c & 31)) & 1u) || v + c >= plan_n) return -1;
+    const int32_t u = ppos[v + c];
+    return (u >= 0 && u < a.max_ctx) ? u : -1;
+  };
+  for (int c = tid * per; c < min(S, (tid + 1) * per); ++c) {
+    const int32_t u = staged_pos(c);
+    if (u < 0) continue;
+    const int32_t slot = pt[u];
+    if (slot >= 0 && slot < B) atomicOr(&s_hot[slot >> 5], 1u << (slot & 31));   // promoted earlier: committed, hot
+    else ++cnt;
+  }
+  int np;
+  int base = block_sum_scan(cnt, &np, s_wsum[0]);
+  for (int c = tid * per; c < min(S, (tid + 1) * per) && base < B; ++c) {
+    const int32_t u = staged_pos(c);
+    if (u < 0 || pt[u] >= 0) continue;
+    s_P[base++] = (uint16_t)c;
+  }
+  __syncthreads();
+  // 3. demotable slots in slot-order-list order: touched at this epoch, holding a row no committed query chose
+  const int pers = (B + NT - 1) / NT;
+  int dcnt = 0;
+  for (int i = tid * pers; i < min(B, (tid + 1) * pers); ++i) {
+    const int slot = order[i];
+    dcnt += (rec[slot] >= e2 && key[slot] >= 0 && key[slot] < a.max_ctx && !((s_hot[slot >> 5] >> (slot & 31)) & 1u)) ? 1 : 0;
+  }
+  int nd;
+  int dbase = block_sum_scan(dcnt, &nd, s_wsum[1]);
+  for (int i = tid * pers; i < min(B, (tid + 1) * pers); ++i) {
+    const int slot = order[i];
+    if (rec[slot] >= e2 && key[slot] >= 0 && key[slot] < a.max_ctx && !((s_hot[slot >> 5] >> (slot & 31)) & 1u))
+      s_D[dbase++] = (uint16_t)slot;
+  }
+  np = min(np, B);
+  const int m = min(np, nd);
+  __syncthreads();
+  // 4. metadata of the pairs (distinct old and new positions, distinct slots)
+  for (int i = tid; i < m; i += NT) {
+    const int slot = s_D[i];
+    const int32_t u = ppos[v + s_P[i]];
+    pt[key[slot]] = -1;
+    key[slot] = u;
+    pt[u] = slot;
+    rec[slot] = e2;
+    atomicOr(&s_dem[slot >> 5], 1u << (slot & 31));
+  }
+  __syncthreads();
+  // 5. slot order: [slots older than this epoch, unchanged prefix][fills of the epoch][hits], by slot
+  int old_n = 0, fill_n = 0, hit_n = 0;
+  bool is_fill[kSlotsPerThread], is_hit[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int slot = tid * kSlotsPerThread + j;
+    is_fill[j] = is_hit[j] = false;
+    if (slot < B) {
+      const uint32_t rc = rec[slot];
+      const bool dem = (s_dem[slot >> 5] >> (slot & 31)) & 1u;
+      is_fill[j] = rc == e2 || dem;
+      is_hit[j] = rc == e2 + 1u && !dem;
+      old_n += rc < e2 ? 1 : 0;
+      fill_n += is_fill[j] ? 1 : 0;
+      hit_n += is_hit[j] ? 1 : 0;
+    }
+  }
+  int n_old, n_fill, n_hit;
+  const int fbase = block_sum_scan(fill_n, &n_fill, s_wsum[0]);
+  const int hbase = block_sum_scan(hit_n, &n_hit, s_wsum[1]);
+  (void)block_sum_scan(old_n, &n_old, s_wsum[0]);
+  __syncthreads();
+  int fi = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int slot = tid * kSlotsPerThread + j;
+    if (is_fill[j]) order[n_old + fbase + fi++] = (uint16_t)slot;
+    if (is_hit[j]) order[n_old + n_fill + hbase + hi++] = (uint16_t)slot;
+  }
+  // 6. copy the promoted rows from staging into their slots, 16 bytes per lane, one row per wave at a time
+  const int lane = tid & 63, wave = tid >> 6;
+  const int chunks = a.row_bytes >> 4;
+  for (int i = wave; i < m; i += kResolveWaves) {
+    const u32x4* src = (const u32x4*)(a.pool + (stg0 + s_P[i]) * (int64_t)a.row_bytes);
+    u32x4* dst = (u32x4*)(a.pool + (hot0 + s_D[i]) * (int64_t)a.row_bytes);
+    for (int c = lane; c < chunks; c += 64) dst[c] = src[c];
+  }
+  if (a.promoted && tid == 0) a.promoted[r] = m;
+}
+
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs g, int32_t R) {
   __shared__ const char* s_src[kGatherWaves][kGatherList];
   __shared__ char* s_dst[kGatherWaves][kGatherList];
@@ -793,6 +957,17 @@ hipError_t launch_init_meta(const SourceMeta& m, int32_t R, int32_t B, int64_t m
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(resolve_kernel, dim3(a.R), dim3(kResolveThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_promote(const int32_t* locs, const int32_t* nq, const int32_t* accepted, int32_t* promoted,
+                          const SourceMeta& m, char* pool, int64_t max_ctx, int64_t stg_base, int32_t R, int32_t B,
+                          int32_t S, int32_t Qmax, int32_t k, int32_t row_bytes, uint32_t epoch, hipStream_t s) {
+  PromoteArgs a;
+  a.locs = locs; a.nq = nq; a.accepted = accepted; a.promoted = promoted; a.m = m; a.pool = pool;
+  a.max_ctx = max_ctx; a.stg_base = stg_base; a.R = R; a.B = B; a.S = S; a.Qmax = Qmax; a.k = k;
+  a.row_bytes = row_bytes; a.epoch = epoch;
+  hipLaunchKernelGGL(promote_kernel, dim3(R), dim3(kResolveThreads), 0, s, a);
   return hipGetLastError();
 }
 

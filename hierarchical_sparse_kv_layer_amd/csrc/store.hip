@@ -485,6 +485,24 @@ hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_sourc
   return HSK_OK;
 }
 
+hsk_status hsk_promote_staged(hsk_store* st, int32_t source, const int32_t* d_locs, const int32_t* d_nq,
+                              const int32_t* d_accepted, int32_t* d_promoted, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_locs || !d_accepted) return HSK_EINVAL;
+  if (st->last_epoch[source] == 0 || st->replay_dst[source]) return HSK_ESTATE;
+  if (st->d.staging_rows > HSK_MAX_SELECTIONS_PER_REQUEST) return HSK_EINVAL;  // the kernel's staging bitmap
+  hipStream_t s = (hipStream_t)stream;
+  if (st->d.staging_rows == 0) {  // nothing can be staged: nothing to promote
+    if (d_promoted) HSK_HIP(launch_fill_i32(d_promoted, st->d.num_requests, 0, s));
+    return HSK_OK;
+  }
+  void* pool;
+  hsk_pool_base(st, source, &pool);
+  HSK_HIP(launch_promote(d_locs, d_nq, d_accepted, d_promoted, st->meta[source], (char*)pool, st->d.max_ctx,
+                         stg_base_of(st->d, source), st->d.num_requests, st->d.hot_slots, st->d.staging_rows,
+                         st->d.max_queries, st->d.top_k, st->d.row_bytes, st->last_epoch[source], s));
+  return HSK_OK;
+}
+
 hsk_status hsk_snapshot(hsk_store* st, int32_t source, int32_t req, int32_t* key, uint32_t* rec, uint16_t* order,
                         int32_t* pt, int32_t* opt) {
   if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;

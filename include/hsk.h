@@ -337,6 +337,31 @@ hsk_status hsk_ring_window_locs(int64_t ring_rows, int32_t slots, int32_t window
  * replay destination. */
 hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_source, hsk_stream_t stream);
 
+/*
+ * Promotion copy-back ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", section
+ * 3.4 and Figure 3 callout 3: staged rows that are promoted are copied back to stable hot-cache addresses
+ * before the staging arena is reused).  The pages leave open which rows are promoted; this call ties it to
+ * the round's acceptance (Eq. 7): queries 0..d_accepted[r] of request r are committed (the anchor and its
+ * accepted drafts; values are clamped to [0, nq[r] - 1]), the others rejected.  After the source's last
+ * hsk_resolve_step (epoch e):
+ *   - the staged rows that a committed query selected, in staging order, and not already in the hot cache,
+ *   - take the hot slots touched at epoch e whose rows no committed query selected, in ascending
+ *     (recency, slot) order (rows only rejected drafts asked for; this epoch's fills before its hits),
+ * pairwise, as many as both lists allow: the slot's old position leaves the cache, the staged row becomes a
+ * fill of epoch e, and its bytes are copied on the device from its staging row into the slot's pool row (no
+ * host read).  The next resolve then finds committed rows hot instead of fetching them from host again.
+ *   d_locs:     the int32 [R][Qmax][k] locations that the last hsk_resolve_step on `source` emitted.
+ *   d_nq:       int32 [R] query counts of that call, or NULL (all Qmax).
+ *   d_accepted: int32 [R] accepted drafts per request.
+ *   d_promoted: int32 [R] rows promoted per request (device), or NULL.
+ * Order it after the round's attention on `source` (it overwrites hot rows that rejected drafts read) and
+ * before the next resolve on `source` or on a source sharing its staging arena.  A second call after the same
+ * resolve promotes nothing.  HSK_ESTATE if the source has not resolved yet or is a replay destination;
+ * HSK_EINVAL if staging_rows exceeds HSK_MAX_SELECTIONS_PER_REQUEST.
+ */
+hsk_status hsk_promote_staged(hsk_store* store, int32_t source, const int32_t* d_locs, const int32_t* d_nq,
+                              const int32_t* d_accepted, int32_t* d_promoted, hsk_stream_t stream);
+
 /* Device address of a source's pool region (row 0 of the layout above). */
 hsk_status hsk_pool_base(hsk_store* store, int32_t source, void** d_pool_source);
 

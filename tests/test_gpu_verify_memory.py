@@ -133,3 +133,66 @@ def test_draft_ring_write_window_and_attention():
             checked += 1
     assert checked >= 2
     log(f"[ring] R_d={ring}: {checked} attention checks over wrapped windows")
+
+
+@pytest.mark.parametrize("arenas", [0, 2])
+def test_promotion_copy_back_after_acceptance(arenas):
+    """Verification rounds whose 8-query unions overflow the hot cache into staging (own staging per source,
+    and three layers taking turns in two shared arenas): after each layer's attention a random acceptance per
+    request promotes the staged rows of committed queries (Adaptive DHiSparse section 3.4, Figure 3 callout 3).
+    Checked against the oracle every time, bit for bit: the promoted counts, keys, recency stamps, slot order
+    and page table; every hot slot's pool row holds its position's host row afterwards (the copy-back read the
+    staging row, no host read); a repeated call promotes nothing; the next round's resolve (promoted rows are
+    hits) stays bit-exact with the oracle, and so does the arena's next user."""
+    w = synth.WORKLOADS["verify"].scaled(requests=8, layers=3, sources=3, ctx=20_000, queries=8, top_k=512,
+                                         hot_slots=1024, staging_rows=8 * 512, seed=3300 + arenas)
+    h = Harness(w, steps=4, staging_arenas=arenas)
+    rng = np.random.default_rng(77 + arenas)
+    R, B = w.requests, w.hot_slots
+    total = 0
+    for t in range(h.steps):
+        for layer in range(w.layers):
+            res = h.resolve(layer, t)
+            h.check_bytes(res)
+            h.attention(layer, t, res, samples=[(0, 0), (5, 3)])
+            src = res["src"]
+            acc = rng.integers(0, w.queries, size=R).astype(np.int32)
+            acc[0] = w.queries - 1                               # everything committed: nothing to move
+            d_acc = torch.from_numpy(acc).cuda()
+            d_prom = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+            h.store.promote_staged(src, res["d_locs"], d_acc, d_prom)
+            prom = d_prom.cpu().numpy()
+            want = h.ora[src].promote(res["sel"], res["locs"], acc)
+            assert np.array_equal(prom, want), f"promoted counts differ: gpu={prom} oracle={want}"
+            assert prom[0] == 0
+            pool = h.store.pool_rows(src)
+            for r in range(R):
+                g = h.store.snapshot(src, r)
+                a = h.ora[src].snapshot(r)
+                for f in ("key", "rec", "order", "pt"):
+                    assert np.array_equal(g[f], a[f]), f"{f} differs after promotion r={r}"
+                held = np.nonzero(g["key"] >= 0)[0]
+                rows = pool.index_select(0, torch.from_numpy(r * B + held).long().cuda()).cpu().numpy()
+                assert np.array_equal(rows, h.host_rows(src, r)[g["key"][held]]), f"hot rows differ r={r}"
+            total += int(prom.sum())
+            h.store.promote_staged(src, res["d_locs"], d_acc, d_prom)
+            assert int(d_prom.sum().item()) == 0
+            assert np.array_equal(h.ora[src].promote(res["sel"], res["locs"], acc), np.zeros(R, np.int32))
+            log(f"[promote arenas={arenas}] step {t} layer {layer}: staged={int(res['stats']['n_staged'].sum())} "
+                f"promoted={int(prom.sum())}")
+    assert total > 0
+    h.close()
+
+
+def test_promotion_rejects_bad_state():
+    st = hsk.KVStore(requests=2, sources=2, row_bytes=1152, hot_slots=8, tail_rows=4, ctx=64, max_queries=2,
+                     top_k=4, staging_rows=8)
+    locs = torch.zeros((2, 2, 4), dtype=torch.int32, device="cuda")
+    acc = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(hsk.HskError) as e:                  # no resolve yet
+        st.promote_staged(0, locs, acc)
+    assert e.value.status == hsk.HSK_ESTATE
+    with pytest.raises(hsk.HskError) as e:
+        st.promote_staged(5, locs, acc)
+    assert e.value.status == hsk.HSK_EINVAL
+    st.close()
