@@ -51,37 +51,99 @@ def counter_traffic(kernel_key: str, src_path: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, sel_layer0, q_layer0, host_rows_fn, steps_for_resolve: int) -> dict:
-    """The oracle as it stands on a bounded sample of the same workload: resolve of layer 0 for the first
-    `steps_for_resolve` steps (all requests), then fp64 attention of every request at the last of those
-    steps, requests spread over host threads (ctypes drops the GIL inside the oracle)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(w, sel, q, host_rows_fn, resolve_steps: int, attn_reqs: int, threads: int) -> dict:
+    """The oracle on `threads` host threads: resolve of layer 0 for `resolve_steps` steps (all requests,
+    OpenMP across requests), then fp64 attention of `attn_reqs` requests at the last of those steps (one
+    request per thread at a time; ctypes drops the GIL inside the oracle).  Rows/s of one layer-step."""
     import concurrent.futures as cf
 
     import oracle
-    threads = max(1, len(os.sched_getaffinity(0)))
+    oracle.set_threads(threads)
+    warm = oracle.Source(R=w.requests, ctx=w.ctx, B=w.hot_slots, T=w.tail_rows, row_bytes=w.row_bytes)
+    warm.resolve(1, sel[0])      # untimed: starts the OpenMP thread pool
+    del warm
     src = oracle.Source(R=w.requests, ctx=w.ctx, B=w.hot_slots, T=w.tail_rows, row_bytes=w.row_bytes)
     src.commit_prefill()
     t0 = time.perf_counter()
-    for t in range(steps_for_resolve):
-        src.resolve(t + 1, sel_layer0[t])
-    t_res = (time.perf_counter() - t0) / steps_for_resolve
-    t = steps_for_resolve - 1
-    rows = [host_rows_fn(r)[sel_layer0[t, r, 0]].view(np.uint16) for r in range(w.requests)]
+    for t in range(resolve_steps):
+        src.resolve(t + 1, sel[t])
+    t_res = (time.perf_counter() - t0) / resolve_steps
+    t = resolve_steps - 1
+    reqs = list(range(min(attn_reqs, w.requests)))
+    rows = [host_rows_fn(r)[sel[t, r, 0]].view(np.uint16) for r in reqs]
 
-    def one(r):
-        return oracle.mla_attention(q_layer0[r, 0], rows[r], w.dk, w.dv, w.scale)
+    def one(i):
+        return oracle.mla_attention(q[reqs[i], 0], rows[i], w.dk, w.dv, w.scale)
 
     t0 = time.perf_counter()
-    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(one, range(w.requests)))
-    t_att = time.perf_counter() - t0
+    if threads == 1:
+        for i in range(len(reqs)):
+            one(i)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, range(len(reqs))))
+    t_att = (time.perf_counter() - t0) * w.requests / len(reqs)   # scaled to all requests
     per_layer_step = t_res + t_att
-    rows_per_layer_step = w.requests * w.queries * w.top_k
-    return {"value": rows_per_layer_step / per_layer_step, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{w.name}: layer 0, resolve of all {w.requests} requests for {steps_for_resolve} steps "
-                       f"({t_res * 1e3:.1f} ms/call, 1 thread) + fp64 attention of all {w.requests} requests "
-                       f"x 128 heads x {w.top_k} rows at step {t} ({t_att:.2f} s on {threads} threads)"),
+    return {"value": w.requests * w.queries * w.top_k / per_layer_step, "unit": "rows/s", "threads": threads,
+            "resolve_ms_per_call": t_res * 1e3, "attention_s_per_layer_step": t_att,
             "steps_per_s": 1.0 / (per_layer_step * w.layers)}
+
+
+def cpu_baseline(w, sel_layer0, q_layer0, host_rows_fn, steps_for_resolve: int, tiny=None) -> dict:
+    """The oracle as it stands, on the host's cores, on a bounded sample of the benchmark workload: resolve of
+    layer 0 for `steps_for_resolve` steps (all requests) and fp64 attention of every request at the last of
+    those steps, on every core available to the process; again on one thread (attention of 8 requests, scaled);
+    and the tiny decode (4 requests, 8 steps, all of it) on every core and on one."""
+    import oracle
+    threads = max(1, len(os.sched_getaffinity(0)))
+    full = _oracle_rate(w, sel_layer0, q_layer0, host_rows_fn, steps_for_resolve, w.requests, threads)
+    one = _oracle_rate(w, sel_layer0, q_layer0, host_rows_fn, steps_for_resolve, 8, 1)
+    out = {"value": full["value"], "unit": "rows/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": (f"{w.name}: layer 0, resolve of all {w.requests} requests for {steps_for_resolve} steps "
+                      f"({full['resolve_ms_per_call']:.2f} ms/call on {threads} threads, OpenMP across requests) "
+                      f"+ fp64 attention of all {w.requests} requests x {w.heads} heads x {w.top_k} rows at step "
+                      f"{steps_for_resolve - 1} ({full['attention_s_per_layer_step']:.2f} s on {threads} threads)"),
+           "steps_per_s": full["steps_per_s"],
+           "one_thread": {**one, "sample": (f"same resolve sample on 1 thread "
+                                            f"({one['resolve_ms_per_call']:.2f} ms/call) + fp64 attention of 8 "
+                                            f"requests on 1 thread, scaled to {w.requests}")}}
+    if tiny is not None:
+        tw, tsel, tq, trows = tiny
+        out["tiny_decode"] = {
+            "all_threads": _oracle_rate(tw, tsel, tq, trows, tw.steps, tw.requests, threads),
+            "one_thread": _oracle_rate(tw, tsel, tq, trows, tw.steps, tw.requests, 1),
+            "sample": f"tiny: {tw.requests} requests, {tw.steps} resolve steps, attention of every request "
+                      f"at the last step ({tw.heads} heads x {tw.top_k} rows)"}
+    oracle.set_threads(threads)
+    return out
+
+
+def tiny_inputs(synth):
+    """The tiny decode's inputs for the oracle baseline (host rows generated on the host, no GPU)."""
+    tw = synth.WORKLOADS["tiny"]
+    sel = synth.selection_stream(tw, 0, steps=tw.steps)
+    q = synth.queries(tw, 0, tw.steps - 1)
+    rows = {}
+
+    def host_rows(r):
+        if r not in rows:
+            buf = np.zeros((tw.ctx, tw.row_bytes), np.uint8)
+            synth.fill_kv_rows(buf.ctypes.data, tw, 0, r, 0, tw.ctx)
+            rows[r] = buf
+        return rows[r]
+    return tw, sel, q, host_rows
 
 
 def resolve_algorithmic_bytes(w) -> int:
@@ -919,7 +981,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, sels[0], q_host[0][min(3, total_steps) - 1],
-                                              lambda r: store.host_rows(0, r), min(4, total_steps))
+                                              lambda r: store.host_rows(0, r), min(4, total_steps),
+                                              tiny=tiny_inputs(synth))
     print(json.dumps(result), flush=True)
     store.close()
     return 0 if status == 0 else 1

@@ -69,6 +69,10 @@ def lib():
         L.ora_residency_set.restype = i32
         L.ora_resolve.argtypes = [vp, u32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.ora_resolve.restype = i32
+        L.ora_set_threads.argtypes = [i32]
+        L.ora_set_threads.restype = None
+        L.ora_get_threads.argtypes = []
+        L.ora_get_threads.restype = i32
         L.ora_promote.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp]
         L.ora_promote.restype = i32
         L.ora_snapshot.argtypes = [vp, i32, vp, vp, vp, vp, vp]
@@ -212,6 +216,15 @@ class Source:
         out = np.zeros(lo.size, np.int64)
         lib().ora_pool_lookup(self._h, _p(lo), lo.size, _p(out))
         return out.reshape(np.shape(locs))
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle resolve's loop over requests (results do not depend on it)."""
+    lib().ora_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().ora_get_threads())
 
 
 def mla_attention(q: np.ndarray, rows: np.ndarray, dk: int, dv: int, scale: float) -> np.ndarray:

@@ -24,6 +24,7 @@
 #include "hsk_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -349,6 +350,9 @@ int32_t ora_resolve(ora_source* s, uint32_t epoch, const int32_t* sel, int32_t Q
     int32_t q = nq ? nq[r] : Qmax;
     if (q < 0 || q > Qmax) return ORA_EINVAL;
   }
+  /* requests are independent (their hot caches, page tables, tails, staging rows and output rows are
+   * disjoint), so they may run on several threads; the result does not depend on the thread count */
+#pragma omp parallel for schedule(dynamic, 1)
   for (int32_t r = 0; r < s->R; ++r) {
     int64_t off = (int64_t)r * Qmax * k;
     resolve_request(s, r, epoch, sel + off, Qmax, k, nq ? nq[r] : Qmax, locs + off, cls ? cls + off : NULL,
@@ -431,6 +435,12 @@ int32_t ora_promote(ora_source* s, const int32_t* sel, int32_t Qmax, int32_t k, 
   }
   return ORA_OK;
 }
+
+void ora_set_threads(int32_t n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
+int32_t ora_get_threads(void) { return omp_get_max_threads(); }
 
 void ora_snapshot(const ora_source* s, int32_t r, int32_t* key, uint32_t* rec, int32_t* order, int32_t* pt,
                   int32_t* opt) {

@@ -89,6 +89,10 @@ int32_t ora_resolve(ora_source* s, uint32_t epoch, const int32_t* sel, int32_t Q
 int32_t ora_promote(ora_source* s, const int32_t* sel, int32_t Qmax, int32_t k, const int32_t* nq,
                     const int32_t* locs, const int32_t* accepted, int32_t* promoted);
 
+/* threads of the request-parallel loop in ora_resolve (OpenMP); results do not depend on it */
+void ora_set_threads(int32_t n);
+int32_t ora_get_threads(void);
+
 /* state of request r: key[B], rec[B], order[B] (slots ascending by (rec, slot)), pt[ctx_r], opt[pages_r] */
 void ora_snapshot(const ora_source* s, int32_t r, int32_t* key, uint32_t* rec, int32_t* order, int32_t* pt,
                   int32_t* opt);

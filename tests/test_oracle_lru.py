@@ -272,3 +272,28 @@ def test_dedup_ratio_and_saved_fraction():
     saved = 1.0 - st["n_miss"] / st["n_miss_sel"]
     assert abs(saved - (1 - 1 / rho)) < 1e-12
     assert abs((1 - 1 / 1.41) - 0.29) < 0.005
+
+
+def test_resolve_does_not_depend_on_thread_count():
+    """The request-parallel loop of the oracle resolve gives the same locations, stats, plans and states on
+    one thread and on several."""
+    rng = np.random.default_rng(123)
+    R, n, B, T, Q, k = 16, 400, 32, 8, 3, 24
+    sels = [np.stack([np.stack([rng.choice(n, size=k, replace=False) for _ in range(Q)]) for _ in range(R)])
+            .astype(np.int32) for _ in range(5)]
+    outs = []
+    for threads in (1, 7):
+        oracle.set_threads(threads)
+        src = oracle.Source(R=R, ctx=n, B=B, T=T, staging_rows=Q * k, row_bytes=16)
+        src.commit_prefill()
+        res = [src.resolve(t + 1, sels[t]) for t in range(5)]
+        outs.append((res, [src.snapshot(r) for r in range(R)]))
+    oracle.set_threads(0)
+    (a, sa), (b, sb) = outs
+    for x, y in zip(a, b):
+        assert np.array_equal(x["locs"], y["locs"]) and np.array_equal(x["stats"], y["stats"])
+        for (p1, l1), (p2, l2) in zip(x["plan"], y["plan"]):
+            assert np.array_equal(p1, p2) and np.array_equal(l1, l2)
+    for x, y in zip(sa, sb):
+        for f in ("key", "rec", "order", "pt"):
+            assert np.array_equal(x[f], y[f])
