@@ -154,26 +154,8 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   const bool one_round = nrounds <= 1;
 
   // ---- phase 0: slot order and keys to LDS, clear bitmaps, validate every selected position ------------
-  {
-    uint16_t ov_[kSlotsPerThread];
-    int32_t kv_[kSlotsPerThread];
-#pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) {
-      const int q = tid + j * NT;
-      ov_[j] = q < B ? order[q] : 0;
-      kv_[j] = q < B ? key[q] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < kSlotsPerThread; ++j) {
-      const int q = tid + j * NT;
-      if (q < B) {
-        s_order[q] = ov_[j];
-        s_key[q] = kv_[j];
-      }
-    }
-  }
-  for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
-  if (tid < 4) s_cnt[tid] = 0;
+  // The selections are requested first: the page-table probes depend on them, and loads complete in order,
+  // so the probes then wait for the selections only, not for the slot order and keys requested after them.
   bool bad = !nq_ok;
   int32_t pv[kPer];
   for (int rd = 0; rd < nrounds; ++rd) {
@@ -185,6 +167,16 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       bad |= (pv[e] < 0) || ((int64_t)pv[e] >= n);
     }
   }
+  uint16_t ov_[kSlotsPerThread];
+  int32_t kv_[kSlotsPerThread];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int q = tid + j * NT;
+    ov_[j] = q < B ? order[q] : 0;
+    kv_[j] = q < B ? key[q] : 0;
+  }
+  for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
+  if (tid < 4) s_cnt[tid] = 0;
   // With one round, the page-table words (and optional-page map entries) of this thread's selections are
   // requested now, before the validation barrier, so the probe's latency overlaps it; positions are
   // clamped into the request's rows for the address only (an invalid request returns at the barrier).
@@ -196,6 +188,14 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       ptv[e] = pt[pc];
       const int64_t page = opt ? min((int64_t)(pc / a.P), a.max_pages - 1) : 0;
       ovv[e] = opt ? opt[page] : -1;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSlotsPerThread; ++j) {
+    const int q = tid + j * NT;
+    if (q < B) {
+      s_order[q] = ov_[j];
+      s_key[q] = kv_[j];
     }
   }
   int32_t* fill = a.fill ? a.fill + (int64_t)r * total : nullptr;
@@ -216,10 +216,44 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     return;
   }
 
+  // class counts and the request's statistics (every thread calls it): wave sums first (1,024 same-address
+  // LDS atomics would serialise for microseconds), two counts per word in 16-bit fields (a wave handles at
+  // most 64 x 4 x 16 = 4,096 selections), summed by the DPP scan and read from lane 63
+  int my_tail = 0, my_opt = 0, my_hit_sel = 0, my_miss_sel = 0;
+  auto write_stats = [&](int m_, int nhit_, int over_) {
+    const int c01 = wave_incl_scan(my_tail | (my_opt << 16));
+    const int c23 = wave_incl_scan(my_hit_sel | (my_miss_sel << 16));
+    const int w01 = __builtin_amdgcn_readlane(c01, 63), w23 = __builtin_amdgcn_readlane(c23, 63);
+    if ((tid & 63) == 0) {
+      atomicAdd(&s_cnt[0], w01 & 0xFFFF);
+      atomicAdd(&s_cnt[1], w01 >> 16);
+      atomicAdd(&s_cnt[2], w23 & 0xFFFF);
+      atomicAdd(&s_cnt[3], w23 >> 16);
+    }
+    lds_barrier();
+    if (tid == 0) {
+      a.m.plan_n[r] = m_;
+      if (a.stats) {
+        hsk_stats st;
+        st.n_sel = nsel;
+        st.n_tail = s_cnt[0];
+        st.n_opt = s_cnt[1];
+        st.n_hit = nhit_;
+        st.n_hit_sel = s_cnt[2];
+        st.n_miss = m_;
+        st.n_miss_sel = s_cnt[3];
+        st.n_staged = over_;
+        st.status = HSK_OK;
+        st.reserved = 0;
+        st.fetched_bytes = (int64_t)m_ * a.row_bytes;
+        a.stats[r] = st;
+      }
+    }
+  };
+
   // ---- phase 1: direct pass, page-table probe, hit bitmap, first-occurrence claims of misses ----------
   // A missing position p gets atomicMin(pt[p], INT_MIN + f) from each selection f naming it, so the word
   // ends holding the first occurrence whatever the order of the atomics.
-  int my_tail = 0, my_opt = 0, my_hit_sel = 0, my_miss_sel = 0;
   int32_t code[kPer];
   for (int rd = 0; rd < nrounds; ++rd) {
     const int fb = rd * per_round + kPer * tid;
@@ -277,7 +311,54 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
         if (fb + e < nsel) locs[fb + e] = code[e];
     }
   }
-  __syncthreads();
+
+  // ---- no miss in this request: no claims, victims or copies.  The slot order becomes [slots not hit, in
+  // their old order][hit slots ascending], which is the ascending (rec, slot) order once the hits get 2e + 1;
+  // one block scan ranks both groups (two counts per word in 16-bit fields: at most B <= 8,192 each).
+  // Every location is final already (a direct row or a hit's slot).
+  if (!__syncthreads_or(my_miss_sel != 0)) {
+    const int per = (B + NT - 1) / NT;
+    const int q0 = tid * per;
+    uint16_t sl[kSlotsPerThread];
+    int cnt_nh = 0;
+#pragma unroll
+    for (int e = 0; e < kSlotsPerThread; ++e) {
+      sl[e] = 0xFFFF;
+      if (e < per && q0 + e < B) {
+        const int sv = s_order[q0 + e];
+        if (((s_hit[sv >> 5] >> (sv & 31)) & 1u) == 0u) { sl[e] = (uint16_t)sv; ++cnt_nh; }
+      }
+    }
+    const int hw = tid < nwords ? __popc(s_hit[tid]) : 0;
+    int tot;
+    const int pre = block_sum_scan(cnt_nh | (hw << 16), &tot, s_wsum[0]);
+    const int n_nonhit = tot & 0xFFFF, nhit0 = tot >> 16;
+    if (tid < nwords) s_hit_pre[tid] = pre >> 16;
+    int rank = pre & 0xFFFF;
+#pragma unroll
+    for (int e = 0; e < kSlotsPerThread; ++e)
+      if (sl[e] != 0xFFFF) order[rank++] = sl[e];
+    lds_barrier();
+    const uint32_t e2h = 2u * a.epoch + 1u;
+    for (int sv = tid; sv < B; sv += NT) {
+      const int w = sv >> 5;
+      const uint32_t bit = 1u << (sv & 31);
+      if (s_hit[w] & bit) {
+        order[n_nonhit + s_hit_pre[w] + __popc(s_hit[w] & (bit - 1u))] = (uint16_t)sv;
+        rec[sv] = e2h;
+      }
+    }
+    if (one_round) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (kPer * tid + e < nsel) locs[kPer * tid + e] = code[e];
+    }
+    for (int f = nsel + tid; f < total; f += NT) locs[f] = -1;
+    if (fill)
+      for (int f = tid; f < total; f += NT) fill[f] = -1;
+    write_stats(0, nhit0, 0);
+    return;
+  }
 
   // ---- phase 2: distinct misses in first-occurrence order (ascending f) --------------------------------
   int m = 0;
@@ -475,39 +556,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   }
   lds_barrier();
   for (int q = tid; q < B; q += NT) order[q] = s_neworder[q];
-  // class counts: wave sums first (1,024 same-address LDS atomics would serialise for microseconds), two
-  // counts per word in 16-bit fields (a wave handles at most 64 x 4 x 16 = 4,096 selections), summed by
-  // the DPP scan and read from lane 63
-  {
-    const int c01 = wave_incl_scan(my_tail | (my_opt << 16));
-    const int c23 = wave_incl_scan(my_hit_sel | (my_miss_sel << 16));
-    const int w01 = __builtin_amdgcn_readlane(c01, 63), w23 = __builtin_amdgcn_readlane(c23, 63);
-    if ((tid & 63) == 0) {
-      atomicAdd(&s_cnt[0], w01 & 0xFFFF);
-      atomicAdd(&s_cnt[1], w01 >> 16);
-      atomicAdd(&s_cnt[2], w23 & 0xFFFF);
-      atomicAdd(&s_cnt[3], w23 >> 16);
-    }
-  }
-  lds_barrier();
-  if (tid == 0) {
-    a.m.plan_n[r] = m;
-    if (a.stats) {
-      hsk_stats st;
-      st.n_sel = nsel;
-      st.n_tail = s_cnt[0];
-      st.n_opt = s_cnt[1];
-      st.n_hit = nhit;
-      st.n_hit_sel = s_cnt[2];
-      st.n_miss = m;
-      st.n_miss_sel = s_cnt[3];
-      st.n_staged = over;
-      st.status = HSK_OK;
-      st.reserved = 0;
-      st.fetched_bytes = (int64_t)m * a.row_bytes;
-      a.stats[r] = st;
-    }
-  }
+  write_stats(m, nhit, over);
 
   // ---- phase 6: this call's distinct missing rows, host -> pool ------------------------------------------
   // The copy done by GPU threads (HiSparse section 3.4, phase 4), here by the resolving workgroup itself, so
