@@ -28,7 +28,7 @@ HSK_EWAIT = -8
 HSK_ESCRATCH = -9
 NOALLOC_SCRATCH_BYTES = 64 << 20
 PAGE_READY, PAGE_BACKED = 1, 2
-GATHER_ZEROCOPY, GATHER_NO_IO = 0, 1
+GATHER_ZEROCOPY, GATHER_NO_IO, GATHER_DEFERRED = 0, 1, 2
 ATTN_MLA, ATTN_GQA = 0, 1
 MAX_HOT_SLOTS = 8192
 
@@ -88,6 +88,7 @@ _sig = {
     "hsk_residency_pages": (_i32, [_vp, _i32, _vp, _vp, _i64, _P(_i64)]),
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
+    "hsk_fetch_plan": (_i32, [_vp, _i32, _vp]),
     "hsk_promote_staged": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "hsk_context_rows": (_i32, [_vp, _i32, _i32, _P(_i64)]),
@@ -291,6 +292,10 @@ def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> N
     _check(_lib.hsk_replay_plan(store, plan_source, dst_source, _stream(stream)), "hsk_replay_plan")
 
 
+def fetch_plan(store: int, source: int, stream=None) -> None:
+    _check(_lib.hsk_fetch_plan(store, source, _stream(stream)), "hsk_fetch_plan")
+
+
 def promote_staged(store: int, source: int, locs, nq, accepted, promoted=None, stream=None) -> None:
     _check(_lib.hsk_promote_staged(store, source, _ptr(locs), _ptr(nq), _ptr(accepted), _ptr(promoted),
                                    _stream(stream)), "hsk_promote_staged")
@@ -449,6 +454,9 @@ class KVStore:
 
     def replay_plan(self, plan_source: int, dst_source: int, stream=None):
         replay_plan(self.handle, plan_source, dst_source, stream)
+
+    def fetch_plan(self, source: int, stream=None):
+        fetch_plan(self.handle, source, stream)
 
     def pool_base(self, source: int) -> int:
         return pool_base(self.handle, source)

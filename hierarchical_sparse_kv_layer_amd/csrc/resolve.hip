@@ -631,7 +631,7 @@ __device__ __forceinline__ void wave_copy_row(const u32x4* __restrict__ src, u32
 // the misses are spread over requests.  A wave first lists its rows (host and pool addresses) in LDS, 64
 // requests at a time with one request per lane, then copies the listed rows as one stream of 16-byte chunks
 // over its 64 lanes, kDepth loads in flight per lane before the stores.
-constexpr int kGatherWaves = kGatherThreads / 64;
+constexpr int kGatherWaves = kFetchThreads / 64;
 constexpr int kGatherList = 64;
 
 // Promotion copy-back ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", section 3.4
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(kResolveThreads) void promote_kernel(PromoteArgs a)
   if (a.promoted && tid == 0) a.promoted[r] = m;
 }
 
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs g, int32_t R) {
+__global__ __launch_bounds__(kFetchThreads) void gather_kernel(GatherArgs g, int32_t R) {
   __shared__ const char* s_src[kGatherWaves][kGatherList];
   __shared__ char* s_dst[kGatherWaves][kGatherList];
   constexpr int kDepth = 8;
@@ -1021,7 +1021,7 @@ hipError_t launch_promote(const int32_t* locs, const int32_t* nq, const int32_t*
 }
 
 hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s) {
-  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kGatherThreads), 0, s, g, R);
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kFetchThreads), 0, s, g, R);
   return hipGetLastError();
 }
 

@@ -46,7 +46,9 @@ static bool valid_desc(const hsk_desc* d) {
   if (d->max_queries < 1 || d->top_k < 1) return false;
   if ((int64_t)d->max_queries * d->top_k > HSK_MAX_SELECTIONS_PER_REQUEST) return false;
   if (d->max_ctx < 1 || d->max_ctx > 0x7fffffffLL || !d->ctx_len) return false;
-  if (d->gather_mode != HSK_GATHER_ZEROCOPY && d->gather_mode != HSK_GATHER_NO_IO) return false;
+  if (d->gather_mode != HSK_GATHER_ZEROCOPY && d->gather_mode != HSK_GATHER_NO_IO &&
+      d->gather_mode != HSK_GATHER_DEFERRED)
+    return false;
   if (d->gather_blocks < 0 || d->host_alias_sources < 0 || d->host_alias_sources > 1) return false;
   for (int32_t r = 0; r < d->num_requests; ++r)
     if (d->ctx_len[r] < 1 || d->ctx_len[r] > d->max_ctx) return false;
@@ -316,7 +318,7 @@ hsk_status hsk_reclaim_plan(const int64_t* h_pages_held, int32_t n, int64_t defi
 
 static int32_t gather_blocks_for(const hsk_store* st) {
   if (st->d.gather_blocks > 0) return st->d.gather_blocks;
-  return 384;  // 1,536 waves: rows are spread evenly over them whatever the batch (PCIe rate plateaus from ~256)
+  return 32;  // 512 waves: rows are spread evenly over them whatever the batch (the host link fills from ~256)
 }
 
 static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel,
@@ -462,16 +464,9 @@ hsk_status hsk_context_rows(hsk_store* st, int32_t source, int32_t req, int64_t*
   return HSK_OK;
 }
 
-hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
-  if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
-      dst_source >= st->d.num_sources || plan_source == dst_source)
-    return HSK_EINVAL;
-  if (st->d.staging_arenas && st->d.staging_rows) return HSK_EINVAL;
-  // A destination's pool rows follow the plan source's slot table, not its own metadata: it never resolves
-  // again (HSK_ESTATE), and it cannot serve as a plan source, having no plan of its own.
-  if (st->replay_dst[plan_source] || st->last_epoch[dst_source] != 0) return HSK_ESTATE;
-  st->replay_dst[dst_source] = 1;
-  if (st->d.gather_mode != HSK_GATHER_ZEROCOPY) return HSK_OK;
+// The rows of plan_source's last miss plan, from dst_source's host rows into dst_source's pool at the plan's
+// pool rows: the gather kernel, gather_blocks workgroups.
+static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s) {
   void* pool;
   hsk_pool_base(st, dst_source, &pool);
   GatherArgs g;
@@ -481,8 +476,28 @@ hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_sourc
   g.plan_dst = st->meta[plan_source].plan_dst;
   g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
   g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
-  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), (hipStream_t)stream));
+  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
   return HSK_OK;
+}
+
+hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
+  if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
+      dst_source >= st->d.num_sources || plan_source == dst_source)
+    return HSK_EINVAL;
+  if (st->d.staging_arenas && st->d.staging_rows) return HSK_EINVAL;
+  // A destination's pool rows follow the plan source's slot table, not its own metadata: it never resolves
+  // again (HSK_ESTATE), and it cannot serve as a plan source, having no plan of its own.
+  if (st->replay_dst[plan_source] || st->last_epoch[dst_source] != 0) return HSK_ESTATE;
+  st->replay_dst[dst_source] = 1;
+  if (st->d.gather_mode == HSK_GATHER_NO_IO) return HSK_OK;
+  return gather_plan(st, plan_source, dst_source, (hipStream_t)stream);
+}
+
+hsk_status hsk_fetch_plan(hsk_store* st, int32_t source, hsk_stream_t stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || st->d.gather_mode != HSK_GATHER_DEFERRED)
+    return HSK_EINVAL;
+  if (st->last_epoch[source] == 0 || st->replay_dst[source]) return HSK_ESTATE;
+  return gather_plan(st, source, source, (hipStream_t)stream);
 }
 
 hsk_status hsk_promote_staged(hsk_store* st, int32_t source, const int32_t* d_locs, const int32_t* d_nq,

@@ -55,9 +55,13 @@ enum {
 /* A hipStream_t, passed as a plain pointer; NULL is the null stream. */
 typedef void* hsk_stream_t;
 
-/* Gather modes.  HSK_GATHER_NO_IO skips the host reads (the rows left in the slots are stale): it is a
- * timing bound only, like the no-IO oracle of HiSparse section 4.6, and never a correct result. */
-enum { HSK_GATHER_ZEROCOPY = 0, HSK_GATHER_NO_IO = 1 };
+/* Gather modes.  HSK_GATHER_ZEROCOPY: each resolve call ends by copying its misses.  HSK_GATHER_DEFERRED:
+ * a resolve call plans only (locations, metadata and the miss plan are final, the missing rows' pool
+ * contents are not) and hsk_fetch_plan queues the copy, on a stream of the caller's choice (the plan-then-IO
+ * split of HiSparse section 3.5, which lets the copy run beside other work).  HSK_GATHER_NO_IO skips the
+ * host reads (the rows left in the slots are stale): it is a timing bound only, like the no-IO oracle of
+ * HiSparse section 4.6, and never a correct result. */
+enum { HSK_GATHER_ZEROCOPY = 0, HSK_GATHER_NO_IO = 1, HSK_GATHER_DEFERRED = 2 };
 
 /* Limits of this build. */
 #define HSK_MAX_HOT_SLOTS 8192
@@ -95,8 +99,9 @@ typedef struct hsk_desc {
   int64_t max_ctx;             /* rows of host history reserved per request and source */
   const int64_t* ctx_len;      /* host array [R]: n_r at creation (the imported history, every source),
                                   1 <= n_r <= max_ctx, n_r < 2^31; hsk_append_rows grows it per source */
-  int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY or HSK_GATHER_NO_IO */
-  int32_t gather_blocks;       /* workgroups (of 4 waves) of the plan-replay copy kernel; 0 = automatic (384) */
+  int32_t gather_mode;         /* HSK_GATHER_ZEROCOPY, HSK_GATHER_NO_IO or HSK_GATHER_DEFERRED */
+  int32_t gather_blocks;       /* workgroups (of 16 waves) of the plan copy kernel (hsk_replay_plan,
+                                  hsk_fetch_plan); 0 = automatic (32) */
   int32_t staging_arenas;      /* 0: staging inside each source region; A >= 1: A arenas shared by the sources */
 } hsk_desc;
 
@@ -269,8 +274,10 @@ hsk_status hsk_residency_pages(hsk_store* store, int32_t req, int32_t* ids, uint
  *   d_stats hsk_stats [R] device out, or NULL
  * Queued on `stream`: one resolve kernel, one workgroup per request, which ends by copying its request's
  * distinct missing rows from pinned host memory into their slots with 16-byte zero-copy loads (none with
- * HSK_GATHER_NO_IO).  Locations and pool rows are final when the stream reaches the end of the call.  The distinct missing rows and their destination
- * rows are kept as the source's miss plan (HiSparse section 3.5) until its next resolve call.
+ * HSK_GATHER_NO_IO or HSK_GATHER_DEFERRED).  Locations and pool rows are final when the stream reaches the
+ * end of the call (with HSK_GATHER_DEFERRED, the pool rows of the misses once hsk_fetch_plan's copy is
+ * done).  The distinct missing rows and their destination rows are kept as the source's miss plan
+ * (HiSparse section 3.5) until its next resolve call.
  */
 hsk_status hsk_resolve_step(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
                             const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, hsk_stream_t stream);
@@ -336,6 +343,18 @@ hsk_status hsk_ring_window_locs(int64_t ring_rows, int32_t slots, int32_t window
  * HSK_ESTATE, and so does a replay into a source that has resolved before or from a source that is itself a
  * replay destination. */
 hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_source, hsk_stream_t stream);
+
+/* Deferred fetch (HiSparse section 3.5, plan-then-IO; section 3.4 phase 4, the copy by GPU threads): queue on
+ * `stream` the copy of `source`'s last miss plan, the distinct rows its last hsk_resolve_step found missing,
+ * from the source's pinned host rows into the pool rows that call emitted for them.  For stores in
+ * HSK_GATHER_DEFERRED mode, whose resolve calls do not copy.  The copy kernel runs gather_blocks workgroups
+ * of 16 waves (0 = automatic: 32), spread evenly over the plan's rows; 16 of them fill the host link and
+ * leave the other compute units to work on other streams meanwhile.
+ * Ordering is the caller's: queue it after the resolve (same stream, or an event), make readers of the
+ * rows (attention) wait for it, and order the source's next resolve call after it (that call rewrites the
+ * plan and may evict the slots being filled).  EINVAL: bad source or a store in another gather mode;
+ * ESTATE: no resolve on that source yet, or a replay destination. */
+hsk_status hsk_fetch_plan(hsk_store* store, int32_t source, hsk_stream_t stream);
 
 /*
  * Promotion copy-back ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", section

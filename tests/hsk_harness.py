@@ -28,8 +28,12 @@ def log(msg):
 
 class Harness:
     def __init__(self, w: synth.Workload, steps: int | None = None, gather_blocks: int = 0, check_meta_every: int = 1,
-                 staging_arenas: int = 0):
+                 staging_arenas: int = 0, deferred: bool = False):
+        """deferred: the store plans only (HSK_GATHER_DEFERRED) and each resolve is followed by hsk_fetch_plan
+        on a side stream, ordered by events (resolve -> fetch -> readers)."""
         self.w = w
+        self.deferred = deferred
+        self.copy_stream = torch.cuda.Stream() if deferred else None
         self.steps = w.steps if steps is None else steps
         self.U = w.units
         self.check_meta_every = check_meta_every
@@ -52,7 +56,8 @@ class Harness:
                                  tail_rows=w.tail_rows, ctx=w.ctx, page_rows=self.page_rows,
                                  opt_pool_pages=opt_pages, max_queries=w.queries, top_k=w.top_k,
                                  staging_rows=w.staging_rows, host_alias=w.host_alias, gather_blocks=gather_blocks,
-                                 staging_arenas=staging_arenas)
+                                 staging_arenas=staging_arenas,
+                                 gather_mode=hsk.GATHER_DEFERRED if deferred else hsk.GATHER_ZEROCOPY)
         host_sources = 1 if w.host_alias else w.sources
         for s in range(host_sources):
             for r in range(self.U):
@@ -134,6 +139,15 @@ class Harness:
             self.store.resolve_attend(src, e, d_sel, d_locs, ad, q, out, scratch, stats=d_stats)
         else:
             self.store.resolve_step(src, e, d_sel, d_locs, d_stats)
+            if self.deferred:
+                main = torch.cuda.current_stream()
+                planned = torch.cuda.Event()
+                planned.record(main)
+                self.copy_stream.wait_event(planned)
+                self.store.fetch_plan(src, stream=self.copy_stream)
+                fetched = torch.cuda.Event()
+                fetched.record(self.copy_stream)
+                main.wait_event(fetched)
         locs = d_locs.cpu().numpy()
         stats = hsk.stats_to_numpy(d_stats)
         st = self.store.sync_status()
