@@ -235,11 +235,13 @@ def misses_only(hsk, synth, w, gather_blocks: int, calls: int = 12) -> dict:
             "note": "resolve kernel with its zero-copy miss copies per call; bytes = distinct misses x 1152"}
 
 
-def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) -> dict:
-    """Fig. 8a analog with W queries per request: every call selects rows no earlier call selected, and the
+def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 9) -> dict:
+    """Fig. 8a analog with W queries per request: every call selects rows no recent call selected, and the
     W queries of a request share all of their k rows, half of them, or none, so the distinct missing rows per
     request are k, (W + 1) k / 2 or W k.  Each distinct row is copied once (the shared ones dedup); the
-    slope of time against copied bytes is the achieved host-link rate."""
+    slope of time against copied bytes is the achieved host-link rate.  A fourth point repeats the last
+    all-shared call (every row a hot hit, nothing copied): the measured fixed cost of a W-query call.  Each
+    mode times `calls` calls after one warm-up call (min, mean and max reported); the fit uses the means."""
     import torch
     R, k, n = w.requests, w.top_k, w.ctx
     S = W * k - k
@@ -252,25 +254,35 @@ def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) 
     cursor = [0] * R
 
     def take(r, m):
+        # fresh positions; the hot cache holds only the last call's k rows, so a position drawn again after
+        # a full pass over the context is a miss unless that call selected it (stats count what was copied)
+        if cursor[r] + m > n:
+            perms[r] = g.permutation(n).astype(np.int32)
+            cursor[r] = 0
         a = perms[r][cursor[r]:cursor[r] + m]
         cursor[r] += m
-        assert a.size == m, "context exhausted"
         return a
 
     locs = torch.empty((R, W, k), dtype=torch.int32, device="cuda")
     stats = hsk.stats_tensor(R)
     stream = torch.cuda.current_stream()
     points, epoch = {}, 1
-    for mode, shared in (("shared", k), ("half_shared", k // 2), ("disjoint", 0)):
+    last = None
+    for mode, shared in (("shared", k), ("half_shared", k // 2), ("disjoint", 0), ("shared_repeat", None)):
         times, byts = [], []
         for c in range(calls + 1):
-            sel = np.empty((R, W, k), np.int32)
-            for r in range(R):
-                common = take(r, shared)
-                for j in range(W):
-                    sel[r, j, :shared] = common
-                    sel[r, j, shared:] = take(r, k - shared)
-            d = torch.from_numpy(sel).cuda()
+            if shared is None:
+                d = last
+            else:
+                sel = np.empty((R, W, k), np.int32)
+                for r in range(R):
+                    common = take(r, shared)
+                    for j in range(W):
+                        sel[r, j, :shared] = common
+                        sel[r, j, shared:] = take(r, k - shared)
+                d = torch.from_numpy(sel).cuda()
+                if mode == "shared":
+                    last = d
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             st.resolve_step(0, epoch, d, locs, stats)
@@ -280,7 +292,8 @@ def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) 
             if c:   # the first call of each mode warms up
                 times.append(a.elapsed_time(b))
                 byts.append(int(hsk.stats_to_numpy(stats)["fetched_bytes"].sum()))
-        points[mode] = {"bytes_per_call": float(np.mean(byts)), "ms_per_call": float(np.mean(times))}
+        points[mode] = {"bytes_per_call": float(np.mean(byts)), "ms_per_call": float(np.mean(times)),
+                        "ms_min": float(np.min(times)), "ms_max": float(np.max(times)), "calls": calls}
     status = st.sync_status()
     st.close()
     x = np.array([v["bytes_per_call"] for v in points.values()])
@@ -288,8 +301,10 @@ def misses_sweep(hsk, synth, w, gather_blocks: int, W: int = 8, calls: int = 2) 
     slope, icpt = np.polyfit(x, y, 1)
     gbs = 1.0 / slope / 1e9
     return {"W": W, "points": points, "fit_GBps": gbs, "fit_intercept_us": icpt * 1e6,
+            "zero_copy_call_us": points["shared_repeat"]["ms_per_call"] * 1e3,
             "host_link_peak_GBps": PCIE_PEAK_GBS, "frac_host_link": gbs / PCIE_PEAK_GBS, "status": status,
-            "note": f"{R} requests x {W} queries x top-{k}; hot slots = k, staging {S} rows per request"}
+            "note": f"{R} requests x {W} queries x top-{k}; hot slots = k, staging {S} rows per request; "
+                    "call times from HIP events around each call"}
 
 
 def no_io_bound(hsk, synth, w, sels, d_q, ad, scratch, nscratch, steps: int) -> dict:
@@ -906,6 +921,9 @@ def main() -> int:
                     help="the headline step: 1 = one store, each layer's resolve (with its copies) then attention "
                          "on one stream; M > 1 = M micro-batches with the copies on a copy stream under the "
                          "other micro-batches' work (the serial step is reported beside it)")
+    ap.add_argument("--only", choices=["hits", "sweep"], default=None,
+                    help="profiling aid: after the warmup steps run only the hits-only layer steps or the W = 8 "
+                         "miss sweep, and print their result")
     ap.add_argument("--fetch-blocks", type=int, default=16,
                     help="workgroups (16 waves each) of the copy kernel in the overlapped step")
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
@@ -998,6 +1016,14 @@ def main() -> int:
     if store.sync_status() != 0:
         log("[bench] device-side error during warmup")
         return 1
+    if args.only:
+        if args.only == "hits":
+            r = hits_only(hsk, w, store, sels, d_q, d_locs, d_stats, ad, scratch, nscratch, pools, first_epoch=W + 1)
+        else:
+            r = misses_sweep(hsk, synth, w, args.gather_blocks)
+        print(json.dumps({args.only: r}), flush=True)
+        store.close()
+        return 0
     misses = []
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()

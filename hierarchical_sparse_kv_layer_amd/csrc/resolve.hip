@@ -121,7 +121,6 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
   __shared__ uint16_t s_order[HSK_MAX_HOT_SLOTS];
   __shared__ uint16_t s_victim[HSK_MAX_HOT_SLOTS];
   __shared__ uint16_t s_neworder[HSK_MAX_HOT_SLOTS];
-  __shared__ int32_t s_key[HSK_MAX_HOT_SLOTS];
   __shared__ int s_wsum[2][kResolveWaves];
   __shared__ int s_cnt[4];
 
@@ -168,12 +167,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     }
   }
   uint16_t ov_[kSlotsPerThread];
-  int32_t kv_[kSlotsPerThread];
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int q = tid + j * NT;
     ov_[j] = q < B ? order[q] : 0;
-    kv_[j] = q < B ? key[q] : 0;
   }
   for (int w = tid; w < nwords; w += NT) { s_hit[w] = 0u; s_vic[w] = 0u; }
   if (tid < 4) s_cnt[tid] = 0;
@@ -193,10 +190,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
 #pragma unroll
   for (int j = 0; j < kSlotsPerThread; ++j) {
     const int q = tid + j * NT;
-    if (q < B) {
-      s_order[q] = ov_[j];
-      s_key[q] = kv_[j];
-    }
+    if (q < B) s_order[q] = ov_[j];
   }
   int32_t* fill = a.fill ? a.fill + (int64_t)r * total : nullptr;
   if (__syncthreads_or(bad)) {
@@ -499,6 +493,10 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     if (tid < nwords) s_vic_pre[tid] = pre;
   }
   __syncthreads();
+  // the positions held by the first two strided victims this thread evicts, read before the stores of phases 4
+  // and 5 (later victims, past 2,048 per request, are read where they are evicted)
+  const int32_t old0 = tid < v ? key[s_victim[tid]] : -1;
+  const int32_t old1 = tid + NT < v ? key[s_victim[tid + NT]] : -1;
 
   // ---- phase 4: publish locations in selection order ---------------------------------------------------
   for (int rd = 0; rd < nrounds; ++rd) {
@@ -543,7 +541,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     const int32_t p = i == tid ? pp0 : i == tid + NT ? pp1 : ppos[i];
     if (i < v) {
       const int s = s_victim[i];
-      const int32_t old = s_key[s];
+      const int32_t old = i == tid ? old0 : i == tid + NT ? old1 : key[s];
       if (old >= 0) pt[old] = -1;  // eviction: old is not pending in this call
       key[s] = p;
       rec[s] = e2;
