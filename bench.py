@@ -518,7 +518,7 @@ def run_adaptive(hsk, synth, w, steps: int) -> dict:
             "host_fetch_fraction_after_reclaim": float(np.mean(after)), "per_step": per_step, "status": status}
 
 
-def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_blocks: int) -> dict:
+def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_blocks: int, split: int) -> dict:
     """The benchmark step with the host IO hidden under the other work (HiSparse section 3.5, overlap of IO
     with computation): the batch is served as M micro-batches of R/M requests, each with its own store (in
     HSK_GATHER_DEFERRED mode) and stream, and one copy stream runs every hsk_fetch_plan in turn.  Per layer
@@ -527,7 +527,13 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
     order (micro-batch 0's layer l, then micro-batch 1's, ...), and while the copy stream fetches one
     micro-batch's rows the others resolve and attend; every request still runs its layers in order, each
     layer's attention after its own resolve and fetch.  The fetch kernel's few workgroups leave the other
-    compute units to the attention.  Same selections and queries as the serial step."""
+    compute units to the attention, whose `split` partitions per request (3: 96 workgroups for 32 requests)
+    leave room for the fetch and the next resolve.  Same selections and queries as the serial step.
+
+    The M + 1 streams are consecutive new pool streams, not the current stream: HIP serves streams from a few
+    hardware queues (4 here), assigned in turn as the streams are created, and the pool's streams were created
+    together, so consecutive ones sit on different queues.  Two of them on one queue run in one FIFO (a fetch
+    then waits behind an attention), and the step slows from 1.71 to ~2.0 ms."""
     import torch
     R, k = w.requests, w.top_k
     assert R % M == 0
@@ -552,14 +558,15 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
         d_stats.append([hsk.stats_tensor(Rm) for _ in range(w.layers)])
         pools.append([st.pool_base(l) for l in range(w.layers)])
         ad = hsk.mla_desc(requests=Rm, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k,
-                          row_elems=w.row_elems, scale=w.scale)
+                          row_elems=w.row_elems, scale=w.scale, split=split)
         ads.append(ad)
         n = hsk.attn_scratch_bytes(ad)
         scratch.append((torch.empty(n, dtype=torch.uint8, device=dev), n))
         outs.append(torch.empty((Rm, 1, w.heads, w.dv), dtype=torch.int16, device=dev))
     log(f"[overlap] {M} micro-batches of {Rm} requests set up in {time.perf_counter() - t0:.1f} s")
-    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in range(M - 1)]
+    streams = [torch.cuda.Stream() for _ in range(M)]
     copy = torch.cuda.Stream()
+    torch.cuda.synchronize()
     planned = [torch.cuda.Event() for _ in range(M)]
     fetched = [torch.cuda.Event() for _ in range(M)]
 
@@ -591,7 +598,7 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
         status = status or st.sync_status()
         st.close()
     return {"ms_per_step": elapsed * 1e3 / K, "steps_per_s": K / elapsed, "micro_batches": M,
-            "requests_per_micro_batch": Rm, "fetch_workgroups": fetch_blocks,
+            "requests_per_micro_batch": Rm, "fetch_workgroups": fetch_blocks, "attention_partitions": split,
             "distinct_misses_last_step": int(sum(misses)), "status": status}
 
 
@@ -926,6 +933,8 @@ def main() -> int:
                          "miss sweep, and print their result")
     ap.add_argument("--fetch-blocks", type=int, default=16,
                     help="workgroups (16 waves each) of the copy kernel in the overlapped step")
+    ap.add_argument("--overlap-split", type=int, default=3,
+                    help="attention partitions per request in the overlapped step")
     ap.add_argument("--path", default="separate", choices=["separate", "fused"],
                     help="separate: hsk_resolve_step then hsk_sparse_decode_attn per layer; fused: "
                          "hsk_resolve_attend per layer")
@@ -1081,7 +1090,8 @@ def main() -> int:
     }
     if args.micro_batches > 1 and not fused:
         # the headline step: the same selections and queries, with the copies under the other work
-        ov = run_overlapped(hsk, synth, w, sels, q_host, K, W, args.micro_batches, args.fetch_blocks)
+        ov = run_overlapped(hsk, synth, w, sels, q_host, K, W, args.micro_batches, args.fetch_blocks,
+                            args.overlap_split)
         result["serial"] = {"value": value, "ms_per_step": ms_per_step, "steps_per_s": K / elapsed,
                             "schedule": "one store; per layer hsk_resolve_step (copies inside) then "
                                         "hsk_sparse_decode_attn, one stream"}
@@ -1091,7 +1101,8 @@ def main() -> int:
         result["steps_per_s"] = ov["steps_per_s"]
         result["config"]["schedule"] = (f"{ov['micro_batches']} micro-batches of {ov['requests_per_micro_batch']} "
                                         f"requests, one stream each; hsk_fetch_plan on a copy stream "
-                                        f"({ov['fetch_workgroups']} copy workgroups)")
+                                        f"({ov['fetch_workgroups']} copy workgroups); attention in "
+                                        f"{ov['attention_partitions']} partitions per request")
         result["status"] = status = status or ov["status"]
     else:
         result["config"]["schedule"] = "one store, one stream"
