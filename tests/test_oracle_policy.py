@@ -123,3 +123,50 @@ def test_figure6_analog_on_the_100k_stream(capsys):
     rate = {(n, B): r for n, B, r in rows}
     assert rate[("Belady", 2 * k)] <= min(rate[("LRU", 2 * k)], rate[("FIFO", 2 * k)], rate[("random", 2 * k)])
     assert rate[("LRU", 4 * k)] <= rate[("LRU", 2 * k)] <= rate[("top-k only", k)]
+
+
+def _splitmix64(state):
+    """SplitMix64 (Vigna's published definition): returns (new state, output)."""
+    m = (1 << 64) - 1
+    state = (state + 0x9E3779B97F4A7C15) & m
+    z = state
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return state, z ^ (z >> 31)
+
+
+def test_random_policy_victim_is_uniform_over_non_hit_slots():
+    """The random policy's victim is drawn uniformly from the slots not hit in the step: with B slots holding
+    a and one other row, re-selecting a after one intervening miss hits unless that miss drew a's slot, so the
+    miss frequency over seeds is 1/B; a slot hit in the step is never drawn, so with a hit beside the miss the
+    draw is over B - 1 slots.  Binomial bounds at 4 standard deviations over 4,000 seeds."""
+    n_seeds = 4000
+    n = 100
+    a, b, c = 3, 5, 7
+    for B in (2, 4):
+        sel = np.array([[a], [b], [a]], np.int32)
+        miss = np.array([oracle.policy_replay(sel, n, B, "random", seed=s)[2] for s in range(n_seeds)])
+        p = 1.0 / B
+        assert abs(miss.mean() - p) <= 4 * np.sqrt(p * (1 - p) / n_seeds), (B, miss.mean())
+    # B = 3, k = 2: step 1 fills a and b, step 2 hits a and misses c, which draws b's slot or the empty one
+    # (1/2 each; a uniform draw over all three slots would give 1/3 and sometimes evict a)
+    sel_b = np.array([[a, b], [a, c], [b, b]], np.int32)
+    sel_a = np.array([[a, b], [a, c], [a, a]], np.int32)
+    miss_b = np.array([oracle.policy_replay(sel_b, n, 3, "random", seed=s)[2] for s in range(n_seeds)])
+    miss_a = np.array([oracle.policy_replay(sel_a, n, 3, "random", seed=s)[2] for s in range(n_seeds)])
+    assert abs(miss_b.mean() - 0.5) <= 4 * np.sqrt(0.25 / n_seeds), miss_b.mean()
+    assert not miss_a.any(), "a slot hit in the step was drawn as a victim"
+
+
+def test_random_policy_draws_follow_splitmix64():
+    """Exact draws: the k-th victim of a stream is output k of SplitMix64 seeded with `seed`, reduced modulo
+    the number of candidate slots, counted in slot order.  For [a], [b], [a] with B = 2 the third step misses
+    exactly when the first two draws pick the same slot."""
+    n, a, b = 50, 11, 12
+    sel = np.array([[a], [b], [a]], np.int32)
+    for seed in range(64):
+        st, r1 = _splitmix64(seed)
+        st, r2 = _splitmix64(st)
+        want = int(r1 % 2 == r2 % 2)
+        got = int(oracle.policy_replay(sel, n, 2, "random", seed=seed)[2])
+        assert got == want, seed
