@@ -49,6 +49,26 @@ def test_deferred_fetch_multiquery_staging():
     h.close()
 
 
+def test_deferred_fetch_shared_staging_arena():
+    """Three layers take turns in one shared staging arena (8 queries per request, unions overflowing into
+    staging every step): each layer's fetch writes its staged rows into the arena at the rows its resolve
+    emitted, checked against the oracle and the host rows before the next layer reuses the arena."""
+    w = synth.WORKLOADS["verify"].scaled(requests=6, layers=3, sources=3, ctx=20_000, queries=8, top_k=512,
+                                         hot_slots=1024, staging_rows=8 * 512, seed=7300)
+    h = Harness(w, steps=3, staging_arenas=1, deferred=True)
+    staged = 0
+    for t in range(h.steps):
+        for layer in range(w.layers):
+            res = h.resolve(layer, t)
+            h.check_bytes(res)
+            staged += int(res["stats"]["n_staged"].sum())
+            if t == h.steps - 1:
+                h.attention(layer, t, res, samples=[(0, 0), (5, 7)])
+    assert staged > 0, "the case must overflow into staging"
+    log(f"[fetch arena] staged rows over the run: {staged}")
+    h.close()
+
+
 def test_deferred_fetch_full_size_layers():
     """The 100K-context batch-64 shape, 4 layers with their own payloads, 2 steps, with the copy kernel's
     16 workgroups (the launch the overlapped benchmark schedule uses)."""
