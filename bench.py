@@ -521,9 +521,9 @@ def run_adaptive(hsk, synth, w, steps: int) -> dict:
 def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_blocks: int, split: int) -> dict:
     """The benchmark step with the host IO hidden under the other work (HiSparse section 3.5, overlap of IO
     with computation): the batch is served as M micro-batches of R/M requests, each with its own store (in
-    HSK_GATHER_DEFERRED mode) and stream, and one copy stream runs every hsk_fetch_plan in turn.  Per layer
-    and micro-batch: resolve (plan only) on the micro-batch's stream -> event -> fetch on the copy stream
-    -> event -> attention on the micro-batch's stream.  The copies are serialised on the link in issue
+    HSK_GATHER_DEFERRED mode) and stream, and one copy stream runs every fetch in turn.  Per layer and
+    micro-batch, one hsk_resolve_fetch_attend call: resolve (plan only) on the micro-batch's stream -> event
+    -> fetch on the copy stream -> event -> attention on the micro-batch's stream.  The copies are serialised on the link in issue
     order (micro-batch 0's layer l, then micro-batch 1's, ...), and while the copy stream fetches one
     micro-batch's rows the others resolve and attend; every request still runs its layers in order, each
     layer's attention after its own resolve and fetch.  The fetch kernel's few workgroups leave the other
@@ -540,7 +540,7 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
     Rm = R // M
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    stores, d_sel, d_q, d_locs, d_stats, pools, ads, scratch, outs = [], [], [], [], [], [], [], [], []
+    stores, d_sel, d_q, d_locs, d_stats, ads, scratch, outs = [], [], [], [], [], [], [], []
     for mb in range(M):
         st = hsk.KVStore(requests=Rm, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
                          tail_rows=w.tail_rows, ctx=w.ctx, max_queries=1, top_k=k, gather_blocks=fetch_blocks,
@@ -556,7 +556,6 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
                     for l in range(w.layers)])
         d_locs.append([torch.empty((Rm, 1, k), dtype=torch.int32, device=dev) for _ in range(w.layers)])
         d_stats.append([hsk.stats_tensor(Rm) for _ in range(w.layers)])
-        pools.append([st.pool_base(l) for l in range(w.layers)])
         ad = hsk.mla_desc(requests=Rm, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k,
                           row_elems=w.row_elems, scale=w.scale, split=split)
         ads.append(ad)
@@ -567,21 +566,14 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
     streams = [torch.cuda.Stream() for _ in range(M)]
     copy = torch.cuda.Stream()
     torch.cuda.synchronize()
-    planned = [torch.cuda.Event() for _ in range(M)]
-    fetched = [torch.cuda.Event() for _ in range(M)]
 
     def step(t):
         for l in range(w.layers):
             for mb in range(M):
-                s = streams[mb]
-                stores[mb].resolve_step(l, t + 1, d_sel[mb][l][t], d_locs[mb][l], d_stats[mb][l], stream=s)
-                planned[mb].record(s)
-                copy.wait_event(planned[mb])
-                stores[mb].fetch_plan(l, stream=copy)
-                fetched[mb].record(copy)
-                s.wait_event(fetched[mb])
-                hsk.sparse_decode_attn(ads[mb], d_q[mb][l][t], pools[mb][l], d_locs[mb][l], None, outs[mb],
-                                       scratch[mb][0], scratch[mb][1], stream=s)
+                # resolve (plan only) -> fetch on the copy stream -> attention, ordered by the store's events
+                stores[mb].resolve_fetch_attend(l, t + 1, d_sel[mb][l][t], d_locs[mb][l], ads[mb], d_q[mb][l][t],
+                                                outs[mb], scratch[mb][0], stats=d_stats[mb][l], stream=streams[mb],
+                                                copy_stream=copy)
 
     for t in range(W):
         step(t)

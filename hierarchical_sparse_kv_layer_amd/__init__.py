@@ -89,6 +89,8 @@ _sig = {
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
     "hsk_fetch_plan": (_i32, [_vp, _i32, _vp]),
+    "hsk_resolve_fetch_attend": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                        _vp, _vp]),
     "hsk_promote_staged": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_append_rows": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp]),
     "hsk_context_rows": (_i32, [_vp, _i32, _i32, _P(_i64)]),
@@ -296,6 +298,14 @@ def fetch_plan(store: int, source: int, stream=None) -> None:
     _check(_lib.hsk_fetch_plan(store, source, _stream(stream)), "hsk_fetch_plan")
 
 
+def resolve_fetch_attend(store: int, source: int, epoch: int, sel, nq, locs, stats, adesc, q, out, scratch,
+                         scratch_bytes: int, stream=None, copy_stream=None) -> None:
+    _check(_lib.hsk_resolve_fetch_attend(store, source, int(epoch), _ptr(sel), _ptr(nq), _ptr(locs), _ptr(stats),
+                                         ctypes.byref(adesc), _ptr(q), _ptr(out), _ptr(scratch), int(scratch_bytes),
+                                         _stream(stream), _stream(copy_stream if copy_stream is not None else stream)),
+           "hsk_resolve_fetch_attend")
+
+
 def promote_staged(store: int, source: int, locs, nq, accepted, promoted=None, stream=None) -> None:
     _check(_lib.hsk_promote_staged(store, source, _ptr(locs), _ptr(nq), _ptr(accepted), _ptr(promoted),
                                    _stream(stream)), "hsk_promote_staged")
@@ -457,6 +467,11 @@ class KVStore:
 
     def fetch_plan(self, source: int, stream=None):
         fetch_plan(self.handle, source, stream)
+
+    def resolve_fetch_attend(self, source: int, epoch: int, sel, locs, adesc, q, out, scratch, stats=None, nq=None,
+                             stream=None, copy_stream=None):
+        resolve_fetch_attend(self.handle, source, epoch, sel, nq, locs, stats, adesc, q, out, scratch,
+                             scratch.numel() * scratch.element_size(), stream, copy_stream)
 
     def pool_base(self, source: int) -> int:
         return pool_base(self.handle, source)

@@ -135,6 +135,8 @@ struct hsk_store {
   std::vector<hipEvent_t> wt_done;          // [S][2] write-through of the last two appends per source
   std::vector<uint8_t> wt_pending;          // [S][2] event recorded and not yet waited for
   std::vector<hipEvent_t> tail_done;        // [S] tail writes of the last append
+  std::vector<hipEvent_t> planned;          // [S] resolve (plan only) of hsk_resolve_fetch_attend done
+  std::vector<hipEvent_t> fetched;          // [S] its fetch done on the copy stream
   std::vector<int32_t> append_parity;       // [S]
   int32_t* d_err = nullptr;
   int32_t* d_fill = nullptr;                // [R][Qmax][k] per-selection host source of a fused call

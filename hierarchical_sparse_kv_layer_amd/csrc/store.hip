@@ -122,6 +122,10 @@ void hsk_kv_store_destroy(hsk_store* st) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : st->tail_done)
     if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->planned)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : st->fetched)
+    if (e) (void)hipEventDestroy(e);
   for (char* h : st->host)
     if (h) (void)hipHostFree(h);
   if (st->h_stage) (void)hipHostFree(st->h_stage);
@@ -158,6 +162,11 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   st->wt_pending.assign(2 * (size_t)desc->num_sources, 0);
   st->tail_done.assign((size_t)desc->num_sources, nullptr);
   st->append_parity.assign((size_t)desc->num_sources, 0);
+  st->planned.assign((size_t)desc->num_sources, nullptr);
+  st->fetched.assign((size_t)desc->num_sources, nullptr);
+  for (auto* v : {&st->planned, &st->fetched})
+    for (hipEvent_t& e : *v)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
   for (hipEvent_t& e : st->wt_done)
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
   for (hipEvent_t& e : st->tail_done)
@@ -387,6 +396,58 @@ hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, con
                           st->d.max_ctx * (int64_t)st->d.row_bytes, d_out, d_scratch, scratch_bytes, s);
 }
 
+static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s) {
+  void* pool;
+  hsk_pool_base(st, dst_source, &pool);
+  GatherArgs g;
+  const int32_t hs = st->d.host_alias_sources ? 0 : dst_source;
+  g.host = st->host[hs]; g.pool = (char*)pool;
+  g.plan_n = st->meta[plan_source].plan_n; g.plan_pos = st->meta[plan_source].plan_pos;
+  g.plan_dst = st->meta[plan_source].plan_dst;
+  g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
+  g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
+  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
+  return HSK_OK;
+}
+
+hsk_status hsk_resolve_fetch_attend(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel,
+                                    const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, const hsk_attn_desc* desc,
+                                    const void* d_q, void* d_out, void* d_scratch, size_t scratch_bytes,
+                                    hsk_stream_t stream, hsk_stream_t copy_stream) {
+  if (!st || source < 0 || source >= st->d.num_sources || !d_sel || !d_locs || !desc || !d_q || !d_out ||
+      !d_scratch)
+    return HSK_EINVAL;
+  if (st->d.gather_mode != HSK_GATHER_DEFERRED) return HSK_EINVAL;
+  // the attention reads this store's rows at the emitted locations: the same resolution units (requests, or
+  // request x KV head for GQA pages), queries, k and row width
+  const int64_t units = desc->kind == HSK_ATTN_GQA ? (int64_t)desc->num_requests * desc->kv_heads : desc->num_requests;
+  if (units != st->d.num_requests || desc->max_queries != st->d.max_queries || desc->top_k != st->d.top_k ||
+      (int64_t)desc->row_elems * 2 != st->d.row_bytes)
+    return HSK_EINVAL;
+  size_t need = 0;
+  if (hsk_attn_scratch_bytes(desc, &need) != HSK_OK || scratch_bytes < need || ((uintptr_t)d_scratch % 256))
+    return HSK_EINVAL;
+  if (st->replay_dst[source]) return HSK_ESTATE;
+  if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
+  hipStream_t s = (hipStream_t)stream, c = (hipStream_t)copy_stream;
+  ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
+  HSK_HIP(launch_resolve(a, s));
+  st->last_epoch[source] = epoch;
+  if (c != s) {
+    HSK_HIP(hipEventRecord(st->planned[source], s));
+    HSK_HIP(hipStreamWaitEvent(c, st->planned[source], 0));
+  }
+  const hsk_status f = gather_plan(st, source, source, c);
+  if (f != HSK_OK) return f;
+  if (c != s) {
+    HSK_HIP(hipEventRecord(st->fetched[source], c));
+    HSK_HIP(hipStreamWaitEvent(s, st->fetched[source], 0));
+  }
+  void* pool;
+  hsk_pool_base(st, source, &pool);
+  return hsk_sparse_decode_attn(desc, d_q, pool, d_locs, d_nq, d_out, d_scratch, scratch_bytes, stream);
+}
+
 hsk_status hsk_append_rows(hsk_store* st, int32_t source, const void* d_rows, int32_t count, hsk_stream_t stream,
                            hsk_stream_t backup_stream) {
   if (!st || source < 0 || source >= st->d.num_sources || !d_rows || count < 1 || 2 * count > st->d.tail_rows ||
@@ -466,20 +527,6 @@ hsk_status hsk_context_rows(hsk_store* st, int32_t source, int32_t req, int64_t*
 
 // The rows of plan_source's last miss plan, from dst_source's host rows into dst_source's pool at the plan's
 // pool rows: the gather kernel, gather_blocks workgroups.
-static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s) {
-  void* pool;
-  hsk_pool_base(st, dst_source, &pool);
-  GatherArgs g;
-  const int32_t hs = st->d.host_alias_sources ? 0 : dst_source;
-  g.host = st->host[hs]; g.pool = (char*)pool;
-  g.plan_n = st->meta[plan_source].plan_n; g.plan_pos = st->meta[plan_source].plan_pos;
-  g.plan_dst = st->meta[plan_source].plan_dst;
-  g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
-  g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
-  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
-  return HSK_OK;
-}
-
 hsk_status hsk_replay_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hsk_stream_t stream) {
   if (!st || plan_source < 0 || plan_source >= st->d.num_sources || dst_source < 0 ||
       dst_source >= st->d.num_sources || plan_source == dst_source)

@@ -356,6 +356,7 @@ hsk_status hsk_replay_plan(hsk_store* store, int32_t plan_source, int32_t dst_so
  * ESTATE: no resolve on that source yet, or a replay destination. */
 hsk_status hsk_fetch_plan(hsk_store* store, int32_t source, hsk_stream_t stream);
 
+
 /*
  * Promotion copy-back ("Adaptive DHiSparse: Speculative Decoding over a Load-Adaptive KV Hierarchy", section
  * 3.4 and Figure 3 callout 3: staged rows that are promoted are copied back to stable hot-cache addresses
@@ -465,6 +466,30 @@ hsk_status hsk_sparse_decode_attn_noalloc(const hsk_attn_desc* desc, const void*
 hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
                               int32_t* d_locs, hsk_stats* d_stats, const hsk_attn_desc* desc, const void* d_q,
                               void* d_out, void* d_scratch, size_t scratch_bytes, hsk_stream_t stream);
+
+/*
+ * One layer of a deferred store with its host IO overlapped (HiSparse section 3.5: plan, then IO beside other
+ * work; Adaptive DHiSparse Eq. 1 attention over the resolved rows).  Queues, in order:
+ *   on `stream`       the resolve of hsk_resolve_step (plan only), then an event;
+ *   on `copy_stream`  a wait for that event, the fetch of hsk_fetch_plan, then an event;
+ *   on `stream`       a wait for the fetch, then hsk_sparse_decode_attn(desc, d_q, pool of `source`, d_locs, d_nq,
+ *                     d_out, d_scratch, scratch_bytes).
+ * While the copy stream streams this source's missing rows over the host link, the caller's other streams (other
+ * micro-batches, other work) run; the attention starts when its rows are in.  Calls for different stores or
+ * sources sharing one copy stream are fetched in call order, one at a time.  copy_stream may equal stream (no
+ * events then).  The events belong to the store, one pair per source.
+ *   d_sel, d_nq, d_locs, d_stats, epoch: as hsk_resolve_step.
+ *   desc: any attention descriptor whose resolution units (num_requests; num_requests x kv_heads for
+ *         HSK_ATTN_GQA), max_queries and top_k equal the store's requests, max_queries and top_k, and with
+ *         row_elems * 2 = row_bytes; d_q, d_out, d_scratch, scratch_bytes as hsk_sparse_decode_attn.
+ * EINVAL (nothing queued): a store not in HSK_GATHER_DEFERRED mode, a descriptor hsk_sparse_decode_attn would
+ * reject or that does not match the store, too small or misaligned scratch; ESTATE for a replay destination;
+ * EEPOCH as hsk_resolve_step.  Outputs of a request the resolve rejects are undefined (status in its stats).
+ */
+hsk_status hsk_resolve_fetch_attend(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
+                                    const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats,
+                                    const hsk_attn_desc* desc, const void* d_q, void* d_out, void* d_scratch,
+                                    size_t scratch_bytes, hsk_stream_t stream, hsk_stream_t copy_stream);
 
 /* ---------------------------------------------------------------------------------------------------- */
 /* Inspection (tests) and lifetime                                                                     */

@@ -124,8 +124,10 @@ class Harness:
         return q, dropped
 
     # ------------------------------------------------------------------------------------------------
-    def resolve(self, layer: int, step: int, check: bool = True, meta_reqs=None, fused: bool = False):
-        """One resolve call (fused: hsk_resolve_attend, whose attention output is kept as res["out"])."""
+    def resolve(self, layer: int, step: int, check: bool = True, meta_reqs=None, fused: bool = False,
+                overlap: bool = False, same_stream: bool = False):
+        """One resolve call (fused: hsk_resolve_attend; overlap: hsk_resolve_fetch_attend on a deferred store,
+        with the fetch on the side stream unless same_stream; the attention output is kept as res["out"])."""
         w = self.w
         src = self.source_of(layer)
         e = self.epoch_of(layer, step)
@@ -137,6 +139,11 @@ class Harness:
         if fused:
             q, ad, out, scratch = self._attn_inputs(layer, step)
             self.store.resolve_attend(src, e, d_sel, d_locs, ad, q, out, scratch, stats=d_stats)
+        elif overlap:
+            q, ad, out, scratch = self._attn_inputs(layer, step)
+            main = torch.cuda.current_stream()
+            self.store.resolve_fetch_attend(src, e, d_sel, d_locs, ad, q, out, scratch, stats=d_stats, stream=main,
+                                            copy_stream=main if same_stream else self.copy_stream)
         else:
             self.store.resolve_step(src, e, d_sel, d_locs, d_stats)
             if self.deferred:

@@ -128,3 +128,63 @@ def test_fetch_errors():
             got = pool.index_select(0, locs[r].reshape(-1).long()).cpu().numpy()
             assert np.array_equal(got, st.host_rows(s, r)[sel[r].reshape(-1).cpu().numpy()]), (s, r)
     st.close()
+
+
+OVERLAP_CASES = {
+    "tiny_mla16": ("tiny", dict(requests=5, top_k=129, hot_slots=300, heads=16)),
+    "mla128_k2048": ("tiny", dict(requests=3, ctx=30_000, top_k=2048, hot_slots=4096, heads=128, keep_frac=0.6)),
+    "verify_8q": ("verify", dict(requests=4, ctx=20_000, queries=8, top_k=512, hot_slots=1024, staging_rows=8 * 512)),
+    "quest_gqa": ("quest", dict(requests=2, layers=1)),
+}
+
+
+@pytest.mark.parametrize("case", list(OVERLAP_CASES))
+@pytest.mark.parametrize("same_stream", [False, True])
+def test_resolve_fetch_attend(case, same_stream):
+    """hsk_resolve_fetch_attend: resolve (plan only), fetch on the copy stream, attention after it, in one call:
+    resolution bit-exact against the oracle, pool bytes equal to the host rows, attention within tolerance of the
+    fp64 oracle; MLA with 16 and 128 heads, 8 queries per request with staging, GQA pages; copy stream distinct from
+    or equal to the stream."""
+    base, kw = OVERLAP_CASES[case]
+    w = synth.WORKLOADS[base].scaled(**kw, seed=7400 + len(case))
+    h = Harness(w, steps=3, deferred=True)
+    for t in range(h.steps):
+        res = h.resolve(0, t, overlap=True, same_stream=same_stream)
+        h.check_bytes(res, source=0)
+        if w.kind == "mla":
+            samples = [(r, j) for r in range(min(w.requests, 3)) for j in (0, w.queries - 1)]
+        else:
+            samples = [0, 3, h.U - 1]
+        err = h.check_attention(0, t, res, res["out"], samples=samples, source=0)
+        log(f"[overlap {case}] step {t}: misses={int(res['stats']['n_miss'].sum())} attn err {err[0]:.2e}")
+    h.close()
+
+
+def test_resolve_fetch_attend_rejects_and_changes_nothing():
+    """A zero-copy store, a descriptor for another batch, k or row width, and too little scratch are rejected
+    before anything is queued: the same epoch then works."""
+    w = synth.WORKLOADS["tiny"].scaled(requests=2, top_k=64, hot_slots=128, heads=16, seed=77)
+    h = Harness(w, steps=2, deferred=True)
+    q, ad, out, scratch = h._attn_inputs(0, 0)
+    sel = torch.from_numpy(h.sel[0][0]).cuda()
+    locs = torch.empty_like(sel)
+    bad = [hsk.mla_desc(requests=3, max_queries=1, heads=16, dk=576, dv=512, top_k=64, row_elems=576, scale=0.04),
+           hsk.mla_desc(requests=2, max_queries=1, heads=16, dk=576, dv=512, top_k=32, row_elems=576, scale=0.04),
+           hsk.mla_desc(requests=2, max_queries=1, heads=16, dk=576, dv=512, top_k=64, row_elems=584, scale=0.04)]
+    for d in bad:
+        with pytest.raises(hsk.HskError) as e:
+            h.store.resolve_fetch_attend(0, 1, sel, locs, d, q, out, scratch)
+        assert e.value.status == hsk.HSK_EINVAL
+    with pytest.raises(hsk.HskError) as e:
+        h.store.resolve_fetch_attend(0, 1, sel, locs, ad, q, out, scratch[:128])
+    assert e.value.status == hsk.HSK_EINVAL
+    res = h.resolve(0, 0, overlap=True)
+    h.check_bytes(res)
+    h.check_attention(0, 0, res, res["out"])
+    h.close()
+    zc = hsk.KVStore(requests=2, sources=1, row_bytes=1152, hot_slots=128, tail_rows=64, ctx=8192, max_queries=1,
+                     top_k=64)
+    with pytest.raises(hsk.HskError) as e:
+        zc.resolve_fetch_attend(0, 1, sel, locs, ad, q, out, scratch)
+    assert e.value.status == hsk.HSK_EINVAL
+    zc.close()
