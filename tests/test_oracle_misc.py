@@ -155,7 +155,7 @@ def test_sizing_worked_examples():
     assert abs(live - s["gib_live"]) < 0.005
     assert abs(full - s["gib_all"]) < 0.05
     assert abs(full / live - s["ratio"]) < 1e-9
-    # Eq. 10: two live positions of one request never share a ring row, and slots occupy disjoint ranges
+    # Eq. 10: within a slot, positions alive together map to different ring rows; each slot owns its own block of rows
     for t1, t2 in itertools.combinations(range(0, 3 * ring, 97), 2):
         if abs(t1 - t2) < ring:
             assert oracle.ring_addr(3, t1, ring) != oracle.ring_addr(3, t2, ring)
