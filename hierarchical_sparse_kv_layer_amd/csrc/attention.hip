@@ -221,9 +221,11 @@ __global__ __launch_bounds__(128 * NPAIR) void mla_mfma_kernel(MlaArgs a) {
   const int dw = kSplitRoles ? wave - 4 : wave;
   const int my_dma = dw < 0 ? 0 : (kDmaPerTile - dw + NWD - 1) / NWD;
 
+  // a negative location (every location of a request the resolve rejected is -1) reads row 0: such a
+  // query's output is meaningless, but no load leaves the pool
   const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
   for (int x = tid; x < nrows; x += NT) {
-    s_loc[x] = locs[x];
+    s_loc[x] = max(locs[x], 0);
     if constexpr (FUSED) s_fill[x] = a.fill[(int64_t)rq * a.k + i0 + x];
   }
   const char* hostr = FUSED ? a.host + (int64_t)(rq / a.Qmax) * a.host_req_stride : nullptr;
@@ -556,7 +558,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   const int hbase = hgrp * (32 * NW) + wave * 32;
 
   const int32_t* locs = a.locs + (int64_t)rq * a.k + i0;
-  for (int x = tid; x < nrows; x += NT) s_loc[x] = locs[x];
+  // negative locations (a request the resolve rejected) read row 0: meaningless output, no load outside the pool
+  for (int x = tid; x < nrows; x += NT) s_loc[x] = max(locs[x], 0);
   __syncthreads();
   // The query block is requested first, then the first tiles: loads of a wave complete in order, so the
   // first score products (which wait for the query chunks as the compiler counts them, i.e. for
@@ -967,7 +970,8 @@ __global__ __launch_bounds__(256) void gqa_attn_kernel(GqaArgs a) {
   }
   // the partition's page locations go to LDS first: a tile's loads then wait for an LDS read, not for a
   // global one (whose in-order counter would also make them wait for the loads already in flight)
-  for (int x = threadIdx.x; x < npages; x += 256) s_loc[x] = locs[x];
+  // negative locations (a unit the resolve rejected) read page row 0: meaningless output, no load outside the pool
+  for (int x = threadIdx.x; x < npages; x += 256) s_loc[x] = max(locs[x], 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const uint32_t lds0 = (uint32_t)(uintptr_t)(const HSK_LDS char*)&s_tile[0][0];

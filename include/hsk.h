@@ -418,7 +418,9 @@ hsk_status hsk_attn_scratch_bytes(const hsk_attn_desc* desc, size_t* scratch_byt
  *   MLA: d_q bf16 [R][Qmax][H][dk]; d_locs int32 [R][Qmax][k]; d_out bf16 [R][Qmax][H][dv];
  *        d_nq int32 [R] or NULL (queries j >= nq[r] are skipped and their outputs left untouched).
  *   GQA: d_q bf16 [R][H][dk]; d_locs int32 [R * kv_heads][k] (page rows); d_out bf16 [R][H][dk].
- *   d_pool: row 0 of the source's pool (hsk_pool_base); every location must be a valid row of it.
+ *   d_pool: row 0 of the source's pool (hsk_pool_base); every non-negative location must be a valid row of
+ *           it.  A negative location (the -1 that hsk_resolve_step writes for every selection of a request it
+ *           rejects) is read as row 0: the query's output is then meaningless, but no load leaves the pool.
  *   d_scratch: at least hsk_attn_scratch_bytes bytes, 256-byte aligned.
  */
 hsk_status hsk_sparse_decode_attn(const hsk_attn_desc* desc, const void* d_q, const void* d_pool,
@@ -484,7 +486,8 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
  *         row_elems * 2 = row_bytes; d_q, d_out, d_scratch, scratch_bytes as hsk_sparse_decode_attn.
  * EINVAL (nothing queued): a store not in HSK_GATHER_DEFERRED mode, a descriptor hsk_sparse_decode_attn would
  * reject or that does not match the store, too small or misaligned scratch; ESTATE for a replay destination;
- * EEPOCH as hsk_resolve_step.  Outputs of a request the resolve rejects are undefined (status in its stats).
+ * EEPOCH as hsk_resolve_step.  Outputs of a request the resolve rejects (status in its stats) are meaningless:
+ * its locations are -1, which the attention reads as row 0.
  */
 hsk_status hsk_resolve_fetch_attend(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
                                     const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats,

@@ -188,3 +188,96 @@ def test_resolve_fetch_attend_rejects_and_changes_nothing():
         zc.resolve_fetch_attend(0, 1, sel, locs, ad, q, out, scratch)
     assert e.value.status == hsk.HSK_EINVAL
     zc.close()
+
+
+def test_resolve_fetch_attend_query_counts_match_separate_calls():
+    """Per-request query counts (nq = 1, 3, 0, 2 of Qmax = 3): a deferred store through hsk_resolve_fetch_attend
+    and a zero-copy store through hsk_resolve_step + hsk_sparse_decode_attn, same inputs, give identical
+    locations and statistics, identical pool bytes at every location, and bit-identical attention outputs
+    (same kernel, same partitions, same rows) for the queries that exist; the skipped queries' outputs stay
+    untouched."""
+    R, Q, k, B, T, n = 4, 3, 96, 512, 16, 3000   # B >= Q k: no union overflows, no request is rejected
+    w = synth.WORKLOADS["tiny"].scaled(requests=R, queries=Q, top_k=k, hot_slots=B, tail_rows=T, ctx=n, heads=64,
+                                       seed=7700)
+    kw = dict(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=B, tail_rows=T, ctx=n, max_queries=Q, top_k=k)
+    zc = hsk.KVStore(**kw)
+    df = hsk.KVStore(gather_mode=hsk.GATHER_DEFERRED, **kw)
+    for st in (zc, df):
+        for r in range(R):
+            synth.fill_kv_rows(st.host_ptr(0, r), w, 0, r, 0, n)
+        st.commit_prefill()
+    nq = torch.tensor([1, 3, 0, 2], dtype=torch.int32, device="cuda")
+    ad = hsk.mla_desc(requests=R, max_queries=Q, heads=64, dk=576, dv=512, top_k=k, row_elems=576, scale=576 ** -0.5)
+    nb = hsk.attn_scratch_bytes(ad)
+    sc = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    copy = torch.cuda.Stream()
+    sels = synth.selection_stream(w, 0, steps=4)
+    for t in range(4):
+        sel = torch.from_numpy(sels[t]).cuda()
+        q = torch.from_numpy(synth.queries(w, 0, t).view(np.int16)).cuda()
+        outs = [torch.full((R, Q, 64, 512), 77, dtype=torch.int16, device="cuda") for _ in range(2)]
+        locs = [torch.full_like(sel, -7) for _ in range(2)]
+        stats = [hsk.stats_tensor(R) for _ in range(2)]
+        zc.resolve_step(0, t + 1, sel, locs[0], stats[0], nq=nq)
+        hsk.sparse_decode_attn(ad, q, zc.pool_base(0), locs[0], nq, outs[0], sc[0], nb)
+        df.resolve_fetch_attend(0, t + 1, sel, locs[1], ad, q, outs[1], sc[1], stats=stats[1], nq=nq,
+                                copy_stream=copy)
+        torch.cuda.synchronize()
+        assert zc.sync_status() == 0 and df.sync_status() == 0
+        assert torch.equal(locs[0], locs[1])
+        s0, s1 = hsk.stats_to_numpy(stats[0]), hsk.stats_to_numpy(stats[1])
+        for f in s0.dtype.names:
+            if f != "pad":
+                assert np.array_equal(s0[f], s1[f]), f
+        for r in range(R):
+            m = int(nq[r])
+            if m == 0:
+                continue
+            rows = locs[1][r, :m].reshape(-1).long()
+            assert torch.equal(zc.pool_rows(0).index_select(0, rows), df.pool_rows(0).index_select(0, rows))
+            assert torch.equal(outs[0][r, :m], outs[1][r, :m]), (t, r)
+            assert bool((outs[1][r, m:] == 77).all()), "a skipped query's output was written"
+    zc.close()
+    df.close()
+
+
+def test_resolve_fetch_attend_rejected_request_reads_inside_the_pool():
+    """A request whose union overflows the hot slots with no staging rows is rejected (ESTAGE, locations -1);
+    the call's attention still runs over the batch: the rejected request's locations are read as row 0 (no
+    load outside the pool), and every other request's output equals the separate calls' on a zero-copy store."""
+    R, Q, k, B, T, n = 3, 3, 96, 256, 16, 3000
+    w = synth.WORKLOADS["tiny"].scaled(requests=R, queries=Q, top_k=k, hot_slots=B, tail_rows=T, ctx=n, heads=64,
+                                       seed=7700)
+    sel_np = synth.selection_stream(w, 0, steps=1)[0].copy()
+    # request 1: three disjoint lists of 96 rows below the tail -> a 288-row union against 256 slots; requests
+    # 0 and 2 use one query each (95 distinct rows)
+    sel_np[1] = np.arange(3 * k, dtype=np.int32).reshape(Q, k) + 100
+    nq = torch.tensor([1, 3, 1], dtype=torch.int32, device="cuda")
+    kw = dict(requests=R, sources=1, row_bytes=w.row_bytes, hot_slots=B, tail_rows=T, ctx=n, max_queries=Q, top_k=k)
+    zc = hsk.KVStore(**kw)
+    df = hsk.KVStore(gather_mode=hsk.GATHER_DEFERRED, **kw)
+    for st in (zc, df):
+        for r in range(R):
+            synth.fill_kv_rows(st.host_ptr(0, r), w, 0, r, 0, n)
+        st.commit_prefill()
+    ad = hsk.mla_desc(requests=R, max_queries=Q, heads=64, dk=576, dv=512, top_k=k, row_elems=576, scale=576 ** -0.5)
+    nb = hsk.attn_scratch_bytes(ad)
+    sc = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    sel = torch.from_numpy(sel_np).cuda()
+    q = torch.from_numpy(synth.queries(w, 0, 0).view(np.int16)).cuda()
+    outs = [torch.zeros((R, Q, 64, 512), dtype=torch.int16, device="cuda") for _ in range(2)]
+    locs = [torch.full_like(sel, -7) for _ in range(2)]
+    stats = [hsk.stats_tensor(R) for _ in range(2)]
+    zc.resolve_step(0, 1, sel, locs[0], stats[0], nq=nq)
+    hsk.sparse_decode_attn(ad, q, zc.pool_base(0), locs[0], nq, outs[0], sc[0], nb)
+    df.resolve_fetch_attend(0, 1, sel, locs[1], ad, q, outs[1], sc[1], stats=stats[1], nq=nq,
+                            copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert zc.sync_status() == hsk.HSK_ESTAGE and df.sync_status() == hsk.HSK_ESTAGE
+    s1 = hsk.stats_to_numpy(stats[1])
+    assert s1["status"][1] == hsk.HSK_ESTAGE and s1["status"][0] == 0 and s1["status"][2] == 0
+    assert torch.equal(locs[0], locs[1]) and bool((locs[1][1] == -1).all())
+    for r in (0, 2):
+        assert torch.equal(outs[0][r, 0], outs[1][r, 0]), r
+    zc.close()
+    df.close()
