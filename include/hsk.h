@@ -479,7 +479,9 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
  * While the copy stream streams this source's missing rows over the host link, the caller's other streams (other
  * micro-batches, other work) run; the attention starts when its rows are in.  Calls for different stores or
  * sources sharing one copy stream are fetched in call order, one at a time.  copy_stream may equal stream (no
- * events then).  The events belong to the store, one pair per source.
+ * events then).  The events belong to the store, one pair per source.  The source's next call comes after
+ * this one's fetch when it is queued on the same `stream` (its attention waits for the fetch); on another
+ * stream the caller orders it after this call's attention.
  *   d_sel, d_nq, d_locs, d_stats, epoch: as hsk_resolve_step.
  *   desc: any attention descriptor whose resolution units (num_requests; num_requests x kv_heads for
  *         HSK_ATTN_GQA), max_queries and top_k equal the store's requests, max_queries and top_k, and with
