@@ -1,7 +1,8 @@
 """GPU parity at the benchmark's full sizes, in the launch configurations the benchmark times, for the
 workloads whose other parity tests run scaled down: speculative verification (128 requests x 16 queries:
 2,048 queries, one attention partition), page-level GQA with plan replay (32 requests x 8 KV heads = 256
-units) and load-adaptive residency (64 requests, 500,000-row context, reclaim of 16 requests).
+units) and load-adaptive residency (64 requests, 500,000-row context, reclaim of 16 requests); and the
+100K-context batch-64 decode in the benchmark's overlapped schedule (two micro-batches of 32 requests).
 
 Resolution is compared bit-exactly on every call (locations, statistics, miss plan; slot metadata on a
 subset of requests); pool bytes and attention on sampled requests.  Attention within
@@ -16,6 +17,8 @@ torch = pytest.importorskip("torch")
 if not torch.cuda.is_available():  # pragma: no cover - CPU containers
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import hierarchical_sparse_kv_layer_amd as hsk  # noqa: E402
+import oracle  # noqa: E402
 import synth  # noqa: E402
 from hsk_harness import Harness, log  # noqa: E402
 
@@ -93,3 +96,61 @@ def test_adaptive_full_size_reclaim_sampled():
             tot_sel += int(res["stats"]["n_sel"].sum())
         log(f"[full adaptive] step {t}: host-fetch fraction {tot_miss / tot_sel:.4f}")
     h.close()
+
+
+def test_dsa100k_overlapped_schedule_full_size():
+    """The benchmark's overlapped step at full size: two micro-batches of 32 requests (deferred stores, 4 layers
+    with their own payloads, 100,000-row contexts), each on its own stream, one copy stream shared by both
+    (16 copy workgroups), attention in 3 partitions per request, all calls of a step queued before any check.
+    Every call's locations and statistics against the oracle, bit for bit; pool bytes and attention sampled."""
+    base = synth.WORKLOADS["dsa100k"]
+    M, Rm = 2, base.requests // 2
+    ws = [base.scaled(requests=Rm, seed=base.seed + 100 * mb) for mb in range(M)]
+    log(f"[full overlap] {M} micro-batches x {Rm} requests, {base.layers} layers, ctx={base.ctx}")
+    hs = [Harness(w, steps=2, gather_blocks=16, check_meta_every=2, deferred=True) for w in ws]
+    streams = [torch.cuda.Stream() for _ in range(M)]
+    copy = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    for t in range(hs[0].steps):
+        # every input of the step first (on the default stream), then all calls queued without a host wait, in the
+        # benchmark's order: layer by layer, micro-batch 0 then 1
+        calls = []
+        for layer in range(base.layers):
+            for mb, (h, w) in enumerate(zip(hs, ws)):
+                sel = h.sel[layer][t]
+                d_sel = torch.from_numpy(sel).cuda()
+                ad = hsk.mla_desc(requests=Rm, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=w.top_k,
+                                  row_elems=w.row_elems, scale=w.scale, split=3)
+                calls.append(dict(mb=mb, layer=layer, sel=sel, d_sel=d_sel, d_locs=torch.full_like(d_sel, -7),
+                                  d_stats=hsk.stats_tensor(Rm), ad=ad,
+                                  q=torch.from_numpy(synth.queries(w, layer, t).view(np.int16)).cuda(),
+                                  out=torch.zeros((Rm, 1, w.heads, w.dv), dtype=torch.int16, device="cuda"),
+                                  scratch=torch.empty(hsk.attn_scratch_bytes(ad), dtype=torch.uint8, device="cuda")))
+        torch.cuda.synchronize()
+        for c in calls:
+            h = hs[c["mb"]]
+            h.store.resolve_fetch_attend(h.source_of(c["layer"]), h.epoch_of(c["layer"], t), c["d_sel"], c["d_locs"],
+                                         c["ad"], c["q"], c["out"], c["scratch"], stats=c["d_stats"],
+                                         stream=streams[c["mb"]], copy_stream=copy)
+        torch.cuda.synchronize()
+        for c in calls:
+            mb, layer, sel, d_locs, d_stats, out = c["mb"], c["layer"], c["sel"], c["d_locs"], c["d_stats"], c["out"]
+            h, w = hs[mb], ws[mb]
+            src = h.source_of(layer)
+            assert h.store.sync_status() == 0
+            o = h.ora[src].resolve(h.epoch_of(layer, t), sel)
+            locs = d_locs.cpu().numpy()
+            assert np.array_equal(locs, o["locs"]), (mb, layer, t)
+            st = hsk.stats_to_numpy(d_stats)
+            for f in oracle.STATS_DTYPE.names:
+                if f != "pad":
+                    assert np.array_equal(st[f], o["stats"][f]), (mb, layer, t, f)
+            reqs = [int(r) for r in rng.choice(Rm, size=2, replace=False)]
+            res = {"sel": sel, "d_locs": d_locs, "src": src}
+            h.check_bytes(res, reqs=reqs)
+            err = h.check_attention(layer, t, res, out, samples=[(r, 0) for r in reqs])
+            log(f"[full overlap] step {t} layer {layer} micro-batch {mb}: miss={int(st['n_miss'].sum())} "
+                f"attn err {err[0]:.2e}")
+    for h in hs:
+        h.close()
