@@ -281,3 +281,35 @@ def test_resolve_fetch_attend_rejected_request_reads_inside_the_pool():
         assert torch.equal(outs[0][r, 0], outs[1][r, 0]), r
     zc.close()
     df.close()
+
+
+def test_fetch_edge_cases():
+    """One request; a call whose rows are all hits (an empty plan: the fetch copies nothing and the pool keeps its
+    bytes); the same plan fetched twice (the second copy writes the same bytes again)."""
+    w = synth.WORKLOADS["tiny"].scaled(requests=1, top_k=64, hot_slots=128, heads=16, seed=7800)
+    h = Harness(w, steps=1, deferred=True)
+    res = h.resolve(0, 0)                          # cold: every non-tail row misses
+    h.check_bytes(res)
+    assert int(res["stats"]["n_miss"].sum()) > 0
+    sel = torch.from_numpy(h.sel[0][0]).cuda()
+    locs = torch.empty_like(sel)
+    stats = hsk.stats_tensor(1)
+    before = h.store.pool_rows(0).clone()
+    h.store.resolve_step(0, 2, sel, locs, stats)   # the same selection again: all hits
+    h.store.fetch_plan(0)
+    torch.cuda.synchronize()
+    assert h.store.sync_status() == 0
+    st = hsk.stats_to_numpy(stats)
+    assert int(st["n_miss"][0]) == 0 and int(st["n_hit_sel"][0]) + int(st["n_tail"][0]) == w.top_k
+    assert torch.equal(before, h.store.pool_rows(0)), "an empty plan changed the pool"
+    assert h.store.read_plan(0, 0)[0].size == 0
+    # a new selection with misses, fetched twice
+    sel2 = torch.from_numpy(((h.sel[0][0] + 997) % (w.ctx - w.tail_rows)).astype(np.int32)).cuda()
+    h.store.resolve_step(0, 3, sel2, locs, stats)
+    h.store.fetch_plan(0)
+    h.store.fetch_plan(0)
+    torch.cuda.synchronize()
+    assert h.store.sync_status() == 0 and int(hsk.stats_to_numpy(stats)["n_miss"][0]) > 0
+    got = h.store.pool_rows(0).index_select(0, locs.reshape(-1).long()).cpu().numpy()
+    assert np.array_equal(got, h.store.host_rows(0, 0)[sel2.cpu().numpy().reshape(-1)])
+    h.close()
