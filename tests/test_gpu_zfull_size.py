@@ -42,6 +42,27 @@ def test_verify_full_size_launch_sampled():
     h.close()
 
 
+def test_quest_full_size_overlapped_layer():
+    """Page-level GQA at full size through hsk_resolve_fetch_attend on a deferred store: 256 units, top 256 of
+    8,192 pages, the layer-0 resolve, its fetch on a copy stream and the page attention in one call; then layer
+    1's replay of the plan, which copies in deferred stores too.  Resolution bit-exact, pool bytes and attention
+    sampled."""
+    w = synth.WORKLOADS["quest"]
+    log(f"[full quest overlap] R={w.requests} Hkv={w.kv_heads} k={w.top_k} pages={w.ctx}")
+    h = Harness(w, steps=2, deferred=True)
+    rng = np.random.default_rng(29)
+    for t in range(h.steps):
+        res = h.resolve(0, t, overlap=True, meta_reqs=range(0, h.U, 51))
+        units = [int(u) for u in rng.choice(h.U, size=4, replace=False)]
+        h.check_bytes(res, source=0, reqs=units)
+        err = h.check_attention(0, t, res, res["out"], samples=units, source=0)
+        if t == 0:
+            h.store.replay_plan(0, 1)
+            h.check_bytes(res, source=1, reqs=units)
+        log(f"[full quest overlap] step {t}: misses={int(res['stats']['n_miss'].sum())} attn err {err[0]:.2e}")
+    h.close()
+
+
 def test_quest_full_size_replay_sampled():
     """Page-level GQA at full size: 256 (request, KV head) units, top 256 of 8,192 pages, layer 0 resolves
     and layers 1-7 replay its miss plan on a side stream; every layer's attention sampled."""
