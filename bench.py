@@ -488,8 +488,7 @@ def _verify_overlapped(hsk, synth, w, steps: int, sels, q, M: int = 2, fetch_blo
             for mb in range(M)]
     qm = [[q[l][mb * Rm:(mb + 1) * Rm].contiguous() for l in range(L)] for mb in range(M)]
     log(f"[verify] overlapped schedule: {M} micro-batches set up in {time.perf_counter() - t0:.1f} s")
-    streams = [torch.cuda.Stream() for _ in range(M)]
-    copy = torch.cuda.Stream()
+    *streams, copy = hsk.dedicated_streams(M + 1)
     torch.cuda.synchronize()
 
     def step(t):
@@ -608,10 +607,9 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
     compute units to the attention, whose `split` partitions per request (3: 96 workgroups for 32 requests)
     leave room for the fetch and the next resolve.  Same selections and queries as the serial step.
 
-    The M + 1 streams are consecutive new pool streams, not the current stream: HIP serves streams from a few
-    hardware queues (4 here), assigned in turn as the streams are created, and the pool's streams were created
-    together, so consecutive ones sit on different queues.  Two of them on one queue run in one FIFO (a fetch
-    then waits behind an attention), and the step slows from 1.71 to ~2.0 ms."""
+    The M + 1 streams each have a hardware queue of their own (hsk_stream_create): HIP serves ordinary streams
+    from a few hardware queues (4 here) handed out in turn, and two of the step's streams on one queue run as one
+    FIFO (a fetch then waits behind an attention; the step slows from 1.71 to ~2.0 ms)."""
     import torch
     R, k = w.requests, w.top_k
     assert R % M == 0
@@ -641,8 +639,7 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
         scratch.append((torch.empty(n, dtype=torch.uint8, device=dev), n))
         outs.append(torch.empty((Rm, 1, w.heads, w.dv), dtype=torch.int16, device=dev))
     log(f"[overlap] {M} micro-batches of {Rm} requests set up in {time.perf_counter() - t0:.1f} s")
-    streams = [torch.cuda.Stream() for _ in range(M)]
-    copy = torch.cuda.Stream()
+    *streams, copy = hsk.dedicated_streams(M + 1)
     torch.cuda.synchronize()
 
     def step(t):
@@ -744,14 +741,80 @@ def run_decode(hsk, synth, w, steps: int) -> dict:
     status = st.sync_status()
     tail_ok = all(st.context_rows(l, r) == w.ctx + steps for l in range(L) for r in range(R))
     st.close()
+    ov = _decode_overlapped(hsk, synth, w, steps, sels, rows, q, warm, half)
+    status = status or ov["status"]
+    tail_ok = tail_ok and ov.pop("context_grew")
     return {"workload": f"decode: {R} requests x 1 query, {L} layers with own payloads, context {w.ctx} growing by "
                         f"one row per step, B={w.hot_slots}, tail {w.tail_rows}, top-k {k} (the newest row "
                         f"always selected)", "steps_timed": timed,
             "rows_per_s": R * k * L * timed / t_all, "steps_per_s": timed / t_all,
             "append_call_ms": float(np.mean(app_ms)), "resolve_ms": float(np.mean(res_ms)),
-            "attention_ms": float(np.mean(att_ms)), "context_grew": tail_ok, "status": status,
+            "attention_ms": float(np.mean(att_ms)), "context_grew": tail_ok, "overlapped": ov, "status": status,
             "note": "append_call_ms covers the tail write on the main stream (event to event); the write-through "
                     "runs on a backup stream beside the following calls"}
+
+
+def _decode_overlapped(hsk, synth, w, steps: int, sels, rows, q, warm: int, timed: int, M: int = 2,
+                       fetch_blocks: int = 16, split: int = 3) -> dict:
+    """The decode loop in the overlapped schedule: M micro-batches of R/M requests, each a deferred store on its
+    own stream; per layer, the append (tail write and write-through both on the micro-batch's stream: a shared
+    backup stream would make each micro-batch's appends wait for the other's, locking them in step) then one
+    hsk_resolve_fetch_attend whose fetch runs on the copy stream shared by all.  Same rows, selections and
+    queries as the serial loop; the same steps timed."""
+    import torch
+    R, k, L = w.requests, w.top_k, w.layers
+    Rm = R // M
+    stores, outs, scr, ads, locs, stats = [], [], [], [], [], []
+    for mb in range(M):
+        st = hsk.KVStore(requests=Rm, sources=w.sources, row_bytes=w.row_bytes, hot_slots=w.hot_slots,
+                         tail_rows=w.tail_rows, ctx=w.ctx, max_ctx=w.ctx + steps, max_queries=1, top_k=k,
+                         gather_mode=hsk.GATHER_DEFERRED, gather_blocks=fetch_blocks)
+        for s_ in range(w.sources):
+            for r in range(Rm):
+                synth.fill_kv_rows(st.host_ptr(s_, r), w, s_, mb * Rm + r, 0, w.ctx)
+        st.commit_prefill()
+        stores.append(st)
+        ad = hsk.mla_desc(requests=Rm, max_queries=1, heads=w.heads, dk=w.dk, dv=w.dv, top_k=k,
+                          row_elems=w.row_elems, scale=w.scale, split=split)
+        ads.append(ad)
+        scr.append(torch.empty(hsk.attn_scratch_bytes(ad), dtype=torch.uint8, device="cuda"))
+        outs.append(torch.empty((Rm, 1, w.heads, w.dv), dtype=torch.int16, device="cuda"))
+        locs.append(torch.empty((Rm, 1, k), dtype=torch.int32, device="cuda"))
+        stats.append(hsk.stats_tensor(Rm))
+    part = lambda x, mb: x[mb * Rm:(mb + 1) * Rm].contiguous()  # noqa: E731
+    p_sel = [[[part(sels[l][t], mb) for t in range(steps)] for l in range(L)] for mb in range(M)]
+    p_rows = [[[part(rows[l][t], mb) for t in range(steps)] for l in range(L)] for mb in range(M)]
+    p_q = [[part(q[l], mb) for l in range(L)] for mb in range(M)]
+    *streams, copy = hsk.dedicated_streams(M + 1)
+    torch.cuda.synchronize()
+
+    def step(t):
+        for l in range(L):
+            for mb in range(M):
+                stores[mb].append_rows(l, p_rows[mb][l][t], 1, stream=streams[mb], backup_stream=streams[mb])
+                stores[mb].resolve_fetch_attend(l, t + 1, p_sel[mb][l][t], locs[mb], ads[mb], p_q[mb][l], outs[mb],
+                                                scr[mb], stats=stats[mb], stream=streams[mb], copy_stream=copy)
+
+    for t in range(warm):
+        step(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(warm, warm + timed):
+        step(t)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    for t in range(warm + timed, steps):
+        step(t)
+    torch.cuda.synchronize()
+    status = 0
+    grew = True
+    for st in stores:
+        status = status or st.sync_status()
+        grew = grew and all(st.context_rows(l, r) == w.ctx + steps for l in range(L) for r in range(Rm))
+        st.close()
+    return {"ms_per_step": el * 1e3 / timed, "steps_per_s": timed / el, "rows_per_s": R * k * L * timed / el,
+            "micro_batches": M, "requests_per_micro_batch": Rm, "fetch_workgroups": fetch_blocks,
+            "attention_partitions": split, "context_grew": grew, "status": status}
 
 
 def _loadstep_arm(hsk, synth, w, ls, optional: bool) -> dict:

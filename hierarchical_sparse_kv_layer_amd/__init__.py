@@ -89,6 +89,8 @@ _sig = {
     "hsk_resolve_step": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp]),
     "hsk_replay_plan": (_i32, [_vp, _i32, _i32, _vp]),
     "hsk_fetch_plan": (_i32, [_vp, _i32, _vp]),
+    "hsk_stream_create": (_i32, [ctypes.POINTER(_vp)]),
+    "hsk_stream_destroy": (_i32, [_vp]),
     "hsk_resolve_fetch_attend": (_i32, [_vp, _i32, _u32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                         _vp, _vp]),
     "hsk_promote_staged": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
@@ -292,6 +294,23 @@ def ring_window_locs(ring_rows: int, slots: int, window: int, t_end, locs, strea
 
 def replay_plan(store: int, plan_source: int, dst_source: int, stream=None) -> None:
     _check(_lib.hsk_replay_plan(store, plan_source, dst_source, _stream(stream)), "hsk_replay_plan")
+
+
+_DEDICATED = {}   # device -> torch streams on hardware queues of their own, kept for the life of the process
+
+
+def dedicated_streams(n: int) -> list:
+    """n torch streams, each on a hardware queue of its own (hsk_stream_create), for an overlapped schedule.
+    The streams are created on first use and reused by later calls on the same device; they stay alive until the
+    process ends, because PyTorch's caching allocator keeps referring to a stream that tensors were allocated on."""
+    import torch
+    dev = torch.cuda.current_device()
+    pool = _DEDICATED.setdefault(dev, [])
+    while len(pool) < n:
+        h = _vp()
+        _check(_lib.hsk_stream_create(ctypes.byref(h)), "hsk_stream_create")
+        pool.append(torch.cuda.ExternalStream(h.value))
+    return pool[:n]
 
 
 def fetch_plan(store: int, source: int, stream=None) -> None:

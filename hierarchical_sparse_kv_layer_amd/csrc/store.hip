@@ -410,6 +410,28 @@ static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_so
   return HSK_OK;
 }
 
+hsk_status hsk_stream_create(hsk_stream_t* stream) {
+  if (!stream) return HSK_EINVAL;
+  *stream = nullptr;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 1)
+    return HSK_EHIP;
+  std::vector<uint32_t> mask((size_t)(ncu + 31) / 32, 0xFFFFFFFFu);
+  hipStream_t s = nullptr;
+  if (hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data()) != hipSuccess || !s) {
+    (void)hipGetLastError();
+    return HSK_EHIP;
+  }
+  *stream = (hsk_stream_t)s;
+  return HSK_OK;
+}
+
+hsk_status hsk_stream_destroy(hsk_stream_t stream) {
+  if (!stream) return HSK_EINVAL;
+  return hipStreamDestroy((hipStream_t)stream) == hipSuccess ? HSK_OK : HSK_EHIP;
+}
+
 hsk_status hsk_resolve_fetch_attend(hsk_store* st, int32_t source, uint32_t epoch, const int32_t* d_sel,
                                     const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats, const hsk_attn_desc* desc,
                                     const void* d_q, void* d_out, void* d_scratch, size_t scratch_bytes,

@@ -102,3 +102,9 @@ def test_attention_rejects_non_positive_or_non_finite_scale(hsk):
         g = hsk.gqa_desc(requests=2, heads=32, kv_heads=8, dh=128, top_k=16, page_tokens=16, scale=sc)
         with pytest.raises(hsk.HskError):
             hsk.attn_scratch_bytes(g)
+
+
+def test_stream_helpers_reject_null(hsk):
+    """hsk_stream_create needs somewhere to put the stream; hsk_stream_destroy needs a stream (no device call)."""
+    assert hsk._lib.hsk_stream_create(None) == hsk.HSK_EINVAL
+    assert hsk._lib.hsk_stream_destroy(None) == hsk.HSK_EINVAL

@@ -313,3 +313,22 @@ def test_fetch_edge_cases():
     got = h.store.pool_rows(0).index_select(0, locs.reshape(-1).long()).cpu().numpy()
     assert np.array_equal(got, h.store.host_rows(0, 0)[sel2.cpu().numpy().reshape(-1)])
     h.close()
+
+
+def test_overlapped_calls_on_dedicated_streams():
+    """hsk_stream_create streams (hardware queues of their own) for the micro-batch streams and the copy stream:
+    two stores' calls interleaved as in the overlapped schedule, each checked against its oracle."""
+    ws = [synth.WORKLOADS["tiny"].scaled(requests=3, top_k=256, hot_slots=512, heads=64, seed=7900 + i)
+          for i in range(2)]
+    hs = [Harness(w, steps=3, deferred=True) for w in ws]
+    *streams, copy = hsk.dedicated_streams(len(hs) + 1)
+    for h in hs:
+        h.copy_stream = copy
+    for t in range(3):
+        for h, s in zip(hs, streams):
+            with torch.cuda.stream(s):
+                res = h.resolve(0, t, overlap=True)
+                h.check_bytes(res)
+                h.check_attention(0, t, res, res["out"])
+    for h in hs:
+        h.close()
