@@ -1102,7 +1102,9 @@ def main() -> int:
         fn = {"verify": run_verify, "adaptive": run_adaptive, "quest": run_quest, "decode": run_decode,
               "loadstep": run_loadstep}[args.workload]
         steps = args.steps if args.steps != 32 else w.steps
-        print(json.dumps(fn(hsk, synth, w, steps)), flush=True)
+        r = fn(hsk, synth, w, steps)
+        hsk.release_dedicated_streams()
+        print(json.dumps(r), flush=True)
         return 0
     assert w.kind == "mla" and w.queries == 1, "the benchmark line is the single-query MLA decode"
     K, W = args.steps, args.warmup
@@ -1247,6 +1249,8 @@ def main() -> int:
         result["no_io_bound"] = no_io_bound(hsk, synth, w, sels, d_q, ad, scratch, nscratch,
                                             steps=min(total_steps, 12))
         result["host_link_ceiling"] = memcpy_ceiling()
+    # the overlapped schedule's streams: nothing was allocated on them, so they can go before the process ends
+    hsk.release_dedicated_streams()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on a bounded sample)")
         result["cpu_baseline"] = cpu_baseline(w, sels[0], q_host[0][min(3, total_steps) - 1],

@@ -313,6 +313,17 @@ def dedicated_streams(n: int) -> list:
     return pool[:n]
 
 
+def release_dedicated_streams() -> None:
+    """Destroy the streams dedicated_streams made on the current device, after waiting for them.  Only for callers
+    that never allocated a tensor while one of them was the current stream (the caching allocator would keep
+    referring to it)."""
+    import torch
+    pool = _DEDICATED.pop(torch.cuda.current_device(), [])
+    for s in pool:
+        s.synchronize()
+        _check(_lib.hsk_stream_destroy(ctypes.c_void_p(s.cuda_stream)), "hsk_stream_destroy")
+
+
 def fetch_plan(store: int, source: int, stream=None) -> None:
     _check(_lib.hsk_fetch_plan(store, source, _stream(stream)), "hsk_fetch_plan")
 
