@@ -628,12 +628,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   // S of tile T for this wave's 32 heads.  The K reads are issued from inline assembly two chunks ahead of
   // their products, with the waits written out (LDS reads of one wave complete in order), from four base
   // registers per tile and immediate offsets.
+  // The score products are written in assembly too, in the form that accumulates in ordinary VGPRs: the 256
+  // output accumulators fill the accumulation registers, and a builtin product would put S there as well
+  // (272 of 256), so that the compiler moved one output block and S between the two files on every tile.
+  // Their hazards, which the compiler does not see in assembly: a chain's products accumulate into the same
+  // registers (no wait states needed); the first takes 0 for the accumulator; the last is followed by 20 wait
+  // states before anything may read S; the operands come from LDS reads (waited for) and from the query
+  // block loaded before the loop, never from a VALU write just before a product.
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   auto scores = [&](const HSK_LDS char* tile, auto&& side) {
     const uint32_t t0 = (uint32_t)(uintptr_t)tile;
     const uint32_t kb0 = t0 + kb[0], kb1 = t0 + kb[1], kb2 = t0 + kb[2], kb3 = t0 + kb[3];
     u32x4v kf[3];
-    f32x16 sc = f32x16{};
+    f32x16 sc, out;
 #define HSK_K_READ(C)                                                                                       \
   {                                                                                                        \
     const uint32_t b_ = ((C)&3) == 0 ? kb0 : ((C)&3) == 1 ? kb1 : ((C)&3) == 2 ? kb2 : kb3;               \
@@ -641,8 +648,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   }
 #define HSK_K_STEP(C, WAIT)                                                                                 \
   {                                                                                                        \
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kf[(C) % 3]) : "i"(WAIT));                                \
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[(C) % 3]), qf[C], sc, 0, 0, 0); \
+    if ((C) == 0)                                                                                          \
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"                       \
+                   : "=&v"(sc) : "v"(kf[0]), "v"(qf[0]), "i"(WAIT));                                       \
+    else if ((C) < KC - 1)                                                                                 \
+      asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"                      \
+                   : "+v"(sc) : "v"(kf[(C) % 3]), "v"(qf[C]), "i"(WAIT));                                  \
+    else                                                                                                   \
+      asm volatile("s_waitcnt lgkmcnt(%4)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 7\n\ts_nop 7\n\ts_nop 3" \
+                   : "=&v"(out) : "v"(kf[(C) % 3]), "v"(qf[C]), "v"(sc), "i"(WAIT));                       \
   }
     HSK_K_READ(0) HSK_K_READ(1)
     HSK_K_READ(2) HSK_K_STEP(0, 2) side(0);
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #undef HSK_K_READ
 #undef HSK_K_STEP
     static_assert(KC == 36, "the unrolled score sequence covers 36 chunks");
-    return sc;
+    return out;
   };
   // maximum over the valid rows of a tile, in log2 units, the same in lanes l and l ^ 32 (rows past the
   // partition's end are set to -inf without a branch)
