@@ -24,6 +24,9 @@ constexpr int kGatherThreads = 256;
 // them fill the host link while leaving the other compute units free.
 constexpr int kFetchThreads = 1024;
 constexpr int64_t kAlign = 256;
+// A copy kernel that waits inside for a plan published by a resolve on another stream gives up after this many
+// polls of a request's ready word (each a device-scope load and a short sleep: seconds in all).
+constexpr uint32_t kPlanSpinLimit = 1u << 22;
 
 // Device pointers of one source's metadata (all inside the caller's workspace).
 struct SourceMeta {
@@ -35,12 +38,13 @@ struct SourceMeta {
   int32_t* plan_n;    // [R] distinct missing rows of the last resolve call
   int32_t* plan_pos;  // [R][plan_cap] their positions, in miss order
   int32_t* plan_dst;  // [R][plan_cap] the pool row each was copied to
+  uint32_t* ready;    // [R] epoch of the last resolve that published its plan here (0: none)
 };
 
 // Byte offsets of every region of the workspace.
 struct WorkspaceLayout {
   int64_t ctx, wt_pos, err, fill, total;   // ctx [S][R] i64, wt_pos [S][2][R] i32
-  std::vector<int64_t> key, rec, order, pt, opt, plan_n, plan_pos, plan_dst;
+  std::vector<int64_t> key, rec, order, pt, opt, plan_n, plan_pos, plan_dst, ready;
 };
 
 bool layout_workspace(const hsk_desc& d, WorkspaceLayout* out);
@@ -64,6 +68,7 @@ struct ResolveArgs {
   const char* host;    // nullable: host rows of (host source, request 0); set, the kernel copies the misses
   char* pool;          // row 0 of the source's pool (the copies' destination)
   int64_t host_req_stride;  // bytes between requests in the host rows
+  uint32_t* ready;     // nullable: each workgroup stores epoch in ready[r] once its request's plan is visible
   int32_t plan_cap;
   int32_t R, B, T, P, S, Qmax, k, row_bytes;
   uint32_t epoch;
@@ -76,6 +81,9 @@ struct GatherArgs {
   const int32_t* plan_pos;
   const int32_t* plan_dst;
   int64_t host_req_stride; // bytes between requests in the host rows
+  const uint32_t* ready;   // nullable: wait in the kernel until ready[r] == epoch before reading request r's plan
+  int32_t* err;            // with ready: the store's error word (HSK_ESTATE when a plan never appears)
+  uint32_t epoch;
   int32_t plan_cap;
   int32_t row_bytes;
 };
@@ -135,8 +143,7 @@ struct hsk_store {
   std::vector<hipEvent_t> wt_done;          // [S][2] write-through of the last two appends per source
   std::vector<uint8_t> wt_pending;          // [S][2] event recorded and not yet waited for
   std::vector<hipEvent_t> tail_done;        // [S] tail writes of the last append
-  std::vector<hipEvent_t> planned;          // [S] resolve (plan only) of hsk_resolve_fetch_attend done
-  std::vector<hipEvent_t> fetched;          // [S] its fetch done on the copy stream
+  std::vector<hipEvent_t> fetched;          // [S] the fetch of hsk_resolve_fetch_attend done on the copy stream
   std::vector<int32_t> append_parity;       // [S]
   int32_t* d_err = nullptr;
   int32_t* d_fill = nullptr;                // [R][Qmax][k] per-selection host source of a fused call

@@ -193,6 +193,20 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     if (q < B) s_order[q] = ov_[j];
   }
   int32_t* fill = a.fill ? a.fill + (int64_t)r * total : nullptr;
+  // With a ready array (a copy kernel on another stream waits for this request's plan inside the kernel),
+  // every exit publishes the plan: every wave waits until its stores are acknowledged by the L2, then, after
+  // the barrier, one device-scope release (a single L2 write-back for the workgroup: one per wave made the
+  // resolve four times slower beside a running attention) and the store of the call's epoch.  Every caller
+  // below is reached by the whole workgroup.
+  auto publish = [&]() {
+    if (!a.ready) return;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(a.ready + r, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
   if (__syncthreads_or(bad)) {
     for (int f = tid; f < total; f += NT) {
       locs[f] = -1;
@@ -207,6 +221,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       }
       atomicCAS(a.err, 0, HSK_ERANGE);
     }
+    publish();
     return;
   }
 
@@ -351,6 +366,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
     if (fill)
       for (int f = tid; f < total; f += NT) fill[f] = -1;
     write_stats(0, nhit0, 0);
+    publish();
     return;
   }
 
@@ -453,6 +469,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       }
       atomicCAS(a.err, 0, HSK_ESTAGE);
     }
+    publish();
     return;
   }
   const int n_keep = free_slots - v;
@@ -600,6 +617,7 @@ __global__ __launch_bounds__(kResolveThreads) void resolve_kernel(ResolveArgs a)
       }
     }
   }
+  publish();
 }
 
 
@@ -835,7 +853,23 @@ __global__ __launch_bounds__(kFetchThreads) void gather_kernel(GatherArgs g, int
   int64_t C = 0;  // rows of the requests before this group of 64
   for (int r0 = 0; r0 < R; r0 += 64) {
     const int r = r0 + lane;
-    const int m = r < R ? g.plan_n[r] : 0;
+    bool ok = true;
+    if (g.ready) {
+      // request r's plan comes from a resolve on another stream: wait (bounded) until it publishes this
+      // call's epoch, then acquire; a plan that never appears is an error and its request copies nothing
+      ok = r >= R;
+      for (uint32_t spin = 0; !ok; ++spin) {
+        ok = __hip_atomic_load(g.ready + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g.epoch;
+        if (ok) break;
+        if (spin >= kPlanSpinLimit) {
+          atomicCAS(g.err, 0, HSK_ESTATE);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    const int m = r < R && ok ? g.plan_n[r] : 0;
     int64_t incl = m;  // inclusive prefix over the lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -999,7 +1033,8 @@ hipError_t launch_init_meta(const SourceMeta& m, int32_t R, int32_t B, int64_t m
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_fill_i32(m.pt, (int64_t)R * max_ctx, -1, s)) != hipSuccess) return e;
   if (m.opt && (e = launch_fill_i32(m.opt, (int64_t)R * max_pages, -1, s)) != hipSuccess) return e;
-  return launch_fill_i32(m.plan_n, R, 0, s);
+  if ((e = launch_fill_i32(m.plan_n, R, 0, s)) != hipSuccess) return e;
+  return launch_fill_i32((int32_t*)m.ready, R, 0, s);  // epochs start at 1: no plan published yet
 }
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {

@@ -4,7 +4,8 @@
 //   workspace: per request context lengths, a sticky error word, the per-selection host sources of a fused
 //              resolve + attend [R][Qmax][k] i32, then per source
 //              key[R][B] i32, rec[R][B] u32, order[R][B] u16, pt[R][max_ctx] i32, opt[R][max_pages] i32,
-//              plan_n[R] i32, plan_pos[R][Qmax*k] i32, plan_dst[R][Qmax*k] i32 (each region 256-B aligned)
+//              plan_n[R] i32, plan_pos[R][Qmax*k] i32, plan_dst[R][Qmax*k] i32, ready[R] u32 (each region
+//              256-B aligned)
 //   pool:      per source rows_per_source rows of row_bytes: [R*B hot | R*T tail | optional pages | R*S staging]
 // Host (library-owned, pinned and mapped): per host source R x max_ctx rows of row_bytes.
 #include <algorithm>
@@ -68,7 +69,7 @@ bool layout_workspace(const hsk_desc& d, WorkspaceLayout* L) {
   // fill codes of the fused resolve + attend, which serves stores with one query per request
   L->fill = off; off = align_up(off + (d.max_queries == 1 ? 4 * R * cap : 0));
   L->key.clear(); L->rec.clear(); L->order.clear(); L->pt.clear(); L->opt.clear();
-  L->plan_n.clear(); L->plan_pos.clear(); L->plan_dst.clear();
+  L->plan_n.clear(); L->plan_pos.clear(); L->plan_dst.clear(); L->ready.clear();
   for (int32_t s = 0; s < d.num_sources; ++s) {
     L->key.push_back(off); off = align_up(off + 4 * R * B);
     L->rec.push_back(off); off = align_up(off + 4 * R * B);
@@ -78,6 +79,7 @@ bool layout_workspace(const hsk_desc& d, WorkspaceLayout* L) {
     L->plan_n.push_back(off); off = align_up(off + 4 * R);
     L->plan_pos.push_back(off); off = align_up(off + 4 * R * cap);
     L->plan_dst.push_back(off); off = align_up(off + 4 * R * cap);
+    L->ready.push_back(off); off = align_up(off + 4 * R);
   }
   L->total = off;
   return true;
@@ -122,8 +124,6 @@ void hsk_kv_store_destroy(hsk_store* st) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : st->tail_done)
     if (e) (void)hipEventDestroy(e);
-  for (hipEvent_t e : st->planned)
-    if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : st->fetched)
     if (e) (void)hipEventDestroy(e);
   for (char* h : st->host)
@@ -162,11 +162,9 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   st->wt_pending.assign(2 * (size_t)desc->num_sources, 0);
   st->tail_done.assign((size_t)desc->num_sources, nullptr);
   st->append_parity.assign((size_t)desc->num_sources, 0);
-  st->planned.assign((size_t)desc->num_sources, nullptr);
   st->fetched.assign((size_t)desc->num_sources, nullptr);
-  for (auto* v : {&st->planned, &st->fetched})
-    for (hipEvent_t& e : *v)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
+  for (hipEvent_t& e : st->fetched)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
   for (hipEvent_t& e : st->wt_done)
     if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) { e = nullptr; hsk_kv_store_destroy(st); return HSK_EHIP; }
   for (hipEvent_t& e : st->tail_done)
@@ -183,6 +181,7 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
     m.plan_n = (int32_t*)(st->ws + L.plan_n[k]);
     m.plan_pos = (int32_t*)(st->ws + L.plan_pos[k]);
     m.plan_dst = (int32_t*)(st->ws + L.plan_dst[k]);
+    m.ready = (uint32_t*)(st->ws + L.ready[k]);
     st->meta.push_back(m);
   }
   st->last_epoch.assign(desc->num_sources, 0u);
@@ -336,7 +335,7 @@ static ResolveArgs resolve_args(hsk_store* st, int32_t source, uint32_t epoch, c
   a.sel = d_sel; a.nq = d_nq; a.locs = d_locs; a.stats = d_stats;
   a.ctx = st->d_ctx + (size_t)source * st->d.num_requests; a.m = st->meta[source];
   a.err = st->d_err; a.fill = nullptr; a.max_ctx = st->d.max_ctx; a.max_pages = st->max_pages;
-  a.host = nullptr; a.pool = nullptr; a.host_req_stride = 0;
+  a.host = nullptr; a.pool = nullptr; a.host_req_stride = 0; a.ready = nullptr;
   const int64_t R = st->d.num_requests;
   a.opt_base = R * st->d.hot_slots + R * st->d.tail_rows;
   a.stg_base = stg_base_of(st->d, source);
@@ -396,7 +395,10 @@ hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, con
                           st->d.max_ctx * (int64_t)st->d.row_bytes, d_out, d_scratch, scratch_bytes, s);
 }
 
-static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s) {
+// ready: wait inside the copy kernel for each request's plan of resolve `epoch` (published by a resolve on
+// another stream); null: the plan is complete when the kernel starts (stream order)
+static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s,
+                              const uint32_t* ready = nullptr, uint32_t epoch = 0) {
   void* pool;
   hsk_pool_base(st, dst_source, &pool);
   GatherArgs g;
@@ -406,6 +408,7 @@ static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_so
   g.plan_dst = st->meta[plan_source].plan_dst;
   g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
   g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
+  g.ready = ready; g.err = st->d_err; g.epoch = epoch;
   HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
   return HSK_OK;
 }
@@ -453,13 +456,14 @@ hsk_status hsk_resolve_fetch_attend(hsk_store* st, int32_t source, uint32_t epoc
   if (epoch <= st->last_epoch[source] || epoch > 0x7fffffffu) return HSK_EEPOCH;
   hipStream_t s = (hipStream_t)stream, c = (hipStream_t)copy_stream;
   ResolveArgs a = resolve_args(st, source, epoch, d_sel, d_nq, d_locs, d_stats);
+  // On two streams the copy does not wait for the resolve through the streams: each resolve workgroup
+  // publishes its request's plan with the call's epoch and the copy kernel waits for it, so consecutive
+  // copies on the copy stream follow each other without a cross-stream wait in between.
+  if (c != s) a.ready = st->meta[source].ready;
   HSK_HIP(launch_resolve(a, s));
   st->last_epoch[source] = epoch;
-  if (c != s) {
-    HSK_HIP(hipEventRecord(st->planned[source], s));
-    HSK_HIP(hipStreamWaitEvent(c, st->planned[source], 0));
-  }
-  const hsk_status f = gather_plan(st, source, source, c);
+  const hsk_status f = c != s ? gather_plan(st, source, source, c, st->meta[source].ready, epoch)
+                              : gather_plan(st, source, source, c);
   if (f != HSK_OK) return f;
   if (c != s) {
     HSK_HIP(hipEventRecord(st->fetched[source], c));

@@ -472,16 +472,22 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
 /*
  * One layer of a deferred store with its host IO overlapped (HiSparse section 3.5: plan, then IO beside other
  * work; Adaptive DHiSparse Eq. 1 attention over the resolved rows).  Queues, in order:
- *   on `stream`       the resolve of hsk_resolve_step (plan only), then an event;
- *   on `copy_stream`  a wait for that event, the fetch of hsk_fetch_plan, then an event;
+ *   on `stream`       the resolve of hsk_resolve_step (plan only); each of its workgroups then publishes its
+ *                     request's plan by storing `epoch` in the store's per-request ready word;
+ *   on `copy_stream`  the fetch of hsk_fetch_plan, whose kernel waits inside, per request, for that word to
+ *                     read `epoch` before it reads the plan, then an event;
  *   on `stream`       a wait for the fetch, then hsk_sparse_decode_attn(desc, d_q, pool of `source`, d_locs, d_nq,
  *                     d_out, d_scratch, scratch_bytes).
  * While the copy stream streams this source's missing rows over the host link, the caller's other streams (other
  * micro-batches, other work) run; the attention starts when its rows are in.  Calls for different stores or
- * sources sharing one copy stream are fetched in call order, one at a time.  copy_stream may equal stream (no
- * events then).  The events belong to the store, one pair per source.  The source's next call comes after
- * this one's fetch when it is queued on the same `stream` (its attention waits for the fetch); on another
- * stream the caller orders it after this call's attention.
+ * sources sharing one copy stream are fetched in call order, one at a time, with no cross-stream wait between
+ * consecutive fetches (such a wait costs several microseconds of idle link each).  A fetch that sees no plan
+ * for a request within seconds copies nothing for it and records HSK_ESTATE in the store's error word
+ * (hsk_sync_status); it cannot happen through these calls alone, since every call queues its resolve before its
+ * fetch and fetches run in call order.  copy_stream may equal stream (plain stream order then, no waits).  The
+ * event belongs to the store, one per source.  The source's next call comes after this one's fetch when it is
+ * queued on the same `stream` (its attention waits for the fetch); on another stream the caller orders it after
+ * this call's attention.
  *   d_sel, d_nq, d_locs, d_stats, epoch: as hsk_resolve_step.
  *   desc: any attention descriptor whose resolution units (num_requests; num_requests x kv_heads for
  *         HSK_ATTN_GQA), max_queries and top_k equal the store's requests, max_queries and top_k, and with

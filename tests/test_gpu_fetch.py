@@ -160,6 +160,29 @@ def test_resolve_fetch_attend(case, same_stream):
     h.close()
 
 
+def test_resolve_fetch_attend_copy_waits_for_a_late_resolve():
+    """With the copy on its own stream, the copy kernel is not ordered after the resolve by the streams: it waits
+    inside for each request's published plan.  Here ~10 ms of matrix products run on the stream before every
+    call, so the copy stream (idle) starts the copy kernel long before the resolve runs: the pool must still get
+    exactly the plan's rows (at the first step a copy that did not wait would read the initial empty plan), and
+    no copy may give up waiting (error word clear)."""
+    w = synth.WORKLOADS["tiny"].scaled(requests=3, ctx=30_000, top_k=2048, hot_slots=4096, heads=128, keep_frac=0.6,
+                                       seed=7450)
+    h = Harness(w, steps=3, deferred=True)
+    a = torch.randn(4096, 4096, device="cuda")
+    for t in range(h.steps):
+        torch.cuda.synchronize()
+        for _ in range(6):
+            a = a @ a
+            a = a / a.norm()
+        res = h.resolve(0, t, overlap=True)
+        h.check_bytes(res, source=0)
+        err = h.check_attention(0, t, res, res["out"], samples=[(r, 0) for r in range(w.requests)], source=0)
+        log(f"[late resolve] step {t}: misses={int(res['stats']['n_miss'].sum())} attn err {err[0]:.2e}")
+    assert h.store.sync_status() == 0
+    h.close()
+
+
 def test_resolve_fetch_attend_rejects_and_changes_nothing():
     """A zero-copy store, a descriptor for another batch, k or row width, and too little scratch are rejected
     before anything is queued: the same epoch then works."""
