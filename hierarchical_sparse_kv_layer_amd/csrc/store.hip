@@ -260,8 +260,8 @@ hsk_status hsk_residency_set(hsk_store* st, int32_t source, int32_t req, const i
                              int64_t n_pages, hsk_stream_t stream) {
   if (!st || source < 0 || source >= st->d.num_sources || req < 0 || req >= st->d.num_requests) return HSK_EINVAL;
   if (st->d.page_rows == 0 || st->res) return HSK_ESTATE;  // scheduled residency owns the maps
-  // optional residency covers complete pages of the imported history only (Adaptive DHiSparse section 3.1:
-  // rows generated during decoding stay under the tail and hot-cache rules)
+  // only whole pages of the history imported at admission may be held optionally (Adaptive DHiSparse
+  // section 3.1); rows produced while decoding are handled by the tail and the hot cache instead
   const int64_t complete = st->n_import[req] / st->d.page_rows;
   if (n_pages < 0 || n_pages > complete || (n_pages > 0 && !h_page_ids)) return HSK_EINVAL;
   for (int64_t g = 0; g < n_pages; ++g)

@@ -140,8 +140,9 @@ int32_t ora_admit(ora_source* s, int32_t r, int64_t n_rows, int64_t uid) {
   return ORA_OK;
 }
 
-/* [AD] 3.1: optional residency covers complete pages of imported history; population copies the page
- * and publishes its ready location afterwards, reclaim drops the location (-1). */
+/* [AD] 3.1: only whole pages of the history a request brought at admission can be held optionally;
+ * populating a page copies it first and then makes its location visible, reclaiming it sets the location
+ * back to -1. */
 int32_t ora_residency_set(ora_source* s, int32_t r, const int32_t* page_ids, int64_t n_pages) {
   if (r < 0 || r >= s->R || s->P == 0) return ORA_EINVAL;
   int64_t complete = s->n_import[r] / s->P;
