@@ -599,8 +599,9 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
     """The benchmark step with the host IO hidden under the other work (HiSparse section 3.5, overlap of IO
     with computation): the batch is served as M micro-batches of R/M requests, each with its own store (in
     HSK_GATHER_DEFERRED mode) and stream, and one copy stream runs every fetch in turn.  Per layer and
-    micro-batch, one hsk_resolve_fetch_attend call: resolve (plan only) on the micro-batch's stream -> event
-    -> fetch on the copy stream -> event -> attention on the micro-batch's stream.  The copies are serialised on the link in issue
+    micro-batch, one hsk_resolve_fetch_attend call: resolve (plan only, each request's plan published with the
+    call's epoch) on the micro-batch's stream; fetch on the copy stream, its kernel waiting for the published
+    plans; event; attention on the micro-batch's stream.  The copies are serialised on the link in issue
     order (micro-batch 0's layer l, then micro-batch 1's, ...), and while the copy stream fetches one
     micro-batch's rows the others resolve and attend; every request still runs its layers in order, each
     layer's attention after its own resolve and fetch.  The fetch kernel's few workgroups leave the other
@@ -609,7 +610,7 @@ def run_overlapped(hsk, synth, w, sels, q_host, K: int, W: int, M: int, fetch_bl
 
     The M + 1 streams each have a hardware queue of their own (hsk_stream_create): HIP serves ordinary streams
     from a few hardware queues (4 here) handed out in turn, and two of the step's streams on one queue run as one
-    FIFO (a fetch then waits behind an attention; the step slows from 1.71 to ~2.0 ms)."""
+    FIFO (a fetch then waits behind an attention; the step slows from ~1.7 to ~2.0 ms)."""
     import torch
     R, k = w.requests, w.top_k
     assert R % M == 0
