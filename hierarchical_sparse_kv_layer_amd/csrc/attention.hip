@@ -805,19 +805,64 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     bf16x8 pf[2];
     for (int T = 0; T + 1 < ntiles; ++T) {
       wait_tile_barrier32(MY * min(ntiles - 2 - T, 1));
-      if (T + kBufs32 - 1 < ntiles) issue(T + kBufs32 - 1, (T + kBufs32 - 1) % kBufs32);
+      // Tile T + 3 is loaded during S(T + 1), one of this wave's MY loads every kDmaStride products, so that
+      // the CU's vector memory path moves the tile while the matrix cores work (issued together before the
+      // products, the loads held each wave ~600 cycles per tile).  The LDS read of the lane's source row
+      // location(s) is issued first, from inline assembly: the K reads' explicit waits (in-order LDS
+      // completion) cover it before its first use at the first load.
+      constexpr int kDmaStride = 36 / MY;
+      const bool load_next = T + kBufs32 - 1 < ntiles;
+      const uint32_t lnext = lds_tile0 + ((T + kBufs32 - 1) % kBufs32) * kTileBytes + wave * 1024;
+      int32_t lv[NTOK];
+      const char* rp[NTOK];
+      if (load_next) {
+        const int tb = (T + kBufs32 - 1) * kTile;
+#pragma unroll
+        for (int v = 0; v < NTOK; ++v) {
+          const int tok = 8 * ((wave + NW * v) & 3) + (lane >> 3);
+          const int x = tb + tok < nrows ? tb + tok : 0;   // rows past the end re-read row 0 (masked)
+          asm volatile("ds_read_b32 %0, %1" : "=v"(lv[v]) : "v"((uint32_t)(uintptr_t)(const HSK_LDS int32_t*)&s_loc[x]) : "memory");
+        }
+      }
+      auto dma_step = [&](int step) {
+        if (!load_next || step % kDmaStride != 1 || step / kDmaStride >= MY) return;
+        const int u = step / kDmaStride;
+        if (u == 0) {
+          // the location reads went out before the K reads, and after the product just issued at most the two
+          // newest K reads are outstanding, so they are complete: this wait (already met) ties their first use
+          // here, where the compiler could otherwise move it ahead of the waits it does not see
+          if constexpr (NTOK == 1)
+            asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(lv[0]));
+          else
+            asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(lv[0]), "+v"(lv[NTOK - 1]));
+#pragma unroll
+          for (int v = 0; v < NTOK; ++v) {
+            const int tok = 8 * ((wave + NW * v) & 3) + (lane >> 3);
+            rp[v] = a.pool + ((int64_t)lv[v] * a.row_bytes + (((lane & 7) ^ tile_swz32(tok)) << 4));
+          }
+        }
+        const uint32_t m0 = lnext + NW * u * 1024;
+        const char* src = NW >= 4 ? rp[0] + u * 128 : rp[u % NTOK] + (u >> 1) * 128;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+      };
       // the softmax of tile T in six pieces between the products of S(T + 1): masks and maxima, the
       // cross-lane maximum and reference, then the exponentials four at a time and the bf16 packing
       const int rem = nrows - T * kTile;
       float tmx = -INFINITY, mneg = 0.f, psum = 0.f, pw[16];
       auto side = [&](int step) {
+        dma_step(step);
         if ((step & 3) != 3 || step > 23) return;
         const int piece = step >> 2;
         if (piece <= 1) {
+          if (rem >= kTile) {   // wave-uniform: only a partition's last tile can hold rows past its end
 #pragma unroll
-          for (int v = 8 * piece; v < 8 * piece + 8; ++v) {
-            sc[v] = 8 * (v >> 2) + 4 * h + (v & 3) < rem ? sc[v] : -INFINITY;
-            tmx = fmaxf(tmx, sc[v]);
+            for (int v = 8 * piece; v < 8 * piece + 8; ++v) tmx = fmaxf(tmx, sc[v]);
+          } else {
+#pragma unroll
+            for (int v = 8 * piece; v < 8 * piece + 8; ++v) {
+              sc[v] = 8 * (v >> 2) + 4 * h + (v & 3) < rem ? sc[v] : -INFINITY;
+              tmx = fmaxf(tmx, sc[v]);
+            }
           }
           if (piece == 1) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmx), __float_as_uint(tmx), false, false);
