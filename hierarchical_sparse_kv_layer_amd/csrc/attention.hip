@@ -14,6 +14,8 @@
 // bf16 (round to nearest even).
 #include <cmath>
 #include <mutex>
+#include <type_traits>
+#include <utility>
 
 #include "hsk_internal.h"
 
@@ -144,6 +146,12 @@ __device__ __forceinline__ void wait_tile_barrier_n(int n) {
     case 18: wait_tile_barrier<18>(); break;
     default: wait_tile_barrier<0>(); break;
   }
+}
+
+// f(integral_constant<int, U>) for every U of the sequence, in order (compile-time indices for instruction fields)
+template <typename F, int... U>
+__device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
 }
 
 // the 32-head kernels' waits: this wave's loads of 0 to 3 tiles (9 or 18 each) still in flight
@@ -603,12 +611,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
       const int x = tb + tok < nrows ? tb + tok : 0;   // rows past the end re-read row 0 (masked)
       rp[v] = a.pool + ((int64_t)s_loc[x] * a.row_bytes + sw);
     }
-#pragma unroll
-    for (int u = 0; u < MY; ++u) {
-      const uint32_t m0 = lbase + NW * u * 1024;
-      const char* src = NW >= 4 ? rp[0] + u * 128 : rp[u % NTOK] + (u >> 1) * 128;
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
-    }
+    const char* const r0 = rp[0];
+    const char* const r1 = rp[NTOK - 1];
+    auto one = [lbase, r0, r1](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      constexpr int off = (NW >= 4 ? u : u >> 1) * 128;
+      // the instruction offset moves the LDS destination as well as the global address: M0 takes it back
+      const uint32_t m0 = lbase + NW * u * 1024 - off;
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
+                   ::"s"(m0), "v"(NW >= 4 || u % 2 == 0 ? r0 : r1), "i"(off) : "memory", "m0");
+    };
+    for_each_const(one, std::make_integer_sequence<int, MY>{});
   };
   {
     const uint16_t* qb = a.q + ((int64_t)rq * a.H + hbase + j) * kMlaDk + 8 * h;
@@ -659,42 +672,42 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                    : "=&v"(out) : "v"(kf[(C) % 3]), "v"(qf[C]), "v"(sc), "i"(WAIT));                       \
   }
     HSK_K_READ(0) HSK_K_READ(1)
-    HSK_K_READ(2) HSK_K_STEP(0, 2) side(0);
-    HSK_K_READ(3) HSK_K_STEP(1, 2) side(1);
-    HSK_K_READ(4) HSK_K_STEP(2, 2) side(2);
-    HSK_K_READ(5) HSK_K_STEP(3, 2) side(3);
-    HSK_K_READ(6) HSK_K_STEP(4, 2) side(4);
-    HSK_K_READ(7) HSK_K_STEP(5, 2) side(5);
-    HSK_K_READ(8) HSK_K_STEP(6, 2) side(6);
-    HSK_K_READ(9) HSK_K_STEP(7, 2) side(7);
-    HSK_K_READ(10) HSK_K_STEP(8, 2) side(8);
-    HSK_K_READ(11) HSK_K_STEP(9, 2) side(9);
-    HSK_K_READ(12) HSK_K_STEP(10, 2) side(10);
-    HSK_K_READ(13) HSK_K_STEP(11, 2) side(11);
-    HSK_K_READ(14) HSK_K_STEP(12, 2) side(12);
-    HSK_K_READ(15) HSK_K_STEP(13, 2) side(13);
-    HSK_K_READ(16) HSK_K_STEP(14, 2) side(14);
-    HSK_K_READ(17) HSK_K_STEP(15, 2) side(15);
-    HSK_K_READ(18) HSK_K_STEP(16, 2) side(16);
-    HSK_K_READ(19) HSK_K_STEP(17, 2) side(17);
-    HSK_K_READ(20) HSK_K_STEP(18, 2) side(18);
-    HSK_K_READ(21) HSK_K_STEP(19, 2) side(19);
-    HSK_K_READ(22) HSK_K_STEP(20, 2) side(20);
-    HSK_K_READ(23) HSK_K_STEP(21, 2) side(21);
-    HSK_K_READ(24) HSK_K_STEP(22, 2) side(22);
-    HSK_K_READ(25) HSK_K_STEP(23, 2) side(23);
-    HSK_K_READ(26) HSK_K_STEP(24, 2) side(24);
-    HSK_K_READ(27) HSK_K_STEP(25, 2) side(25);
-    HSK_K_READ(28) HSK_K_STEP(26, 2) side(26);
-    HSK_K_READ(29) HSK_K_STEP(27, 2) side(27);
-    HSK_K_READ(30) HSK_K_STEP(28, 2) side(28);
-    HSK_K_READ(31) HSK_K_STEP(29, 2) side(29);
-    HSK_K_READ(32) HSK_K_STEP(30, 2) side(30);
-    HSK_K_READ(33) HSK_K_STEP(31, 2) side(31);
-    HSK_K_READ(34) HSK_K_STEP(32, 2) side(32);
-    HSK_K_READ(35) HSK_K_STEP(33, 2) side(33);
-    HSK_K_STEP(34, 1) side(34);
-    HSK_K_STEP(35, 0) side(35);
+    HSK_K_READ(2) HSK_K_STEP(0, 2) side(std::integral_constant<int, 0>{});
+    HSK_K_READ(3) HSK_K_STEP(1, 2) side(std::integral_constant<int, 1>{});
+    HSK_K_READ(4) HSK_K_STEP(2, 2) side(std::integral_constant<int, 2>{});
+    HSK_K_READ(5) HSK_K_STEP(3, 2) side(std::integral_constant<int, 3>{});
+    HSK_K_READ(6) HSK_K_STEP(4, 2) side(std::integral_constant<int, 4>{});
+    HSK_K_READ(7) HSK_K_STEP(5, 2) side(std::integral_constant<int, 5>{});
+    HSK_K_READ(8) HSK_K_STEP(6, 2) side(std::integral_constant<int, 6>{});
+    HSK_K_READ(9) HSK_K_STEP(7, 2) side(std::integral_constant<int, 7>{});
+    HSK_K_READ(10) HSK_K_STEP(8, 2) side(std::integral_constant<int, 8>{});
+    HSK_K_READ(11) HSK_K_STEP(9, 2) side(std::integral_constant<int, 9>{});
+    HSK_K_READ(12) HSK_K_STEP(10, 2) side(std::integral_constant<int, 10>{});
+    HSK_K_READ(13) HSK_K_STEP(11, 2) side(std::integral_constant<int, 11>{});
+    HSK_K_READ(14) HSK_K_STEP(12, 2) side(std::integral_constant<int, 12>{});
+    HSK_K_READ(15) HSK_K_STEP(13, 2) side(std::integral_constant<int, 13>{});
+    HSK_K_READ(16) HSK_K_STEP(14, 2) side(std::integral_constant<int, 14>{});
+    HSK_K_READ(17) HSK_K_STEP(15, 2) side(std::integral_constant<int, 15>{});
+    HSK_K_READ(18) HSK_K_STEP(16, 2) side(std::integral_constant<int, 16>{});
+    HSK_K_READ(19) HSK_K_STEP(17, 2) side(std::integral_constant<int, 17>{});
+    HSK_K_READ(20) HSK_K_STEP(18, 2) side(std::integral_constant<int, 18>{});
+    HSK_K_READ(21) HSK_K_STEP(19, 2) side(std::integral_constant<int, 19>{});
+    HSK_K_READ(22) HSK_K_STEP(20, 2) side(std::integral_constant<int, 20>{});
+    HSK_K_READ(23) HSK_K_STEP(21, 2) side(std::integral_constant<int, 21>{});
+    HSK_K_READ(24) HSK_K_STEP(22, 2) side(std::integral_constant<int, 22>{});
+    HSK_K_READ(25) HSK_K_STEP(23, 2) side(std::integral_constant<int, 23>{});
+    HSK_K_READ(26) HSK_K_STEP(24, 2) side(std::integral_constant<int, 24>{});
+    HSK_K_READ(27) HSK_K_STEP(25, 2) side(std::integral_constant<int, 25>{});
+    HSK_K_READ(28) HSK_K_STEP(26, 2) side(std::integral_constant<int, 26>{});
+    HSK_K_READ(29) HSK_K_STEP(27, 2) side(std::integral_constant<int, 27>{});
+    HSK_K_READ(30) HSK_K_STEP(28, 2) side(std::integral_constant<int, 28>{});
+    HSK_K_READ(31) HSK_K_STEP(29, 2) side(std::integral_constant<int, 29>{});
+    HSK_K_READ(32) HSK_K_STEP(30, 2) side(std::integral_constant<int, 30>{});
+    HSK_K_READ(33) HSK_K_STEP(31, 2) side(std::integral_constant<int, 31>{});
+    HSK_K_READ(34) HSK_K_STEP(32, 2) side(std::integral_constant<int, 32>{});
+    HSK_K_READ(35) HSK_K_STEP(33, 2) side(std::integral_constant<int, 33>{});
+    HSK_K_STEP(34, 1) side(std::integral_constant<int, 34>{});
+    HSK_K_STEP(35, 0) side(std::integral_constant<int, 35>{});
 #undef HSK_K_READ
 #undef HSK_K_STEP
     static_assert(KC == 36, "the unrolled score sequence covers 36 chunks");
@@ -791,7 +804,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
   // straight-line block, the softmax and P.V of tile T, so the matrix cores are fed while the softmax of
   // the previous tile runs.  Tile T + 3 is loaded into the buffer of tile T - 1, which every wave has
   // finished with at the barrier that also makes tile T + 1 visible.
-  auto no_side = [](int) {};
+  auto no_side = [](auto) {};
   auto full_pass = [&](bool set_ref, bool issued) {
     if (!issued) {
 #pragma unroll
@@ -824,10 +837,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
           asm volatile("ds_read_b32 %0, %1" : "=v"(lv[v]) : "v"((uint32_t)(uintptr_t)(const HSK_LDS int32_t*)&s_loc[x]) : "memory");
         }
       }
-      auto dma_step = [&](int step) {
-        if (!load_next || step % kDmaStride != 1 || step / kDmaStride >= MY) return;
-        const int u = step / kDmaStride;
-        if (u == 0) {
+      auto dma_step = [&](auto step_c) {
+        constexpr int step = decltype(step_c)::value;
+        if constexpr (step % kDmaStride == 1 && step / kDmaStride < MY) {
+        if (!load_next) return;
+        constexpr int u = step / kDmaStride;
+        if constexpr (u == 0) {
           // the location reads went out before the K reads, and after the product just issued at most the two
           // newest K reads are outstanding, so they are complete: this wait (already met) ties their first use
           // here, where the compiler could otherwise move it ahead of the waits it does not see
@@ -841,16 +856,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             rp[v] = a.pool + ((int64_t)lv[v] * a.row_bytes + (((lane & 7) ^ tile_swz32(tok)) << 4));
           }
         }
-        const uint32_t m0 = lnext + NW * u * 1024;
-        const char* src = NW >= 4 ? rp[0] + u * 128 : rp[u % NTOK] + (u >> 1) * 128;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory", "m0");
+        // the load's chunk group goes into the instruction's offset field (no address arithmetic per load);
+        // that offset also moves the LDS destination, which M0 takes back
+        constexpr int off = (NW >= 4 ? u : u >> 1) * 128;
+        const uint32_t m0 = lnext + NW * u * 1024 - off;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
+                     ::"s"(m0), "v"(rp[NW >= 4 ? 0 : u % NTOK]), "i"(off) : "memory", "m0");
+        }
       };
       // the softmax of tile T in six pieces between the products of S(T + 1): masks and maxima, the
       // cross-lane maximum and reference, then the exponentials four at a time and the bf16 packing
       const int rem = nrows - T * kTile;
       float tmx = -INFINITY, mneg = 0.f, psum = 0.f, pw[16];
-      auto side = [&](int step) {
-        dma_step(step);
+      auto side = [&](auto step_c) {
+        constexpr int step = decltype(step_c)::value;
+        dma_step(step_c);
         if ((step & 3) != 3 || step > 23) return;
         const int piece = step >> 2;
         if (piece <= 1) {
