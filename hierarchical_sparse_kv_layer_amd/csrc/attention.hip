@@ -1211,13 +1211,18 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xc
   if (S <= 4) {
     float mu[4], lu[4];
     u32x4 v[4];
+    // the rows are loaded whatever the sums (every address is inside the partial buffers) and dropped after:
+    // loaded only for a positive sum, each row load waited for its sum, two round trips instead of one
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t ps = p0 + (int64_t)(u < S ? u : 0) * a.H;
       mu[u] = u < S ? a.pm[ps] : -INFINITY;
       lu[u] = u < S ? a.pl[ps] : 0.f;
-      v[u] = (u < S && mine && lu[u] > 0.f) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = mine ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (!(u < S && lu[u] > 0.f)) v[u] = u32x4{0u, 0u, 0u, 0u};
     const float M = fmaxf(fmaxf(mu[0], mu[1]), fmaxf(mu[2], mu[3]));
     float w[4], L = 0.f;
 #pragma unroll
@@ -1274,8 +1279,11 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, int dv, int xc
       const float m = sidx < S ? a.pm[ps] : -INFINITY;
       const float lp = sidx < S ? a.pl[ps] : 0.f;
       w[u] = (m == -INFINITY || !(lp > 0.f)) ? 0.f : __expf(m - M) * lp * invL;
-      v[u] = (w[u] != 0.f && mine) ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+      v[u] = mine ? *(const u32x4*)(a.po + ps * dv + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (w[u] == 0.f) v[u] = u32x4{0u, 0u, 0u, 0u};   // loaded whatever the weight, dropped here
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
