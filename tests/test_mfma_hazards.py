@@ -7,8 +7,9 @@ template instances:
   - after a product that writes VGPRs, nothing reads or writes those registers for 20 wait states, except
     the next product of the same chain, which takes them whole as its accumulator (forwarded in hardware);
   - before a product, no VALU instruction writes one of its operands within 2 wait states.
-The check walks the listing in text order (fall-through), which is how the unrolled chain and the 20 wait
-states after its last product are laid out.  A planted listing shows the check catches both kinds.
+The check follows the listing's control flow (fall-through and branch targets), forward from every product
+and backward into it.  Planted listings show that it catches both kinds, on a taken branch too, and that it
+does not follow an unconditional branch's fall-through.
 """
 import os
 import re
@@ -34,10 +35,15 @@ def _regs(op):
 
 
 def _parse(lines):
+    """Instructions as (op, text, args); a label is ("LABEL", name, [])."""
     ins = []
     for ln in lines:
         t = ln.split(";")[0].strip()
-        if not t or t.startswith(".") or t.endswith(":"):
+        if not t or t.startswith("."):
+            if t.startswith(".LBB") and t.endswith(":"):
+                ins.append(("LABEL", t[:-1], []))
+            continue
+        if t.endswith(":"):
             continue
         parts = t.split(None, 1)
         args = [a.strip() for a in parts[1].split(",")] if len(parts) > 1 else []
@@ -46,37 +52,70 @@ def _parse(lines):
 
 
 def _wait_states(op, args):
+    if op == "LABEL":
+        return 0
     return int(args[0], 0) + 1 if op == "s_nop" else 1
 
 
+def _cfg(ins):
+    """Successors of every instruction: fall-through, branch targets (both for a conditional branch)."""
+    label = {t: i for i, (op, t, _) in enumerate(ins) if op == "LABEL"}
+    succ = []
+    for i, (op, t, args) in enumerate(ins):
+        nxt = [i + 1] if i + 1 < len(ins) else []
+        if op == "s_branch":
+            succ.append([label[args[0]]] if args[0] in label else [])
+        elif op.startswith("s_cbranch"):
+            succ.append(nxt + ([label[args[0]]] if args and args[0] in label else []))
+        elif op == "s_endpgm":
+            succ.append([])
+        else:
+            succ.append(nxt)
+    pred = [[] for _ in ins]
+    for i, ss in enumerate(succ):
+        for j in ss:
+            pred[j].append(i)
+    return succ, pred
+
+
 def hazards(ins):
-    """(kind, product, offending instruction) for every violation in a parsed listing."""
+    """(kind, product, offending instruction) for every violation on any path of a parsed listing."""
+    succ, pred = _cfg(ins)
     bad = []
     for k, (op, t, args) in enumerate(ins):
         if not op.startswith("v_mfma") or not args[0].startswith("v"):
             continue
         dst = _regs(args[0])
-        ws = 0
-        for op2, t2, a2 in ins[k + 1:]:
-            touched = set().union(*(_regs(a) for a in a2)) if a2 else set()
-            if op2 != "s_nop" and touched & dst:
+        # forward: along every path, nothing touches dst within AFTER wait states, except a chained product
+        # accumulating into exactly dst (which then carries the check on)
+        stack, seen = [(j, 0) for j in succ[k]], set()
+        while stack:
+            i, ws = stack.pop()
+            if (i, ws) in seen or ws >= AFTER:
+                continue
+            seen.add((i, ws))
+            op2, t2, a2 = ins[i]
+            touched = set().union(*(_regs(a) for a in a2)) if (a2 and op2 != "s_nop") else set()
+            if touched & dst:
                 chained = op2.startswith("v_mfma") and len(a2) > 3 and a2[3] == args[0] \
                     and not (_regs(a2[1]) | _regs(a2[2])) & dst
                 if not chained:
                     bad.append(("after", t, t2))
-                break
-            ws += _wait_states(op2, a2)
-            if ws >= AFTER:
-                break
+                continue
+            stack.extend((j, ws + _wait_states(op2, a2)) for j in succ[i])
+        # backward: along every path into the product, no VALU write of an operand within BEFORE wait states
         srcs = set().union(*(_regs(a) for a in args[1:4]))
-        ws = 0
-        for op2, t2, a2 in reversed(ins[:k]):
+        stack, seen = [(j, 0) for j in pred[k]], set()
+        while stack:
+            i, ws = stack.pop()
+            if (i, ws) in seen or ws >= BEFORE:
+                continue
+            seen.add((i, ws))
+            op2, t2, a2 = ins[i]
             if op2.startswith("v_") and not op2.startswith("v_mfma") and a2 and _regs(a2[0]) & srcs:
                 bad.append(("before", t, t2))
-                break
-            ws += _wait_states(op2, a2)
-            if ws >= BEFORE:
-                break
+                continue
+            stack.extend((j, ws + _wait_states(op2, a2)) for j in pred[i])
     return bad
 
 
@@ -84,6 +123,35 @@ def _kernel(lines, name):
     start = next(i for i, l in enumerate(lines) if l.startswith(name + ":"))
     end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
     return _parse(lines[start:end + 1])
+
+
+def test_checker_follows_branches():
+    """A write reached only by a branch is checked on that path; one behind an unconditional branch is not on the
+    fall-through path."""
+    taken = """
+        v_mfma_f32_32x32x16_bf16 v[18:33], v[10:13], v[162:165], 0
+        s_cbranch_vccnz .LBB0_2
+        s_nop 7
+        s_nop 7
+        s_nop 7
+    .LBB0_2:
+        v_mov_b32_e32 v20, 0
+        s_endpgm
+    """.strip().split("\n")
+    assert [b[0] for b in hazards(_parse(taken))] == ["after"]
+    skipped = """
+        v_mfma_f32_32x32x16_bf16 v[18:33], v[10:13], v[162:165], 0
+        s_branch .LBB0_3
+    .LBB0_2:
+        v_mov_b32_e32 v20, 0
+    .LBB0_3:
+        s_nop 7
+        s_nop 7
+        s_nop 7
+        v_mov_b32_e32 v21, 0
+        s_endpgm
+    """.strip().split("\n")
+    assert hazards(_parse(skipped)) == []
 
 
 def test_checker_catches_planted_hazards():
