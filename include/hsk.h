@@ -470,6 +470,17 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
                               void* d_out, void* d_scratch, size_t scratch_bytes, hsk_stream_t stream);
 
 /*
+ * A stream with a hardware queue of its own, for the streams of an overlapped schedule (the copy stream and each
+ * micro-batch's stream of hsk_resolve_fetch_attend).  The HIP runtime serves ordinary streams from a small pool of
+ * hardware queues, handed out in turn as streams are created; two streams on one queue run as one FIFO, so a
+ * fetch queued behind another stream's attention waits for it and the overlap is lost.  A stream created with a
+ * compute-unit mask gets a queue of its own; this one enables every compute unit of the current device, so it
+ * runs like any other stream (default priority).  The caller destroys it with hsk_stream_destroy.
+ * EHIP if the runtime refuses. */
+hsk_status hsk_stream_create(hsk_stream_t* stream);
+hsk_status hsk_stream_destroy(hsk_stream_t stream);
+
+/*
  * One layer of a deferred store with its host IO overlapped (HiSparse section 3.5: plan, then IO beside other
  * work; Adaptive DHiSparse Eq. 1 attention over the resolved rows).  Queues, in order:
  *   on `stream`       the resolve of hsk_resolve_step (plan only); each of its workgroups then publishes its
@@ -497,17 +508,6 @@ hsk_status hsk_resolve_attend(hsk_store* store, int32_t source, uint32_t epoch, 
  * EEPOCH as hsk_resolve_step.  Outputs of a request the resolve rejects (status in its stats) are meaningless:
  * its locations are -1, which the attention reads as row 0.
  */
-/*
- * A stream with a hardware queue of its own, for the streams of an overlapped schedule (the copy stream and each
- * micro-batch's stream of hsk_resolve_fetch_attend).  The HIP runtime serves ordinary streams from a small pool of
- * hardware queues, handed out in turn as streams are created; two streams on one queue run as one FIFO, so a
- * fetch queued behind another stream's attention waits for it and the overlap is lost.  A stream created with a
- * compute-unit mask gets a queue of its own; this one enables every compute unit of the current device, so it
- * runs like any other stream (default priority).  The caller destroys it with hsk_stream_destroy.
- * EHIP if the runtime refuses. */
-hsk_status hsk_stream_create(hsk_stream_t* stream);
-hsk_status hsk_stream_destroy(hsk_stream_t stream);
-
 hsk_status hsk_resolve_fetch_attend(hsk_store* store, int32_t source, uint32_t epoch, const int32_t* d_sel,
                                     const int32_t* d_nq, int32_t* d_locs, hsk_stats* d_stats,
                                     const hsk_attn_desc* desc, const void* d_q, void* d_out, void* d_scratch,
