@@ -90,6 +90,20 @@ def test_attention_scratch_sizes(hsk):
         hsk.attn_scratch_bytes(bad)
     g = hsk.gqa_desc(requests=32, heads=32, kv_heads=8, dh=128, top_k=256, page_tokens=16, scale=0.088)
     assert hsk.attn_scratch_bytes(g) >= 32 * 32 * 128 * 4
+    # a forced split is an upper bound whose partitions must fit: 2,049 pages in 2 would need 1,025 pages in
+    # one GQA partition (1,024 at most), 8,192 rows in 3 would need 2,731 in one MLA partition (2,048 at most)
+    for d in (hsk.gqa_desc(requests=3, heads=32, kv_heads=8, dh=128, top_k=2049, page_tokens=16, scale=0.088,
+                           split=2),
+              hsk.mla_desc(requests=2, max_queries=1, heads=128, dk=576, dv=512, top_k=8192, row_elems=576,
+                           scale=0.04, split=3)):
+        with pytest.raises(hsk.HskError) as e:
+            hsk.attn_scratch_bytes(d)
+        assert e.value.status == hsk.HSK_EINVAL
+    for d in (hsk.gqa_desc(requests=3, heads=32, kv_heads=8, dh=128, top_k=2049, page_tokens=16, scale=0.088,
+                           split=3),
+              hsk.mla_desc(requests=2, max_queries=1, heads=128, dk=576, dv=512, top_k=8192, row_elems=576,
+                           scale=0.04, split=4)):
+        assert hsk.attn_scratch_bytes(d) > 0
 
 
 def test_attention_rejects_non_positive_or_non_finite_scale(hsk):

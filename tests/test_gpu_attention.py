@@ -71,10 +71,13 @@ def test_mla_split_and_ragged_k(k, split):
 
 
 @pytest.mark.parametrize("H", [64, 128])
-@pytest.mark.parametrize("k,split", [(1, 0), (31, 0), (33, 1), (100, 3), (257, 5), (2048, 1), (2048, 0)])
+@pytest.mark.parametrize("k,split", [(1, 0), (31, 0), (33, 1), (100, 3), (257, 5), (2048, 1), (2048, 0),
+                                     (8192, 0), (8192, 5)])
 def test_mla_32_head_waves_split_and_ragged_k(H, k, split):
     """The 32-heads-per-wave kernel (heads in 64s or 128s): ragged last tiles, one row, one partition,
-    uneven forced splits, the full 2,048-row list."""
+    uneven forced splits, the full 2,048-row list, and 8,192 rows (more than one partition may hold: the
+    automatic plan, and five partitions of 1,639 rows, so partition ends fall inside tiles and the combine
+    takes its general path for more than four partitions)."""
     _run_mla(R=2, Q=1, H=H, k=k, n_rows=5000, split=split, seed=7 * k + split + H)
 
 
@@ -175,13 +178,20 @@ def _run_gqa(R, H, Hkv, k, n_pages, page_tokens=16, split=0, seed=0, q_scale=1.0
 
 
 @pytest.mark.parametrize("k,split", [(1, 0), (7, 1), (7, 3), (256, 0), (256, 1), (100, 6), (100, 0), (200, 0),
-                                     (10, 8)])
+                                     (10, 8), (1024, 1), (2049, 0)])
 def test_gqa_pages_split_and_ragged(k, split):
     """GQA page attention: one page, ragged last tiles (k*16 not a multiple of 64 tokens), forced and
     automatic splits.  Automatic splits at R = 3, Hkv = 8 ask for 43 partitions: k = 100 (ceil 3 pages each,
     so only 34 hold pages) and k = 200 (5 pages each, 40 hold pages); the forced k = 10 in 8 (2 pages each,
-    5 hold pages).  The planner makes only the non-empty partitions."""
+    5 hold pages).  The planner makes only the non-empty partitions.  A partition at its largest, 1,024 pages
+    forced into one, and 2,049 pages under the automatic plan."""
     _run_gqa(R=3, H=32, Hkv=8, k=k, n_pages=600, split=split, seed=k * 10 + split)
+
+
+def test_gqa_automatic_plan_at_the_partition_limit():
+    """1,024 units (128 requests x 8 KV heads) need no split for the grid, but 1,025 pages exceed what one
+    partition holds: the automatic plan takes the smallest split that fits (2 partitions of 513 pages)."""
+    _run_gqa(R=128, H=8, Hkv=8, k=1025, n_pages=300, seed=1025)
 
 
 def test_gqa_xcd_grouped_combine_partial_group():
