@@ -817,7 +817,7 @@ __global__ __launch_bounds__(kResolveThreads) void promote_kernel(PromoteArgs a)
 __global__ __launch_bounds__(kFetchThreads) void gather_kernel(GatherArgs g, int32_t R) {
   __shared__ const char* s_src[kGatherWaves][kGatherList];
   __shared__ char* s_dst[kGatherWaves][kGatherList];
-  constexpr int kDepth = 8;
+  constexpr int kDepth = 4;  // 16-byte loads in flight per lane (fewer or more slowed the overlapped step)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * kGatherWaves;
