@@ -122,14 +122,14 @@ def test_adaptive_full_size_reclaim_sampled():
 def test_dsa100k_overlapped_schedule_full_size():
     """The benchmark's overlapped step at full size: two micro-batches of 32 requests (deferred stores, 4 layers
     with their own payloads, 100,000-row contexts), each on its own stream, one copy stream shared by both (all
-    three on hardware queues of their own, hsk_stream_create)
-    (16 copy workgroups), attention in 3 partitions per request, all calls of a step queued before any check.
+    three on hardware queues of their own, hsk_stream_create), 18 copy workgroups, attention in 3 partitions
+    per request, all calls of a step queued before any check.
     Every call's locations and statistics against the oracle, bit for bit; pool bytes and attention sampled."""
     base = synth.WORKLOADS["dsa100k"]
     M, Rm = 2, base.requests // 2
     ws = [base.scaled(requests=Rm, seed=base.seed + 100 * mb) for mb in range(M)]
     log(f"[full overlap] {M} micro-batches x {Rm} requests, {base.layers} layers, ctx={base.ctx}")
-    hs = [Harness(w, steps=2, gather_blocks=16, check_meta_every=2, deferred=True) for w in ws]
+    hs = [Harness(w, steps=2, gather_blocks=18, check_meta_every=2, deferred=True) for w in ws]
     *streams, copy = hsk.dedicated_streams(M + 1)
     torch.cuda.synchronize()
     rng = np.random.default_rng(23)
