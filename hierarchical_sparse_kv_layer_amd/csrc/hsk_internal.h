@@ -20,7 +20,7 @@ constexpr int kResolveThreads = 1024;
 constexpr int kResolveWaves = kResolveThreads / 64;
 constexpr int kGatherThreads = 256;
 // The plan copy kernel: a compute unit's host-read rate grows with the waves it runs (one wave ~0.7 GB/s,
-// four ~1.5, sixteen ~3.4 GB/s) whatever each wave keeps in flight, so its workgroups are 16 waves and 16 of
+// four ~1.5, sixteen ~3.4 GB/s) whatever each wave keeps in flight, so its workgroups are 16 waves and 16-18 of
 // them fill the host link while leaving the other compute units free.
 constexpr int kFetchThreads = 1024;
 constexpr int64_t kAlign = 256;
