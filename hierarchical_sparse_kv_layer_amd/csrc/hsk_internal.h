@@ -97,7 +97,7 @@ struct CopyRun {           // one contiguous byte run, host -> pool
 hipError_t launch_init_meta(const SourceMeta& m, int32_t R, int32_t B, int64_t max_ctx, int64_t max_pages,
                             hipStream_t s);
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
-hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s, hipEvent_t done = nullptr);
 hipError_t launch_promote(const int32_t* locs, const int32_t* nq, const int32_t* accepted, int32_t* promoted,
                           const SourceMeta& m, char* pool, int64_t max_ctx, int64_t stg_base, int32_t R, int32_t B,
                           int32_t S, int32_t Qmax, int32_t k, int32_t row_bytes, uint32_t epoch, hipStream_t s);

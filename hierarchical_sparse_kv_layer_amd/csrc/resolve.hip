@@ -23,6 +23,8 @@
 // plan into another source's pool.
 #include <climits>
 
+#include <hip/hip_ext.h>
+
 #include "hsk_internal.h"
 
 namespace hsk {
@@ -1053,7 +1055,13 @@ hipError_t launch_promote(const int32_t* locs, const int32_t* nq, const int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s) {
+// done: an event that the launch itself records when the kernel ends (its completion signal), so no separate
+// marker follows the kernel on its stream
+hipError_t launch_gather(const GatherArgs& g, int32_t R, int32_t blocks, hipStream_t s, hipEvent_t done) {
+  if (done) {
+    hipExtLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kFetchThreads), 0, s, nullptr, done, 0u, g, R);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(kFetchThreads), 0, s, g, R);
   return hipGetLastError();
 }

@@ -164,10 +164,11 @@ hsk_status hsk_kv_store_init(const hsk_desc* desc, void* d_workspace, void* d_po
   st->append_parity.assign((size_t)desc->num_sources, 0);
   st->fetched.assign((size_t)desc->num_sources, nullptr);
   // A fetched event orders one stream of this device after a copy kernel on another: device scope is all its
-  // release and acquire need, and without the system-scope fences the copy stream's next fetch starts ~2 us
-  // sooner (the rows it copied are read by kernels of this device only).
+  // release and acquire need (the rows it copied are read by kernels of this device only), and without the
+  // system-scope fences the copy stream's next fetch starts ~2 us sooner.  The copy kernel's launch records it
+  // (hipExtLaunchKernel's stop event, which takes an event that keeps timing), so no marker follows the kernel.
   for (hipEvent_t& e : st->fetched)
-    if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       e = nullptr;
       hsk_kv_store_destroy(st);
       return HSK_EHIP;
@@ -405,7 +406,7 @@ hsk_status hsk_resolve_attend(hsk_store* st, int32_t source, uint32_t epoch, con
 // ready: wait inside the copy kernel for each request's plan of resolve `epoch` (published by a resolve on
 // another stream); null: the plan is complete when the kernel starts (stream order)
 static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_source, hipStream_t s,
-                              const uint32_t* ready = nullptr, uint32_t epoch = 0) {
+                              const uint32_t* ready = nullptr, uint32_t epoch = 0, hipEvent_t done = nullptr) {
   void* pool;
   hsk_pool_base(st, dst_source, &pool);
   GatherArgs g;
@@ -416,7 +417,7 @@ static hsk_status gather_plan(hsk_store* st, int32_t plan_source, int32_t dst_so
   g.host_req_stride = st->d.max_ctx * (int64_t)st->d.row_bytes;
   g.plan_cap = st->plan_cap; g.row_bytes = st->d.row_bytes;
   g.ready = ready; g.err = st->d_err; g.epoch = epoch;
-  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s));
+  HSK_HIP(launch_gather(g, st->d.num_requests, gather_blocks_for(st), s, done));
   return HSK_OK;
 }
 
@@ -469,13 +470,11 @@ hsk_status hsk_resolve_fetch_attend(hsk_store* st, int32_t source, uint32_t epoc
   if (c != s) a.ready = st->meta[source].ready;
   HSK_HIP(launch_resolve(a, s));
   st->last_epoch[source] = epoch;
-  const hsk_status f = c != s ? gather_plan(st, source, source, c, st->meta[source].ready, epoch)
+  // on two streams the copy kernel's launch records the fetched event that the attention's stream waits for
+  const hsk_status f = c != s ? gather_plan(st, source, source, c, st->meta[source].ready, epoch, st->fetched[source])
                               : gather_plan(st, source, source, c);
   if (f != HSK_OK) return f;
-  if (c != s) {
-    HSK_HIP(hipEventRecord(st->fetched[source], c));
-    HSK_HIP(hipStreamWaitEvent(s, st->fetched[source], 0));
-  }
+  if (c != s) HSK_HIP(hipStreamWaitEvent(s, st->fetched[source], 0));
   void* pool;
   hsk_pool_base(st, source, &pool);
   return hsk_sparse_decode_attn(desc, d_q, pool, d_locs, d_nq, d_out, d_scratch, scratch_bytes, stream);

@@ -486,7 +486,8 @@ hsk_status hsk_stream_destroy(hsk_stream_t stream);
  *   on `stream`       the resolve of hsk_resolve_step (plan only); each of its workgroups then publishes its
  *                     request's plan by storing `epoch` in the store's per-request ready word;
  *   on `copy_stream`  the fetch of hsk_fetch_plan, whose kernel waits inside, per request, for that word to
- *                     read `epoch` before it reads the plan, then an event;
+ *                     read `epoch` before it reads the plan; its launch records the store's event for the
+ *                     source when the kernel ends;
  *   on `stream`       a wait for the fetch, then hsk_sparse_decode_attn(desc, d_q, pool of `source`, d_locs, d_nq,
  *                     d_out, d_scratch, scratch_bytes).
  * While the copy stream streams this source's missing rows over the host link, the caller's other streams (other
