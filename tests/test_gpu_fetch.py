@@ -20,10 +20,10 @@ import synth  # noqa: E402
 from hsk_harness import Harness, log  # noqa: E402
 
 
-@pytest.mark.parametrize("gather_blocks", [1, 16])
+@pytest.mark.parametrize("gather_blocks", [1, 16, 18])
 def test_deferred_fetch_matches_oracle(gather_blocks):
     """Single-query decode with duplicates of the tail and a ragged k: every call's misses fetched on a side
-    stream by 1 or 16 copy workgroups."""
+    stream by 1, 16 or 18 copy workgroups."""
     w = synth.WORKLOADS["tiny"].scaled(requests=5, top_k=129, hot_slots=300, heads=64, seed=7100 + gather_blocks)
     h = Harness(w, steps=6, gather_blocks=gather_blocks, deferred=True)
     for t in range(h.steps):
@@ -71,9 +71,9 @@ def test_deferred_fetch_shared_staging_arena():
 
 def test_deferred_fetch_full_size_layers():
     """The 100K-context batch-64 shape, 4 layers with their own payloads, 2 steps, with the copy kernel's
-    16 workgroups (the launch the overlapped benchmark schedule uses)."""
+    18 workgroups (the launch the overlapped benchmark schedule uses)."""
     w = synth.WORKLOADS["dsa100k"]
-    h = Harness(w, steps=2, gather_blocks=16, check_meta_every=2, deferred=True)
+    h = Harness(w, steps=2, gather_blocks=18, check_meta_every=2, deferred=True)
     rng = np.random.default_rng(17)
     for t in range(h.steps):
         for layer in range(w.layers):
